@@ -1,0 +1,219 @@
+"""fp64 CPU oracle for one paged decode-attention step (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. It shares no code with the HIP library and never reads
+its results. ``oracle.c`` holds the arithmetic; this module builds it with
+gcc and marshals numpy arrays into it.
+
+Dtype codes follow the storage: float32 arrays are fp32, uint16 arrays are
+bf16 bit patterns, int8 arrays are int8 codes (with float32 scales).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+ORC_F32, ORC_BF16, ORC_I8 = 0, 1, 2
+_ERRORS = {1: "invalid argument", 2: "sequence length or block id out of range", 3: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+    ]
+
+
+def build(force: bool = False, extra_flags: Optional[list] = None, out: Optional[str] = None) -> str:
+    """Compile oracle.c into a shared library with gcc (-O2, OpenMP)."""
+    target = out or _LIB_PATH
+    if not force and out is None and os.path.exists(target) and \
+            os.path.getmtime(target) >= os.path.getmtime(_SRC):
+        return target
+    tmp = target + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"] + list(extra_flags or [])
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, target)
+    return target
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    lib.oracle_attention.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_attention.restype = ctypes.c_int
+    lib.oracle_visited_blocks.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p]
+    lib.oracle_visited_blocks.restype = ctypes.c_int
+    lib.oracle_gather.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_int64]
+    lib.oracle_gather.restype = ctypes.c_int
+    lib.oracle_default_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = _bind(build())
+    return _lib
+
+
+_override = threading.local()
+
+
+def _current():
+    lib = getattr(_override, "lib", None)
+    return lib if lib is not None else _load()
+
+
+class use_variant:
+    """Context manager: route this thread's oracle calls to another build of oracle.c.
+
+    Only the tests use it, to run the pins against copies built with a
+    planted mistake (``-DORC_MUTANT=n``).
+    """
+
+    def __init__(self, path: str):
+        self.lib = _bind(path)
+
+    def __enter__(self):
+        self.prev = getattr(_override, "lib", None)
+        _override.lib = self.lib
+        return self
+
+    def __exit__(self, *exc):
+        _override.lib = self.prev
+        return False
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return ORC_F32
+    if a.dtype == np.uint16:
+        return ORC_BF16
+    if a.dtype == np.int8:
+        return ORC_I8
+    raise TypeError(f"unsupported storage dtype {a.dtype}")
+
+
+class Problem:
+    """Keeps the numpy arrays alive while the C struct points into them."""
+
+    def __init__(self, q, k_pool, v_pool, block_table, seq_lens, *, q_len, window, scale,
+                 k_scale=None, v_scale=None, block_size=16):
+        self.q = np.ascontiguousarray(q)
+        self.k_pool = np.ascontiguousarray(k_pool)
+        self.v_pool = self.k_pool if v_pool is k_pool else np.ascontiguousarray(v_pool)
+        self.block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        self.seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        self.k_scale = None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32)
+        self.v_scale = None if v_scale is None else np.ascontiguousarray(v_scale, dtype=np.float32)
+        if self.q.ndim != 4 or self.k_pool.ndim != 4 or self.k_pool.shape != self.v_pool.shape:
+            raise ValueError("q must be [B,q_len,Hq,D]; pools [num_blocks,block_size,Hkv,D]")
+        B, ql, Hq, D = self.q.shape
+        nb, bs, Hkv, Dk = self.k_pool.shape
+        if ql != q_len or Dk != D or bs != block_size:
+            raise ValueError("shape mismatch")
+        kv_code = _dtype_code(self.k_pool)
+        if _dtype_code(self.v_pool) != kv_code:
+            raise ValueError("k and v pools differ in dtype")
+        s = _Problem()
+        s.q = self.q.ctypes.data
+        s.k_pool = self.k_pool.ctypes.data
+        s.v_pool = self.v_pool.ctypes.data
+        s.k_scale = self.k_scale.ctypes.data if self.k_scale is not None else None
+        s.v_scale = self.v_scale.ctypes.data if self.v_scale is not None else None
+        s.block_table = self.block_table.ctypes.data
+        s.seq_lens = self.seq_lens.ctypes.data
+        s.q_dtype = _dtype_code(self.q)
+        s.kv_dtype = kv_code
+        s.B, s.q_len, s.Hq, s.Hkv, s.D = B, q_len, Hq, Hkv, D
+        s.block_size, s.num_blocks = bs, nb
+        s.max_blocks = self.block_table.shape[1]
+        s.window = int(window)
+        s.scale = float(scale)
+        self.struct = s
+        self.shape = (B, q_len, Hq, D)
+
+    @classmethod
+    def from_inputs(cls, x) -> "Problem":
+        """Build from any object with the paged-input attribute names."""
+        return cls(x.q, x.k_pool, x.v_pool, x.block_table, x.seq_lens, q_len=x.q_len,
+                   window=x.window, scale=x.scale, k_scale=x.k_scale, v_scale=x.v_scale,
+                   block_size=x.block_size)
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise OracleError(_ERRORS.get(rc, f"error {rc}"))
+
+
+def attention(p: Problem, rows: Optional[np.ndarray] = None, threads: int = 0) -> np.ndarray:
+    """fp64 attention. All rows -> [B,q_len,Hq,D]; listed rows -> [n_rows, D]."""
+    lib = _current()
+    B, ql, Hq, D = p.shape
+    if rows is None:
+        out = np.empty((B, ql, Hq, D), dtype=np.float64)
+        _check(lib.oracle_attention(ctypes.byref(p.struct), None, 0, out.ctypes.data, threads))
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((r.size, D), dtype=np.float64)
+        _check(lib.oracle_attention(ctypes.byref(p.struct), r.ctypes.data, r.size, out.ctypes.data, threads))
+    return out
+
+
+def visited_blocks(p: Problem) -> np.ndarray:
+    """[B, max_blocks] int32: 1 where the logical block holds a key some query row sees."""
+    lib = _current()
+    vis = np.empty((p.shape[0], p.block_table.shape[1]), dtype=np.int32)
+    _check(lib.oracle_visited_blocks(ctypes.byref(p.struct), vis.ctypes.data))
+    return vis
+
+
+def gather(p: Problem, which: int, dst_tokens: int, fill: int = 0) -> np.ndarray:
+    """Raw K (which=0) or V (which=1) rows of the visible key range, [B, dst_tokens, Hkv, D]."""
+    lib = _current()
+    B = p.shape[0]
+    _, _, Hkv, D = p.k_pool.shape
+    dst = np.full((B, dst_tokens, Hkv, D), fill, dtype=p.k_pool.dtype)
+    _check(lib.oracle_gather(ctypes.byref(p.struct), which, dst.ctypes.data, dst_tokens))
+    return dst
+
+
+def default_threads() -> int:
+    return int(_current().oracle_default_threads())

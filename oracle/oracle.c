@@ -1,0 +1,307 @@
+/*
+ * oracle.c -- fp64 CPU oracle for one paged decode-attention step.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or helper with the HIP kernels, and it never sees their
+ * results. It is deliberately plain and slow: every output row is computed
+ * on its own, straight from the definition, in double precision.
+ *
+ * What it computes, and where each piece is defined:
+ *
+ *  - Attention for a new query over the cache (CS336 lecture 10 study guide,
+ *    the decode-attention equation): the query is compared with every cached
+ *    key it may see, the new token's own key included; the scores are scaled
+ *    (by 1/sqrt(d_h) there; here by the caller's `scale`), passed through a
+ *    softmax, and the output is the softmax-weighted sum of the values.
+ *  - Paged storage (tiniestgpt notes, "PagedAttention: why it is needed"):
+ *    the cache is a pool k_cache[block][slot][head][dim]; block_table[seq][i]
+ *    names the physical block that holds logical block i of a sequence.
+ *  - Sliding window (Lab 5 Gemma4 handout, "Sliding Window Attention" and
+ *    "Ring KV Cache"): a local layer lets a position see only the most recent
+ *    W tokens. Reading used here: W keys including the query's own position,
+ *    i.e. key j is visible from position p iff p - W < j <= p; a ring of W
+ *    slots holds exactly these. window <= 0 means a global (causal) layer.
+ *  - Grouped-query attention (Lab 5, "Grouped Query Attention"): query heads
+ *    share KV heads in contiguous groups, head h reads KV head h / (Hq/Hkv),
+ *    the mapping obtained by repeating each KV head Hq/Hkv times.
+ *  - Causal multi-token step (tiniestgpt notes, "Speculative decoding"): a
+ *    verify step feeds q_len tokens; query t sits at position L - q_len + t,
+ *    where L (seq_lens[b]) already counts all q_len new tokens.
+ *  - int8 cache (tiniestgpt notes, "Quantization" / KV cache quantization):
+ *    codes are gathered first and then dequantized, value = code * scale,
+ *    with one scale per token per KV head.
+ *
+ * The softmax is taken in the textbook two-pass form: the largest score is
+ * subtracted before exponentiating, then the weights are normalised by their
+ * sum. Both steps are exact rewrites of softmax; no blocking, no running
+ * rescale, no split of the key range.
+ */
+#include <math.h>
+#include <stdint.h>
+/* ORC_MUTANT selects one planted mistake for the tests that prove the pins
+ * catch it; the library the tests, the smoke check and the benchmark use is
+ * always built with ORC_MUTANT == 0. */
+#ifndef ORC_MUTANT
+#define ORC_MUTANT 0
+#endif
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+
+enum {
+  ORC_OK = 0,
+  ORC_ERR_ARG = 1,       /* bad shape / null pointer */
+  ORC_ERR_DATA = 2,      /* seq_len or block id out of range */
+  ORC_ERR_NOMEM = 3
+};
+
+typedef struct {
+  const void* q;            /* [B][q_len][Hq][D], q_dtype */
+  const void* k_pool;       /* [num_blocks][block_size][Hkv][D], kv_dtype */
+  const void* v_pool;       /* same shape and dtype */
+  const float* k_scale;     /* [num_blocks][block_size][Hkv], int8 only */
+  const float* v_scale;     /* same */
+  const int32_t* block_table; /* [B][max_blocks] */
+  const int32_t* seq_lens;  /* [B] */
+  int32_t q_dtype, kv_dtype;
+  int32_t B, q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks;
+  int32_t window;
+  double scale;
+} orc_problem;
+
+/* One stored element, widened to double. bf16 is the upper half of a binary32. */
+static double elem(const void* base, int dtype, size_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[i];
+  if (dtype == ORC_BF16) {
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+  }
+  return (double)((const int8_t*)base)[i];
+}
+
+static int check_problem(const orc_problem* P) {
+  if (!P || !P->q || !P->k_pool || !P->v_pool || !P->block_table || !P->seq_lens) return ORC_ERR_ARG;
+  if (P->B < 0 || P->q_len < 1 || P->Hq < 1 || P->Hkv < 1 || P->D < 1) return ORC_ERR_ARG;
+  if (P->block_size < 1 || P->num_blocks < 1 || P->max_blocks < 1) return ORC_ERR_ARG;
+  if (P->Hq % P->Hkv != 0) return ORC_ERR_ARG;
+  if (P->q_dtype != ORC_F32 && P->q_dtype != ORC_BF16) return ORC_ERR_ARG;
+  if (P->kv_dtype != ORC_F32 && P->kv_dtype != ORC_BF16 && P->kv_dtype != ORC_I8) return ORC_ERR_ARG;
+  if (P->kv_dtype == ORC_I8 && (!P->k_scale || !P->v_scale)) return ORC_ERR_ARG;
+  for (int b = 0; b < P->B; ++b) {
+    int32_t L = P->seq_lens[b];
+    if (L < P->q_len || (int64_t)L > (int64_t)P->max_blocks * P->block_size) return ORC_ERR_DATA;
+    int32_t used = (L + P->block_size - 1) / P->block_size;
+    for (int i = 0; i < used; ++i) {
+      int32_t blk = P->block_table[(size_t)b * P->max_blocks + i];
+      if (blk < 0 || blk >= P->num_blocks) return ORC_ERR_DATA;
+    }
+  }
+  return ORC_OK;
+}
+
+/* Position of query token t of sequence b, and the first key it may see. */
+static void query_span(const orc_problem* P, int b, int t, int32_t* first, int32_t* last) {
+  int32_t L = P->seq_lens[b];
+#if ORC_MUTANT == 3
+  int32_t p = L - 1; (void)t;
+#else
+  int32_t p = L - P->q_len + t;
+#endif
+  int32_t lo = 0;
+  if (P->window > 0) {
+#if ORC_MUTANT == 2
+    lo = p - P->window;
+#else
+    lo = p - P->window + 1;
+#endif
+    if (lo < 0) lo = 0;
+  }
+  *first = lo;
+  *last = p;
+}
+
+/* Element index of (key j, kv head g, dim 0) of sequence b, through the block table. */
+static size_t key_row(const orc_problem* P, int b, int32_t j, int g) {
+  int32_t blk = P->block_table[(size_t)b * P->max_blocks + j / P->block_size];
+  int32_t slot = j % P->block_size;
+#if ORC_MUTANT == 4
+  return (((size_t)blk * P->Hkv + g) * P->block_size + slot) * (size_t)P->D;
+#else
+  return (((size_t)blk * P->block_size + slot) * P->Hkv + g) * (size_t)P->D;
+#endif
+}
+
+static double key_scale(const float* s, const orc_problem* P, int b, int32_t j, int g) {
+  if (P->kv_dtype != ORC_I8) return 1.0;
+  size_t row = key_row(P, b, j, g) / (size_t)P->D;   /* (blk, slot, g) index */
+  return (double)s[row];
+}
+
+/* One output row: (sequence b, query token t, query head h) -> out[0..D). */
+static int attend_row(const orc_problem* P, int b, int t, int h, double* out, double* scores) {
+  const int D = P->D;
+#if ORC_MUTANT == 1
+  const int g = h % P->Hkv;
+#else
+  const int g = h / (P->Hq / P->Hkv);
+#endif
+  int32_t lo, p;
+  query_span(P, b, t, &lo, &p);
+  const size_t qrow = (((size_t)b * P->q_len + t) * P->Hq + h) * (size_t)D;
+  const int32_t n = p - lo + 1;
+
+  for (int32_t j = lo; j <= p; ++j) {
+    size_t kr = key_row(P, b, j, g);
+    double ks = key_scale(P->k_scale, P, b, j, g);
+    double dot = 0.0;
+#if ORC_MUTANT == 8
+    for (int d = 1; d < D; ++d) dot += elem(P->q, P->q_dtype, qrow + d) * (elem(P->k_pool, P->kv_dtype, kr + d) * ks);
+#else
+    for (int d = 0; d < D; ++d) dot += elem(P->q, P->q_dtype, qrow + d) * (elem(P->k_pool, P->kv_dtype, kr + d) * ks);
+#endif
+#if ORC_MUTANT == 5
+    scores[j - lo] = dot;
+#else
+    scores[j - lo] = P->scale * dot;
+#endif
+  }
+  double m = -INFINITY;
+  for (int32_t i = 0; i < n; ++i)
+    if (scores[i] > m) m = scores[i];
+  double z = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    scores[i] = exp(scores[i] - m);
+    z += scores[i];
+  }
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  for (int32_t j = lo; j <= p; ++j) {
+    size_t vr = key_row(P, b, j, g);
+#if ORC_MUTANT == 7
+    double vs = key_scale(P->k_scale, P, b, j, g);
+#else
+    double vs = key_scale(P->v_scale, P, b, j, g);
+#endif
+    double w = scores[j - lo];
+    for (int d = 0; d < D; ++d) out[d] += w * (elem(P->v_pool, P->kv_dtype, vr + d) * vs);
+  }
+#if ORC_MUTANT != 6
+  for (int d = 0; d < D; ++d) out[d] /= z;
+#else
+  (void)z;
+#endif
+  return ORC_OK;
+}
+
+/*
+ * Attention output in fp64.
+ *   rows == NULL: every row, out is [B][q_len][Hq][D].
+ *   rows != NULL: only the listed rows, row index r = (b*q_len + t)*Hq + h,
+ *                 out is [n_rows][D].
+ * nthreads <= 0 uses the OpenMP default. Returns an ORC_* code.
+ */
+int oracle_attention(const orc_problem* P, const int64_t* rows, int64_t n_rows, double* out, int nthreads) {
+  int rc = check_problem(P);
+  if (rc != ORC_OK) return rc;
+  if (!out) return ORC_ERR_ARG;
+  const int64_t total = (int64_t)P->B * P->q_len * P->Hq;
+  const int64_t n = rows ? n_rows : total;
+  if (rows) {
+    for (int64_t i = 0; i < n_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= total) return ORC_ERR_ARG;
+  }
+  int32_t max_len = 1;
+  for (int b = 0; b < P->B; ++b)
+    if (P->seq_lens[b] > max_len) max_len = P->seq_lens[b];
+  int err = ORC_OK;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)max_len);
+    if (!scores) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      err = ORC_ERR_NOMEM;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+      for (int64_t i = 0; i < n; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        int h = (int)(r % P->Hq);
+        int64_t bt = r / P->Hq;
+        int t = (int)(bt % P->q_len);
+        int b = (int)(bt / P->q_len);
+        attend_row(P, b, t, h, out + (size_t)i * P->D, scores);
+      }
+      free(scores);
+    }
+  }
+  return err;
+}
+
+/* Number of threads oracle_attention would use for nthreads <= 0. */
+int oracle_default_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * Logical blocks that hold at least one key visible to at least one query
+ * row of the sequence: vis[b][i] = 1 for such blocks, 0 otherwise
+ * (vis is [B][max_blocks]). Found by listing every visible key.
+ */
+int oracle_visited_blocks(const orc_problem* P, int32_t* vis) {
+  int rc = check_problem(P);
+  if (rc != ORC_OK) return rc;
+  if (!vis) return ORC_ERR_ARG;
+  memset(vis, 0, sizeof(int32_t) * (size_t)P->B * P->max_blocks);
+  for (int b = 0; b < P->B; ++b)
+    for (int t = 0; t < P->q_len; ++t) {
+      int32_t lo, p;
+      query_span(P, b, t, &lo, &p);
+      for (int32_t j = lo; j <= p; ++j) vis[(size_t)b * P->max_blocks + j / P->block_size] = 1;
+    }
+  return ORC_OK;
+}
+
+/*
+ * Raw bytes of the keys (which == 0) or values (which == 1) that some query
+ * row of each sequence can see, in increasing key order, all KV heads:
+ * dst is [B][dst_tokens][Hkv][D] elements of the cache type; for sequence b,
+ * entry w holds key first(b) + w where first(b) is the first key visible to
+ * query token 0. Entries past the visible range are left untouched.
+ */
+int oracle_gather(const orc_problem* P, int which, void* dst, int64_t dst_tokens) {
+  int rc = check_problem(P);
+  if (rc != ORC_OK) return rc;
+  if (!dst || (which != 0 && which != 1) || dst_tokens < 0) return ORC_ERR_ARG;
+  const void* pool = which == 0 ? P->k_pool : P->v_pool;
+  const size_t esz = P->kv_dtype == ORC_F32 ? 4 : (P->kv_dtype == ORC_BF16 ? 2 : 1);
+  const size_t row_bytes = esz * (size_t)P->D;
+  for (int b = 0; b < P->B; ++b) {
+    int32_t lo0, p0, lo_last, p_last;
+    query_span(P, b, 0, &lo0, &p0);
+    query_span(P, b, P->q_len - 1, &lo_last, &p_last);
+    if ((int64_t)(p_last - lo0 + 1) > dst_tokens) return ORC_ERR_ARG;
+    for (int32_t j = lo0; j <= p_last; ++j)
+      for (int g = 0; g < P->Hkv; ++g) {
+        size_t src = key_row(P, b, j, g) * esz;
+        size_t off = ((((size_t)b * dst_tokens) + (size_t)(j - lo0)) * P->Hkv + g) * row_bytes;
+        memcpy((char*)dst + off, (const char*)pool + src, row_bytes);
+      }
+  }
+  return ORC_OK;
+}

@@ -1,0 +1,59 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is oracle.c rebuilt with ``-DORC_MUTANT=n`` (a wrong GQA head
+map, a window one key too wide, verify rows all placed at the last position,
+slot and head swapped in the pool address, the score scale dropped, the
+softmax left unnormalised, the key scale used for values, one dimension left
+out of the dot product). The pins of test_oracle_pins.py run against it; the
+mutant survives only if every pin still passes.
+"""
+
+from __future__ import annotations
+
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    1: "GQA head map h % Hkv",
+    2: "window admits W+1 keys",
+    3: "every verify row placed at the last position",
+    4: "slot and head swapped in the pool address",
+    5: "score scale dropped",
+    6: "softmax not normalised",
+    7: "key scale applied to values",
+    8: "first dimension left out of the dot product",
+}
+
+PIN_CALLS = [
+    lambda: [pins.test_matches_torch_sdpa(c) for c in pins.SDPA_CASES],
+    pins.test_single_key_returns_value,
+    pins.test_window_one_returns_own_value,
+    pins.test_equal_keys_give_mean_value,
+    pins.test_unit_values_give_ones,
+    pins.test_verify_rows_equal_sequential_decode,
+    pins.test_gqa_equals_expanded_heads,
+    pins.test_visited_blocks_closed_form,
+    pins.test_gather_matches_fancy_indexing,
+    lambda: [pins.test_golden_closed_forms(p) for p in
+             sorted(os.path.join(pins.GOLDEN, f) for f in os.listdir(pins.GOLDEN)
+                    if f.endswith(".json") and "k_tokens" in open(os.path.join(pins.GOLDEN, f)).read())],
+]
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
+def test_pins_catch_planted_mistake(mutant):
+    with tempfile.TemporaryDirectory() as d:
+        path = oracle.build(extra_flags=[f"-DORC_MUTANT={mutant}"], out=os.path.join(d, "mut.so"))
+        caught = []
+        with oracle.use_variant(path):
+            for call in PIN_CALLS:
+                try:
+                    call()
+                except (AssertionError, oracle.OracleError):
+                    caught.append(call)
+        assert caught, f"no pin caught mutant {mutant}: {MUTANTS[mutant]}"
