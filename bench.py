@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Paged decode-attention benchmark on one MI355X.
+
+One step = one paged decode-attention call (attention kernel, plus the
+split-combine kernel when the key range is split) over one batch of the
+synthetic workload, inputs resident in HBM. The default workload is the
+Gemma4-12B-like local layer: 32 sequences, one query token each, 16 query
+heads on 8 KV heads, head_dim 256, bf16, 16-token blocks, a 1024-token
+sliding window, context lengths uniform in [512, 8192], blocks randomly
+permuted in a pool of total need + 10%.
+
+Between steps the call rotates over several device copies of the cache (and
+its own block table) so that no step finds its cache in the 256 MB
+Infinity Cache from the previous one: every step reads from HBM.
+
+Prints ONE JSON line on stdout (the run's record); diagnostics go to stderr.
+  value     = queries per second over the K timed steps (query = one token of
+              one sequence through all heads of the layer)
+  roofline  = algorithmic bytes of a step / mean duration of the attention
+              kernel, timed with HIP events recorded on the launch stream
+  cpu_baseline = the fp64 oracle on the host's cores, same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention queries/s and achieved KV HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 << 20         # Infinity Cache
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload (2 = the Gemma4-12B local layer; others for their own measurements)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="cache copies rotated across steps (0: enough to exceed 4x the Infinity Cache)")
+    ap.add_argument("--num-splits", type=int, default=0, help="force the context split count (0: library plan)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "decode attention shards by sequence or KV head with no exchange, so a multi-GPU figure "
+              "would be N independent copies of this one.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_94_amd as pa
+    from paged_kv_cache_94_amd import accounting
+    from workloads import CONFIGS, make_config
+
+    if not os.path.exists(pa.library_path()):
+        from paged_kv_cache_94_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = CONFIGS[args.config]
+    t0 = time.time()
+    x = make_config(args.config)
+    acct = accounting.for_inputs(x)
+    log(f"workload {x.name}: B={x.batch} q_len={x.q_len} Hq={x.num_q_heads} Hkv={x.num_kv_heads} "
+        f"D={x.head_dim} window={x.window} kv={x.kv_dtype} pool={x.num_blocks} blocks "
+        f"(generated in {time.time() - t0:.1f}s)")
+    log(f"algorithmic bytes/step {acct['alg_bytes'] / 1e6:.1f} MB, touched KV {acct['touched_kv_bytes'] / 1e6:.1f} MB, "
+        f"flops/step {acct['flops'] / 1e9:.2f} G")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    copies = args.copies or max(1, min(8, math.ceil(4 * MALL_BYTES / max(1, acct["alg_bytes"]))))
+    q = to_dev(x.q)
+    lens = to_dev(x.seq_lens)
+    k0 = to_dev(x.k_pool)
+    v0 = k0 if x.v_aliases_k else to_dev(x.v_pool)
+    ks0 = None if x.k_scale is None else to_dev(x.k_scale)
+    vs0 = None if x.v_scale is None else to_dev(x.v_scale)
+    table0 = to_dev(x.block_table)
+    entry = "verify" if x.q_len > 1 else ("decode_int8" if x.kv_dtype == "int8" else "decode")
+    out = torch.empty_like(q)
+    calls = []
+    for c in range(copies):
+        if c == 0:
+            k, v, ks, vs, table = k0, v0, ks0, vs0, table0
+        else:
+            k = torch.empty_like(k0).copy_(k0)
+            v = k if x.v_aliases_k else torch.empty_like(v0).copy_(v0)
+            ks = None if ks0 is None else torch.empty_like(ks0).copy_(ks0)
+            vs = None if vs0 is None else torch.empty_like(vs0).copy_(vs0)
+            table = table0.clone()
+        calls.append(pa.Prepared(entry, out, q, k, v, table, lens, window=x.window, scale=x.scale,
+                                 max_seq_len=x.max_seq_len, k_scale=ks, v_scale=vs, num_splits=args.num_splits))
+    plan = pa.plan(q, k0, v0, table0, lens, window=x.window, scale=x.scale, max_seq_len=x.max_seq_len,
+                   k_scale=ks0, v_scale=vs0, num_splits=args.num_splits)
+    log(f"plan: {plan}; {copies} cache copies rotated")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:   # materialise the underlying HIP events before handing their handles over
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        calls[i % copies].launch()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        calls[i % copies].launch(timing=ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    ms_per_step = elapsed / args.steps * 1e3
+    queries = acct["queries"]
+    value = queries * args.steps / elapsed
+    achieved = acct["alg_bytes"] / kern_s / 1e9
+    step_gbs = acct["alg_bytes"] / (elapsed / args.steps) / 1e9
+    log(f"attention kernel: mean {kern_s * 1e6:.2f} us (min {min(kern_ms) * 1e3:.2f}, max {max(kern_ms) * 1e3:.2f}) "
+        f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS * 100:.1f}% of peak; "
+        f"whole step {ms_per_step * 1e3:.2f} us -> {step_gbs:.0f} GB/s, {value:.4g} queries/s")
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device-to-device copies done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle   # the CPU baseline leg is the only part of the benchmark that uses the oracle
+        prob = oracle.Problem.from_inputs(x)
+        threads = oracle.default_threads()
+        reps, spent = 0, 0.0
+        while reps < 2 or spent < args.cpu_seconds:
+            c0 = time.perf_counter()
+            oracle.attention(prob, threads=threads)
+            spent += time.perf_counter() - c0
+            reps += 1
+            if reps >= 1000:
+                break
+        cpu = {"value": queries * reps / spent, "unit": "queries/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole {x.name} batch ({x.batch} sequences x {x.q_len} query token(s), all "
+                         f"{x.num_q_heads} heads), fp64, repeated {reps} times in {spent:.1f} s"}
+        log(f"cpu baseline: {cpu['value']:.4g} queries/s on {threads} threads")
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "int8": "int8 cache, bf16 q"}[x.kv_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{x.name}: B={x.batch}, q_len={x.q_len}, Hq={x.num_q_heads}, Hkv={x.num_kv_heads}, "
+                        f"D={x.head_dim}, block=16, window={x.window}, lens {cfg['lens']} (seed {args.config})",
+            "batch": x.batch,
+            "q_len": x.q_len,
+            "alg_bytes_per_step": acct["alg_bytes"],
+            "step_GBps": step_gbs,
+            "cache_copies": copies,
+            "splits": plan["splits"],
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+/*
+ * pa.h -- paged decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * One attention step of a decoder over a paged KV cache: every query token
+ * gathers its sequence's keys and values through a block table, takes the
+ * softmax of its scaled dot products with the keys it may see, and returns
+ * the weighted sum of the matching values.
+ *
+ *   - Cache layout (tiniestgpt inference notes, "PagedAttention: why it is
+ *     needed"): a physical pool k_cache[block][slot][head][dim] and a table
+ *     block_table[seq][i] naming the physical block of logical block i.
+ *   - The operation (CS336 lecture 10 study guide, decode-attention
+ *     equation): a = softmax(q [K_1..K_n]^T * scale), y = a [V_1..V_n]; the
+ *     step's own key and value are already in the cache.
+ *   - Grouped-query attention (Lab 5 Gemma4 handout, "Grouped Query
+ *     Attention"): query head h reads KV head h / (Hq / Hkv); KV heads are
+ *     never copied per query head.
+ *   - Sliding window (Lab 5, "Sliding Window Attention" and "Ring KV Cache"):
+ *     with window W > 0 a query at position p sees keys p-W < j <= p, the W
+ *     most recent tokens including itself. Blocks holding no such key are
+ *     never loaded (the handout's "skip out-of-window blocks rather than
+ *     compute then mask").
+ *   - int8 cache (tiniestgpt notes, "Quantization", KV cache quantization):
+ *     the same interface; codes are gathered first and dequantized after
+ *     the gather, value = code * scale, one fp32 scale per token per KV head.
+ *   - Verify step (tiniestgpt notes, "Speculative decoding"): q_len tokens
+ *     of one sequence at once, causal among themselves.
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or keeps them. Arrays are dense and
+ *     row-major in the shapes given below.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream). A return of PA_OK means the work was enqueued; device-side
+ *     data errors are not detected (see the preconditions).
+ *   - The library keeps no state between calls except a per-device cache of
+ *     the compute-unit count; it is safe to call from several host threads.
+ *   - On failure the entry point returns a PA_ERR_* code, enqueues nothing,
+ *     and pa_last_error() returns a message for the calling thread.
+ *
+ * Preconditions on device data (not checked by the kernels):
+ *   q_len <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size,
+ *   and block_table[b][i] in [0, num_blocks) for every logical block i that
+ *   holds a key visible to some query of sequence b. Other table entries
+ *   and cache slots past seq_lens[b] are never read.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* pa_stream_t; /* a hipStream_t */
+typedef struct ihipEvent_t* pa_event_t;   /* a hipEvent_t */
+
+/* Element types. q and out share one type; the cache may be int8. */
+enum { PA_F32 = 0, PA_BF16 = 1, PA_INT8 = 2 };
+
+/* Return codes. */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, Hq % Hkv != 0, q_len rule broken, non-finite scale */
+  PA_ERR_UNSUPPORTED = 2, /* head_dim / block_size / dtype / group combination not built */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_workspace_size() */
+  PA_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing */
+};
+
+typedef struct {
+  void* out;                  /* [B][q_len][Hq][D], q_dtype */
+  const void* q;              /* [B][q_len][Hq][D], q_dtype */
+  const void* k_pool;         /* [num_blocks][block_size][Hkv][D], kv_dtype */
+  const void* v_pool;         /* same shape; may equal k_pool (keys and values shared, read once) */
+  const float* k_scale;       /* int8 cache only: [num_blocks][block_size][Hkv]; else NULL */
+  const float* v_scale;       /* int8 cache only: same shape; else NULL */
+  const int32_t* block_table; /* [B][max_blocks_per_seq] physical block ids */
+  const int32_t* seq_lens;    /* [B] cached tokens per sequence, this step's q_len tokens included */
+  int32_t num_seqs;           /* B >= 0 (B == 0 enqueues nothing) */
+  int32_t q_len;              /* query tokens per sequence; query t sits at position seq_len - q_len + t */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv, divides Hq */
+  int32_t head_dim;           /* D: 64, 128 or 256 */
+  int32_t block_size;         /* tokens per cache block: 16 */
+  int32_t num_blocks;         /* blocks in each pool */
+  int32_t max_blocks_per_seq; /* row length of block_table */
+  int32_t max_seq_len;        /* host-side upper bound on seq_lens[]; sizes the launch, no device sync */
+  int32_t window;             /* <= 0: every earlier key; > 0: the W most recent keys */
+  float scale;                /* multiplies q.k before the softmax (1/sqrt(D) for standard attention) */
+  int32_t q_dtype;            /* PA_F32 or PA_BF16 (also the output type) */
+  int32_t kv_dtype;           /* PA_F32, PA_BF16 or PA_INT8 */
+  int32_t num_splits;         /* 0: the library picks the context split; > 0: split each sequence's
+                                 key range into at most this many parts */
+  void* workspace;            /* device scratch for split partials, caller-owned; may be NULL
+                                 when pa_workspace_size() returns 0 */
+  size_t workspace_bytes;     /* size of workspace */
+  int32_t* debug_visits;      /* NULL, or [B][Hkv][max_blocks_per_seq] zeroed by the caller: the
+                                 kernels add 1 for every (sequence, KV head, logical block) they load */
+  pa_event_t timing_start;    /* NULL, or an event recorded on `stream` just before the attention kernel */
+  pa_event_t timing_stop;     /* NULL, or an event recorded just after it (before any combine kernel) */
+} pa_args;
+
+/* Plan the library would use for these arguments (informational). */
+typedef struct {
+  int32_t kernel;             /* 0: vector-ALU kernel, 1: matrix-core (MFMA) kernel */
+  int32_t rows;               /* query rows per KV head = (Hq/Hkv) * q_len */
+  int32_t waves_per_group;    /* wavefronts cooperating on one (sequence, KV head, split) */
+  int32_t splits;             /* context splits per sequence (1: no combine kernel) */
+  int32_t blocks_per_split;   /* logical blocks per split */
+  int32_t grid;               /* workgroups of the attention kernel */
+  size_t workspace_bytes;     /* == pa_workspace_size() */
+} pa_plan_info;
+
+/*
+ * Bytes of workspace the call needs for these arguments (0 when the key
+ * range is not split). Depends on the shapes, max_seq_len, window,
+ * num_splits and the device's compute-unit count, never on device data.
+ * Returns (size_t)-1 if the arguments are invalid.
+ */
+size_t pa_workspace_size(const pa_args* args);
+
+/* Fill *info with the plan for args. Returns a PA_* code. */
+int pa_plan(const pa_args* args, pa_plan_info* info);
+
+/*
+ * Single-token decode step (q_len must be 1) over an fp32 or bf16 cache;
+ * kv_dtype must equal q_dtype. Defined by the decode-attention equation of
+ * the CS336 lecture 10 study guide with the paging, GQA and window rules
+ * above.
+ */
+int pa_decode(const pa_args* args, pa_stream_t stream);
+
+/*
+ * Single-token decode step (q_len must be 1) over an int8 cache with
+ * per-token, per-KV-head fp32 scales (tiniestgpt notes, KV cache
+ * quantization: gather the int8 codes, then dequantize). q_dtype must be
+ * PA_BF16, kv_dtype PA_INT8, and k_scale / v_scale non-NULL.
+ */
+int pa_decode_int8(const pa_args* args, pa_stream_t stream);
+
+/*
+ * Multi-token verify step, q_len >= 1 (tiniestgpt notes, "Speculative
+ * decoding": the target model scores the last known token plus the drafts
+ * in one pass). Query t of sequence b sits at position seq_lens[b]-q_len+t
+ * and sees keys up to and including its own position (and, with a window,
+ * only the W most recent of them). Any supported cache type.
+ */
+int pa_verify(const pa_args* args, pa_stream_t stream);
+
+/*
+ * Debug: copy the raw cache rows that the attention kernels would load
+ * (which = 0: keys, 1: values) into dst, [B][dst_tokens][Hkv][D] elements of
+ * kv_dtype. Entry w of sequence b holds key first(b)+w, first(b) being the
+ * first key visible to query token 0; entries past seq_lens[b]-1 are left
+ * untouched. Uses the same block-range and address computation as the
+ * attention kernels, so a bit-exact comparison checks the gather itself.
+ * dst_tokens must be >= window + q_len - 1 (window > 0) or >= max_seq_len.
+ */
+int pa_debug_gather(const pa_args* args, int32_t which, void* dst, int64_t dst_tokens,
+                    pa_stream_t stream);
+
+/* Static description of a return code. */
+const char* pa_strerror(int code);
+
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,217 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+A thin binding over libpa.so (the C ABI in include/pa.h). Every step of the
+attention runs in the library's HIP kernels; this module only checks tensor
+shapes, dtypes and devices, passes raw pointers plus the current HIP stream,
+and allocates the split workspace through PyTorch's caching allocator.
+
+Layouts (row-major, all tensors on the same GPU):
+    q, out       [B, q_len, Hq, D]            float32 or bfloat16
+    k_pool, v_pool [num_blocks, 16, Hkv, D]   same dtype as q, or int8
+    k_scale, v_scale [num_blocks, 16, Hkv]    float32 (int8 caches)
+    block_table  [B, max_blocks_per_seq]      int32
+    seq_lens     [B]                          int32, this step's tokens included
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+from ._lib import PaError  # noqa: F401
+
+__all__ = ["decode", "decode_int8", "verify", "debug_gather", "plan", "workspace_size", "PaError",
+           "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, allow_int8: bool) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return _lib.PA_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.PA_BF16
+    if allow_int8 and t.dtype == torch.int8:
+        return _lib.PA_INT8
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, scale: Optional[float],
+                max_seq_len: Optional[int], k_scale, v_scale, num_splits: int, debug_visits) -> _lib.PaArgs:
+    torch = _torch()
+    tensors = [t for t in (out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, debug_visits)
+               if t is not None]
+    dev = q.device
+    for t in tensors:
+        _require(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+        _require(t.is_contiguous(), "all tensors must be contiguous")
+    _require(q.dim() == 4 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [B, q_len, Hq, D]")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype,
+             "k_pool/v_pool must be [num_blocks, block_size, Hkv, D] of one dtype")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [B, max_blocks]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens must be int32 [B]")
+    B, q_len, Hq, D = q.shape
+    nb, bs, Hkv, Dk = k_pool.shape
+    _require(Dk == D, "head_dim mismatch between q and the cache")
+    _require(block_table.shape[0] == B and seq_lens.shape[0] == B, "batch mismatch")
+    for s in (k_scale, v_scale):
+        if s is not None:
+            _require(s.dtype == torch.float32 and tuple(s.shape) == (nb, bs, Hkv), "scales must be float32 [nb, bs, Hkv]")
+    if debug_visits is not None:
+        _require(debug_visits.dtype == torch.int32 and tuple(debug_visits.shape) == (B, Hkv, block_table.shape[1]),
+                 "debug_visits must be int32 [B, Hkv, max_blocks]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else q_len   # host sync; pass it to avoid one
+    if scale is None:
+        scale = D ** -0.5
+    a = _lib.PaArgs()
+    a.out, a.q, a.k_pool, a.v_pool = _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool)
+    a.k_scale, a.v_scale = _ptr(k_scale) or None, _ptr(v_scale) or None
+    a.block_table, a.seq_lens = _ptr(block_table), _ptr(seq_lens)
+    a.num_seqs, a.q_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, q_len, Hq, Hkv, D
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = bs, nb, block_table.shape[1]
+    a.max_seq_len = int(max_seq_len)
+    a.window = int(window)
+    a.scale = float(scale)
+    a.q_dtype = _dtype_code(q, allow_int8=False)
+    a.kv_dtype = _dtype_code(k_pool, allow_int8=True)
+    a.num_splits = int(num_splits)
+    a.debug_visits = _ptr(debug_visits) or None
+    return a
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _attach_workspace(a: _lib.PaArgs, workspace, device) -> object:
+    lib = _lib.load()
+    need = lib.pa_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        _lib.check(_lib.PA_ERR_INVALID_ARG)
+    if need == 0:
+        return None
+    if workspace is None:
+        torch = _torch()
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _require(workspace.numel() * workspace.element_size() >= need, f"workspace needs {need} bytes")
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return workspace
+
+
+def _run(entry: str, out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None,
+         k_scale=None, v_scale=None, num_splits=0, workspace=None, debug_visits=None, stream=None,
+         timing=None):
+    lib = _lib.load()
+    a = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
+                    max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
+                    debug_visits=debug_visits)
+    ws = _attach_workspace(a, workspace, q.device)
+    if timing is not None:
+        a.timing_start = ctypes.c_void_p(timing[0].cuda_event if hasattr(timing[0], "cuda_event") else timing[0])
+        a.timing_stop = ctypes.c_void_p(timing[1].cuda_event if hasattr(timing[1], "cuda_event") else timing[1])
+    rc = getattr(lib, entry)(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
+    _lib.check(rc)
+    del ws  # the caching allocator keeps the block stream-ordered until the kernels finish
+    return out
+
+
+def decode(out, q, k_pool, v_pool, block_table, seq_lens, **kw):
+    """Single-token decode (q_len == 1) over an fp32 or bf16 cache. Writes and returns ``out``."""
+    return _run("pa_decode", out, q, k_pool, v_pool, block_table, seq_lens, **kw)
+
+
+def decode_int8(out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, **kw):
+    """Single-token decode over an int8 cache with per-token, per-KV-head fp32 scales."""
+    return _run("pa_decode_int8", out, q, k_pool, v_pool, block_table, seq_lens, k_scale=k_scale,
+                v_scale=v_scale, **kw)
+
+
+def verify(out, q, k_pool, v_pool, block_table, seq_lens, **kw):
+    """q_len >= 1 query tokens per sequence, causal among themselves."""
+    return _run("pa_verify", out, q, k_pool, v_pool, block_table, seq_lens, **kw)
+
+
+def plan(q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None, k_scale=None,
+         v_scale=None, num_splits=0) -> dict:
+    """The launch plan libpa would use for these tensors (no launch)."""
+    lib = _lib.load()
+    a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
+                    max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
+                    debug_visits=None)
+    info = _lib.PaPlanInfo()
+    _lib.check(lib.pa_plan(ctypes.byref(a), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in info._fields_}
+
+
+def workspace_size(q, k_pool, v_pool, block_table, seq_lens, **kw) -> int:
+    return plan(q, k_pool, v_pool, block_table, seq_lens, **kw)["workspace_bytes"]
+
+
+def debug_gather(which: int, dst, q, k_pool, v_pool, block_table, seq_lens, *, window=0, max_seq_len=None,
+                 stream=None):
+    """Raw cache rows the kernels load, in logical key order: dst [B, dst_tokens, Hkv, D]."""
+    lib = _lib.load()
+    _require(dst.is_cuda and dst.is_contiguous() and dst.dtype == k_pool.dtype and dst.dim() == 4,
+             "dst must be a contiguous [B, dst_tokens, Hkv, D] tensor of the cache dtype")
+    a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=1.0,
+                    max_seq_len=max_seq_len, k_scale=None, v_scale=None, num_splits=0, debug_visits=None)
+    rc = lib.pa_debug_gather(ctypes.byref(a), int(which), ctypes.c_void_p(dst.data_ptr()), dst.shape[1],
+                             ctypes.c_void_p(_stream_handle(stream)))
+    _lib.check(rc)
+    return dst
+
+
+class Prepared:
+    """A call whose arguments are marshalled once and launched many times.
+
+    Pointers, shapes and the workspace are fixed at construction (the
+    tiniestgpt notes' rule for replaying a decode step: static buffers, no
+    host sync per step); ``launch`` only enqueues the kernels on a stream.
+    The tensors must stay alive and keep their storage while this object is
+    used.
+    """
+
+    def __init__(self, entry: str, out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None,
+                 max_seq_len=None, k_scale=None, v_scale=None, num_splits=0, workspace=None):
+        self._lib = _lib.load()
+        self._fn = getattr(self._lib, {"decode": "pa_decode", "decode_int8": "pa_decode_int8",
+                                       "verify": "pa_verify"}[entry])
+        self.args = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
+                                max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale,
+                                num_splits=num_splits, debug_visits=None)
+        self.workspace = _attach_workspace(self.args, workspace, q.device)
+        self._keep = (out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale)
+
+    def launch(self, stream=None, timing=None) -> None:
+        if timing is not None:
+            self.args.timing_start = ctypes.c_void_p(timing[0].cuda_event)
+            self.args.timing_stop = ctypes.c_void_p(timing[1].cuda_event)
+        else:
+            self.args.timing_start = None
+            self.args.timing_stop = None
+        _lib.check(self._fn(ctypes.byref(self.args), ctypes.c_void_p(_stream_handle(stream))))
+
+
+__all__.append("Prepared")

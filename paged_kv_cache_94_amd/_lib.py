@@ -1,0 +1,106 @@
+"""ctypes view of libpa.so (include/pa.h). Marshalling only, no compute."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify",
+            "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version")
+
+
+class PaArgs(ctypes.Structure):
+    _fields_ = [
+        ("out", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("debug_visits", ctypes.c_void_p),
+        ("timing_start", ctypes.c_void_p),
+        ("timing_stop", ctypes.c_void_p),
+    ]
+
+
+class PaPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("waves_per_group", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("blocks_per_split", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class PaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libpa.so. Raises if it has not been built: there is no fallback."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_94_amd.build` "
+                               "(the paged-attention kernels have no CPU or PyTorch fallback)")
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(PaArgs)
+        lib.pa_workspace_size.argtypes = [P]
+        lib.pa_workspace_size.restype = ctypes.c_size_t
+        lib.pa_plan.argtypes = [P, ctypes.POINTER(PaPlanInfo)]
+        lib.pa_plan.restype = ctypes.c_int
+        for name in ("pa_decode", "pa_decode_int8", "pa_verify"):
+            fn = getattr(lib, name)
+            fn.argtypes = [P, ctypes.c_void_p]
+            fn.restype = ctypes.c_int
+        lib.pa_debug_gather.argtypes = [P, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.pa_debug_gather.restype = ctypes.c_int
+        lib.pa_strerror.argtypes = [ctypes.c_int]
+        lib.pa_strerror.restype = ctypes.c_char_p
+        lib.pa_last_error.restype = ctypes.c_char_p
+        lib.pa_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def check(rc: int) -> None:
+    if rc != PA_OK:
+        lib = load()
+        detail = lib.pa_last_error().decode() or lib.pa_strerror(rc).decode()
+        raise PaError(rc, detail)

@@ -1,0 +1,294 @@
+// pa_api.cpp -- the C entry points declared in include/pa.h: argument
+// checks, the launch plan (kernel family, context splits, workspace) and
+// the launches. Host code only; the kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pa.h"
+#include "pa_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+// Compute units per device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+struct Plan {
+  int kernel = 0;       // 0 valu, 1 mfma
+  int rows = 0;         // G * q_len
+  int rows_t = 0;       // compiled rows (valu) or 16 * row tiles (mfma)
+  int row_tiles = 0;
+  int nw = 4;
+  int splits = 1;
+  int bps = 1;
+  int n_blk_max = 0;
+  int64_t grid = 0;
+  size_t ws_bytes = 0;
+};
+
+enum Entry { kDecode, kDecodeInt8, kVerify, kAny, kGather };
+
+int validate(const pa_args* a, Entry entry) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (a->q_len < 1) return fail(PA_ERR_INVALID_ARG, "q_len must be >= 1 (got %d)", a->q_len);
+  if ((entry == kDecode || entry == kDecodeInt8) && a->q_len != 1)
+    return fail(PA_ERR_INVALID_ARG, "single-token decode needs q_len == 1 (got %d); use pa_verify", a->q_len);
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->block_size != pa::kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", a->block_size);
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+  if (a->q_dtype != PA_F32 && a->q_dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "q_dtype must be PA_F32 or PA_BF16");
+  if (a->kv_dtype != PA_F32 && a->kv_dtype != PA_BF16 && a->kv_dtype != PA_INT8)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be PA_F32, PA_BF16 or PA_INT8");
+  if (entry == kDecode && a->kv_dtype == PA_INT8)
+    return fail(PA_ERR_INVALID_ARG, "int8 caches go through pa_decode_int8");
+  if (entry == kDecodeInt8 && (a->kv_dtype != PA_INT8 || a->q_dtype != PA_BF16))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_int8 needs q_dtype PA_BF16 and kv_dtype PA_INT8");
+  if (entry != kGather && a->kv_dtype == PA_INT8 && (!a->k_scale || !a->v_scale))
+    return fail(PA_ERR_INVALID_ARG, "int8 cache needs k_scale and v_scale");
+  if (a->kv_dtype != PA_INT8 && a->kv_dtype != a->q_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "a floating-point cache must have the query's dtype");
+  if (a->kv_dtype == PA_INT8 && a->q_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "an int8 cache needs bf16 queries");
+  if (!std::isfinite(a->scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (a->num_blocks < 1 || a->max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be >= 1");
+  if (a->max_seq_len < a->q_len)
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= q_len (%d)", a->max_seq_len, a->q_len);
+  if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len (%d) exceeds max_blocks_per_seq * block_size", a->max_seq_len);
+  if (a->num_splits < 0) return fail(PA_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (a->num_seqs > 0 && (!a->out || !a->q || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens))
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  return PA_OK;
+}
+
+int make_plan(const pa_args* a, Plan* pl) {
+  const int G = a->num_q_heads / a->num_kv_heads;
+  const int D = a->head_dim;
+  Plan P;
+  P.rows = G * a->q_len;
+  const int valu_max_rows = 512 / D;   // query rows the vector kernel keeps in registers
+  if (a->kv_dtype == PA_INT8 || (a->q_dtype == PA_BF16 && P.rows > valu_max_rows)) {
+    P.kernel = 1;
+    P.row_tiles = (P.rows + 15) / 16;
+    P.rows_t = 16 * P.row_tiles;
+    if (P.row_tiles > 2 || (P.row_tiles == 2 && D > 128))
+      return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel supports up to 32 query rows per KV head (D <= 128) "
+                  "or 16 (D = 256); got %d rows, D = %d", P.rows, D);
+  } else {
+    if (P.rows > valu_max_rows)
+      return fail(PA_ERR_UNSUPPORTED, "fp32 path supports at most %d query rows per KV head at D = %d (got %d)",
+                  valu_max_rows, D, P.rows);
+    P.kernel = 0;
+    P.rows_t = 1;
+    while (P.rows_t < P.rows) P.rows_t *= 2;
+  }
+  P.nw = 4;
+
+  const int bs = a->block_size;
+  int n_blk_max = (a->max_seq_len + bs - 1) / bs;
+  if (a->window > 0) {
+    const int64_t span = (int64_t)a->window + a->q_len - 1;   // keys the step can see
+    const int64_t blocks = (span + bs - 2) / bs + 1;         // worst alignment
+    if (blocks < n_blk_max) n_blk_max = (int)blocks;
+  }
+  if (n_blk_max < 1) n_blk_max = 1;
+  P.n_blk_max = n_blk_max;
+
+  const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
+  int S;
+  if (a->num_splits > 0) {
+    S = a->num_splits < n_blk_max ? a->num_splits : n_blk_max;
+  } else {
+    // Aim for about two rounds of resident wavefronts (8 per CU), at least
+    // two blocks per wavefront; a short context is not split.
+    const int64_t target_waves = (int64_t)cu_count() * 8 * 2;
+    const int64_t total_blocks = units * n_blk_max;
+    int64_t bpw = (total_blocks + target_waves - 1) / (target_waves > 0 ? target_waves : 1);
+    if (bpw < 2) bpw = 2;
+    const int64_t bps = bpw * P.nw;
+    S = (int)((n_blk_max + bps - 1) / bps);
+    if (S < 1) S = 1;
+  }
+  P.bps = (n_blk_max + S - 1) / S;
+  P.splits = (n_blk_max + P.bps - 1) / P.bps;
+  P.grid = units * P.splits;
+  if (P.grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
+  P.ws_bytes = P.splits > 1 ? (size_t)units * P.splits * P.rows * (size_t)(D + 2) * sizeof(float) : 0;
+  *pl = P;
+  return PA_OK;
+}
+
+pa::Params make_params(const pa_args* a, const Plan& P) {
+  pa::Params p{};
+  p.out = a->out;
+  p.q = a->q;
+  p.k_pool = a->k_pool;
+  p.v_pool = a->v_pool;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  const size_t acc_bytes = (size_t)a->num_seqs * a->num_kv_heads * P.splits * P.rows * a->head_dim * sizeof(float);
+  p.ws_acc = P.ws_bytes ? reinterpret_cast<float*>(a->workspace) : nullptr;
+  p.ws_ml = P.ws_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + acc_bytes) : nullptr;
+  p.visits = a->debug_visits;
+  p.B = a->num_seqs;
+  p.q_len = a->q_len;
+  p.Hq = a->num_q_heads;
+  p.Hkv = a->num_kv_heads;
+  p.G = a->num_q_heads / a->num_kv_heads;
+  p.rows = P.rows;
+  p.maxb = a->max_blocks_per_seq;
+  p.window = a->window;
+  p.scale_log2 = a->scale * pa::kLog2e;
+  p.splits = P.splits;
+  p.bps = P.bps;
+  return p;
+}
+
+int run(const pa_args* a, pa_stream_t stream, Entry entry) {
+  g_last_error.clear();
+  int rc = validate(a, entry);
+  if (rc) return rc;
+  Plan P;
+  rc = make_plan(a, &P);
+  if (rc) return rc;
+  if (a->num_seqs == 0) return PA_OK;
+  if (P.ws_bytes) {
+    if (!a->workspace || a->workspace_bytes < P.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", P.ws_bytes,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(a->workspace) % 16)
+      return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  const pa::Params p = make_params(a, P);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (a->timing_start && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(a->timing_start), st)) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  bool supported = false;
+  if (P.kernel == 0)
+    e = pa::launch_valu(p, a->q_dtype, a->kv_dtype, a->head_dim, P.rows_t, P.nw, (int)P.grid, st, &supported);
+  else
+    e = pa::launch_mfma(p, a->kv_dtype, a->head_dim, P.row_tiles, P.nw, (int)P.grid, st, &supported);
+  if (!supported)
+    return fail(PA_ERR_UNSUPPORTED, "no kernel built for D=%d rows=%d q_dtype=%d kv_dtype=%d", a->head_dim, P.rows,
+                a->q_dtype, a->kv_dtype);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
+  if (a->timing_stop && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(a->timing_stop), st)) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if (P.splits > 1) {
+    e = pa::launch_combine(p, a->q_dtype, a->head_dim, st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_workspace_size(const pa_args* a) {
+  g_last_error.clear();
+  if (validate(a, kAny)) return (size_t)-1;
+  Plan P;
+  if (make_plan(a, &P)) return (size_t)-1;
+  return P.ws_bytes;
+}
+
+int pa_plan(const pa_args* a, pa_plan_info* info) {
+  g_last_error.clear();
+  if (!info) return fail(PA_ERR_INVALID_ARG, "info is NULL");
+  int rc = validate(a, kAny);
+  if (rc) return rc;
+  Plan P;
+  rc = make_plan(a, &P);
+  if (rc) return rc;
+  info->kernel = P.kernel;
+  info->rows = P.rows;
+  info->waves_per_group = P.nw;
+  info->splits = P.splits;
+  info->blocks_per_split = P.bps;
+  info->grid = (int32_t)P.grid;
+  info->workspace_bytes = P.ws_bytes;
+  return PA_OK;
+}
+
+int pa_decode(const pa_args* a, pa_stream_t stream) { return run(a, stream, kDecode); }
+int pa_decode_int8(const pa_args* a, pa_stream_t stream) { return run(a, stream, kDecodeInt8); }
+int pa_verify(const pa_args* a, pa_stream_t stream) { return run(a, stream, kVerify); }
+
+int pa_debug_gather(const pa_args* a, int32_t which, void* dst, int64_t dst_tokens, pa_stream_t stream) {
+  g_last_error.clear();
+  int rc = validate(a, kGather);
+  if (rc) return rc;
+  if (which != 0 && which != 1) return fail(PA_ERR_INVALID_ARG, "which must be 0 (keys) or 1 (values)");
+  if (a->num_seqs > 0 && !dst) return fail(PA_ERR_INVALID_ARG, "dst is NULL");
+  // The widest visible key range a sequence can have; dst must hold it.
+  int64_t need = a->max_seq_len;
+  if (a->window > 0 && (int64_t)a->window + a->q_len - 1 < need) need = (int64_t)a->window + a->q_len - 1;
+  if (dst_tokens < need)
+    return fail(PA_ERR_INVALID_ARG, "dst_tokens (%lld) must be >= %lld", (long long)dst_tokens, (long long)need);
+  if (a->num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "debug gather handles at most 65535 sequences");
+  if (a->num_seqs == 0) return PA_OK;
+  Plan P;
+  rc = make_plan(a, &P);
+  if (rc) return rc;
+  const pa::Params p = make_params(a, P);
+  hipError_t e = pa::launch_gather(p, a->kv_dtype, a->head_dim, which, dst, dst_tokens,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "gather kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+const char* pa_strerror(int code) {
+  switch (code) {
+    case PA_OK: return "success";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown error";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_version(void) { return 100; }
+
+}  // extern "C"

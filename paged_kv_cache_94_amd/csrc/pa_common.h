@@ -1,0 +1,84 @@
+// pa_common.h -- the part of every attention kernel that follows the block
+// loop: merging the wavefronts of a workgroup and writing either the final
+// output or the split partials, plus the list of kernel entry points the
+// host dispatcher instantiates.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+// Merge NW wavefront states through LDS and write the result.
+//
+// Each wavefront contributes, per query row r < ROWS, its running max m[r]
+// (log2 units), its running sum l[r] and its unnormalised accumulator
+// acc[r][0..D); merging uses the online-softmax rule (Lab 5 handout, "Flash
+// Attention": rescale by 2^(m_w - M) before adding, O = o / l at the end).
+//
+// lds_acc: [NW][ROWS][D] floats, lds_ml: [NW][ROWS][2] floats. The caller
+// has already stored its share and the merge starts with a barrier.
+// split == -1 writes out = o / l in OutT; otherwise (m, l, o) go to the
+// workspace slot of this split.
+template <typename OutT, int D, int ROWS, int NW>
+__device__ __forceinline__ void merge_and_store(const Params& p, const float* lds_acc, const float* lds_ml,
+                                                int32_t b, int32_t g, int32_t split) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int rows = p.rows;
+  const int32_t unit = b * p.Hkv + g;
+  for (int idx = tid; idx < ROWS * D; idx += NW * 64) {
+    const int r = idx / D;
+    const int d = idx % D;
+    if (r >= rows) break;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[(w * ROWS + r) * 2]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = lds_ml[(w * ROWS + r) * 2];
+        const float s = fast_exp2(mw - M);
+        num += s * lds_acc[(w * ROWS + r) * D + d];
+        den += s * lds_ml[(w * ROWS + r) * 2 + 1];
+      }
+    }
+    if (split < 0) {
+      const int t = r / p.G;
+      const int h = g * p.G + r % p.G;
+      OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D;
+      const float v = num / den;
+      if constexpr (sizeof(OutT) == 4) {
+        out[d] = v;
+      } else {
+        out[d] = (__bf16)v;
+      }
+    } else {
+      const size_t slot = ((size_t)unit * p.splits + split) * rows + r;
+      p.ws_acc[slot * D + d] = num;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = M;
+        p.ws_ml[slot * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+}  // namespace pa
+
+// Host-side launchers, one per kernel family (defined in the .hip files).
+namespace pa {
+struct LaunchShape {
+  int kernel;   // 0 valu, 1 mfma
+  int rows_t;   // compiled row count (>= rows)
+  int nw;       // waves per workgroup
+  int grid;     // workgroups
+};
+hipError_t launch_valu(const Params& p, int q_dtype, int kv_dtype, int D, int rows_t, int nw, int grid,
+                       hipStream_t st, bool* supported);
+hipError_t launch_mfma(const Params& p, int kv_dtype, int D, int row_tiles, int nw, int grid,
+                       hipStream_t st, bool* supported);
+hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st);
+hipError_t launch_gather(const Params& p, int kv_dtype, int D, int which, void* dst, int64_t dst_tokens,
+                         hipStream_t st);
+}  // namespace pa

@@ -1,0 +1,276 @@
+// pa_valu.hip -- vector-ALU paged decode attention for small query groups
+// (rows = (Hq/Hkv) * q_len <= 512 / D) over fp32 or bf16 caches.
+//
+// One workgroup owns one (sequence, KV head, context split); its NW
+// wavefronts take the split's logical blocks round-robin. Per block a
+// wavefront reads the 16 cached rows of its KV head straight from HBM into
+// registers: eight lanes cover one 128-byte line of a row with 16-byte
+// loads, so one load instruction moves 8 rows x 128 B and a 16-token block
+// is 2 x (row bytes / 128) instructions per tensor. The K rows are used
+// for every query row of the group from registers (grouped-query attention,
+// Lab 5 handout: heads share K/V without repeating them).
+//
+// Scores: each lane dots its slice of the row with the matching slice of
+// every query row (bf16 pairs through v_dot2, fp32 through FMA), then an
+// octet sum over DPP (quad_perm x2 + half-row mirror) gives every lane of
+// the octet the full score. The online softmax (Lab 5 handout, "Flash
+// Attention": running max m, running sum l, unnormalised output o, O = o/l;
+// base-2 exponents, fp32 state) rescales o only when a row's max grows. A
+// key no query may see is removed by select, never by multiplying with 0,
+// so garbage in unused slots cannot leak in.
+#include "pa_common.h"
+
+namespace pa {
+
+template <bool BF16, int D, int ROWS, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+pa_valu_kernel(const Params p) {
+  constexpr int EB = BF16 ? 2 : 4;          // bytes per cache element
+  constexpr int ROW_BYTES = D * EB;
+  constexpr int LPT = 8;                    // lanes per 128-byte line of a row
+  constexpr int TPI = 64 / LPT;             // rows per load instruction
+  constexpr int TPL = kBlock / TPI;         // rows per lane per block
+  constexpr int COLS = ROW_BYTES / (LPT * 16);
+  constexpr int EPC = 16 / EB;              // elements per 16-byte chunk
+  static_assert(COLS >= 1 && ROW_BYTES % (LPT * 16) == 0, "row must be whole 128-byte lines");
+
+  __shared__ float lds_acc[NW * ROWS * D];
+  __shared__ float lds_ml[NW * ROWS * 2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tsub = lane / LPT;
+  const int part = lane % LPT;
+
+  const int32_t g = blockIdx.x % p.Hkv;
+  const int32_t bsplit = blockIdx.x / p.Hkv;
+  const int32_t b = bsplit % p.B;
+  const int32_t split = bsplit / p.B;
+
+  const int32_t L = p.seq_lens[b];
+  if (!len_ok(L, p)) return;   // broken precondition: touch nothing outside the arrays
+  const KeyRange kr = key_range(L, p.q_len, p.window);
+  const int32_t first = kr.blk_lo + split * p.bps;
+  if (first > kr.blk_hi) return;
+  const int32_t last = min(kr.blk_hi, first + p.bps - 1);
+
+  // Query slices: row r = t * G + gi is query token t of head g*G + gi.
+  uint32_t qw[ROWS][COLS][4];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    if (r < p.rows) {
+      const int t = r / p.G;
+      const int h = g * p.G + r % p.G;
+      const char* qrow = reinterpret_cast<const char*>(p.q) + (((size_t)b * p.q_len + t) * p.Hq + h) * ROW_BYTES;
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) {
+        const uint4 v = load16(qrow + c * LPT * 16 + part * 16);
+        qw[r][c][0] = v.x; qw[r][c][1] = v.y; qw[r][c][2] = v.z; qw[r][c][3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) qw[r][c][0] = qw[r][c][1] = qw[r][c][2] = qw[r][c][3] = 0u;
+    }
+  }
+
+  float m[ROWS], l[ROWS], acc[ROWS][COLS][EPC];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[r][c][e] = 0.f;
+  }
+
+  // Per-row visibility bounds: row r sees keys [lo_r, p0 + t_r].
+  int32_t row_lo[ROWS], row_hi[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int t = r / p.G;
+    row_lo[r] = first_key(kr.p0, t, p.window);
+    row_hi[r] = r < p.rows ? kr.p0 + t : -1;
+  }
+
+  const size_t tok_stride = (size_t)p.Hkv * ROW_BYTES;
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES + part * 16;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES + part * 16;
+  const int32_t* table = p.block_table + (size_t)b * p.maxb;
+  int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
+
+  for (int32_t i = first + wave; i <= last; i += NW) {
+    const int32_t phys = table[i];
+    const size_t blk_off = (size_t)phys * kBlock * tok_stride;
+    uint4 kr_[TPL][COLS], vr_[TPL][COLS];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) kr_[u][c] = load16(kbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) vr_[u][c] = load16(vbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+    if (visits && lane == 0) atomicAdd(visits + i, 1);
+
+    // q . k for every (row slot u, query row r), summed over the octet.
+    float s[TPL][ROWS];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float acc_s = 0.f;
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+          const uint32_t kw[4] = {kr_[u][c].x, kr_[u][c].y, kr_[u][c].z, kr_[u][c].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if constexpr (BF16) {
+              acc_s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[r][c][w]),
+                                                      __builtin_bit_cast(bf16x2, kw[w]), acc_s, false);
+            } else {
+              acc_s = fmaf(__builtin_bit_cast(float, qw[r][c][w]), __builtin_bit_cast(float, kw[w]), acc_s);
+            }
+          }
+        }
+        s[u][r] = octet_sum(acc_s);
+      }
+
+    // Mask by select, scale to base-2 exponent units, per-row block max.
+    bool tok_ok[TPL];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int32_t j = i * kBlock + tsub + TPI * u;
+      tok_ok[u] = j < L && j >= kr.lo0;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const bool ok = j <= row_hi[r] && j >= row_lo[r];
+        s[u][r] = ok ? s[u][r] * p.scale_log2 : -INFINITY;
+      }
+    }
+
+    float pr[TPL][ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      float mb = s[0][r];
+#pragma unroll
+      for (int u = 1; u < TPL; ++u) mb = fmaxf(mb, s[u][r]);
+      mb = octets_max(mb);
+      const float mn = fmaxf(m[r], mb);
+      if (__builtin_amdgcn_readfirstlane((int)(mn > m[r]))) {
+        const float a = fast_exp2(m[r] - mn);   // 0 when m was -inf
+        l[r] *= a;
+#pragma unroll
+        for (int c = 0; c < COLS; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[r][c][e] *= a;
+        m[r] = mn;
+      }
+      const float msafe = m[r] == -INFINITY ? 0.f : m[r];
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        pr[u][r] = fast_exp2(s[u][r] - msafe);
+        l[r] += pr[u][r];
+      }
+    }
+
+    // o += p * v; rows no query may see are zeroed first (they may hold anything).
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) {
+        const uint32_t vw[4] = {tok_ok[u] ? vr_[u][c].x : 0u, tok_ok[u] ? vr_[u][c].y : 0u,
+                                tok_ok[u] ? vr_[u][c].z : 0u, tok_ok[u] ? vr_[u][c].w : 0u};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (BF16) {
+            const float lo = bf16_lo(vw[w]);
+            const float hi = bf16_hi(vw[w]);
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+              acc[r][c][2 * w] = fmaf(pr[u][r], lo, acc[r][c][2 * w]);
+              acc[r][c][2 * w + 1] = fmaf(pr[u][r], hi, acc[r][c][2 * w + 1]);
+            }
+          } else {
+            const float v = __builtin_bit_cast(float, vw[w]);
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) acc[r][c][w] = fmaf(pr[u][r], v, acc[r][c][w]);
+          }
+        }
+      }
+  }
+
+  // Sum the eight octets (different rows, same slices), then hand off to LDS.
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    l[r] = octets_sum(l[r]);
+#pragma unroll
+    for (int c = 0; c < COLS; ++c)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[r][c][e] = octets_sum(acc[r][c][e]);
+  }
+  if (tsub == 0) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int c = 0; c < COLS; ++c)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) lds_acc[(wave * ROWS + r) * D + c * LPT * EPC + part * EPC + e] = acc[r][c][e];
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        lds_ml[(wave * ROWS + r) * 2] = m[r];
+        lds_ml[(wave * ROWS + r) * 2 + 1] = l[r];
+      }
+    }
+  }
+  if constexpr (BF16) {
+    merge_and_store<__bf16, D, ROWS, NW>(p, lds_acc, lds_ml, b, g, p.splits > 1 ? split : -1);
+  } else {
+    merge_and_store<float, D, ROWS, NW>(p, lds_acc, lds_ml, b, g, p.splits > 1 ? split : -1);
+  }
+}
+
+namespace {
+template <bool BF16, int D, int ROWS>
+hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, bool* ok) {
+  if (nw != 4) {
+    *ok = false;
+    return hipSuccess;
+  }
+  *ok = true;
+  hipLaunchKernelGGL((pa_valu_kernel<BF16, D, ROWS, 4>), dim3(grid), dim3(4 * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t by_rows(const Params& p, int rows_t, int nw, int grid, hipStream_t st, bool* ok) {
+  // Query rows live in registers next to a row slice of D/8 elements: keep rows * D / 8 <= 64.
+  switch (rows_t) {
+    case 1: return launch_one<BF16, D, 1>(p, nw, grid, st, ok);
+    case 2: return launch_one<BF16, D, 2>(p, nw, grid, st, ok);
+    case 4: if constexpr (D <= 128) return launch_one<BF16, D, 4>(p, nw, grid, st, ok); break;
+    case 8: if constexpr (D <= 64) return launch_one<BF16, D, 8>(p, nw, grid, st, ok); break;
+  }
+  *ok = false;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_valu(const Params& p, int q_dtype, int kv_dtype, int D, int rows_t, int nw, int grid,
+                       hipStream_t st, bool* supported) {
+  *supported = false;
+  const bool bf16 = kv_dtype == 1;
+  if (q_dtype != kv_dtype || kv_dtype > 1) return hipSuccess;
+  switch (D) {
+    case 64: return bf16 ? by_rows<true, 64>(p, rows_t, nw, grid, st, supported)
+                         : by_rows<false, 64>(p, rows_t, nw, grid, st, supported);
+    case 128: return bf16 ? by_rows<true, 128>(p, rows_t, nw, grid, st, supported)
+                          : by_rows<false, 128>(p, rows_t, nw, grid, st, supported);
+    case 256: return bf16 ? by_rows<true, 256>(p, rows_t, nw, grid, st, supported)
+                          : by_rows<false, 256>(p, rows_t, nw, grid, st, supported);
+  }
+  return hipSuccess;
+}
+
+}  // namespace pa

@@ -1,0 +1,163 @@
+"""The C ABI without a GPU: exported symbols, struct layout, argument checks.
+
+No kernel is launched here: every call below fails validation (or only
+plans) before the library touches the device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from paged_kv_cache_94_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_94_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n)
+
+
+def test_struct_layout_matches_header():
+    src = r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "pa.h"
+#define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("pa_args.size %zu\n", sizeof(pa_args));
+  printf("pa_plan_info.size %zu\n", sizeof(pa_plan_info));
+  %FIELDS%
+  return 0;
+}
+'''
+    fields = "".join(f"F(pa_args, {f})" for f, _ in _lib.PaArgs._fields_)
+    fields += "".join(f"F(pa_plan_info, {f})" for f, _ in _lib.PaPlanInfo._fields_)
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        open(c, "w").write(src.replace("%FIELDS%", fields))
+        exe = os.path.join(d, "layout")
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = dict(line.split() for line in subprocess.run([exe], capture_output=True, text=True,
+                                                            check=True).stdout.splitlines())
+    assert int(got["pa_args.size"]) == ctypes.sizeof(_lib.PaArgs)
+    assert int(got["pa_plan_info.size"]) == ctypes.sizeof(_lib.PaPlanInfo)
+    for f, _ in _lib.PaArgs._fields_:
+        assert int(got[f"pa_args.{f}"]) == getattr(_lib.PaArgs, f).offset, f
+    for f, _ in _lib.PaPlanInfo._fields_:
+        assert int(got[f"pa_plan_info.{f}"]) == getattr(_lib.PaPlanInfo, f).offset, f
+
+
+def _args(**kw):
+    a = _lib.PaArgs()
+    base = dict(out=8, q=8, k_pool=8, v_pool=8, block_table=8, seq_lens=8, num_seqs=4, q_len=1, num_q_heads=16,
+                num_kv_heads=8, head_dim=256, block_size=16, num_blocks=1000, max_blocks_per_seq=512,
+                max_seq_len=8192, window=1024, scale=0.0625, q_dtype=_lib.PA_BF16, kv_dtype=_lib.PA_BF16)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+BAD = [
+    (dict(q_len=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(q_len=2), _lib.PA_ERR_INVALID_ARG),            # pa_decode is single-token
+    (dict(num_q_heads=12, num_kv_heads=8), _lib.PA_ERR_INVALID_ARG),
+    (dict(head_dim=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(block_size=32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=_lib.PA_INT8), _lib.PA_ERR_INVALID_ARG),
+    (dict(kv_dtype=_lib.PA_F32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARG),
+    (dict(max_seq_len=9000), _lib.PA_ERR_INVALID_ARG),
+    (dict(q=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), _lib.PA_ERR_INVALID_ARG),
+    (dict(q_dtype=_lib.PA_F32, kv_dtype=_lib.PA_F32, head_dim=256, num_q_heads=64, num_kv_heads=8),
+     _lib.PA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(k) for k, _ in BAD])
+def test_decode_rejects_bad_arguments(lib, kw, code):
+    a = _args(**kw)
+    assert lib.pa_decode(ctypes.byref(a), None) == code
+    assert lib.pa_last_error()
+
+
+def test_int8_entry_rules(lib):
+    a = _args(kv_dtype=_lib.PA_INT8)          # scales missing
+    assert lib.pa_decode_int8(ctypes.byref(a), None) == _lib.PA_ERR_INVALID_ARG
+    b = _args()                               # bf16 cache through the int8 entry
+    assert lib.pa_decode_int8(ctypes.byref(b), None) == _lib.PA_ERR_INVALID_ARG
+
+
+def test_workspace_is_required_when_split(lib):
+    a = _args(num_splits=4, max_seq_len=8192, window=0)
+    need = lib.pa_workspace_size(ctypes.byref(a))
+    assert need == 4 * 8 * 4 * 2 * (256 + 2) * 4
+    assert lib.pa_decode(ctypes.byref(a), None) == _lib.PA_ERR_WORKSPACE
+
+
+def test_plan_choices(lib):
+    info = _lib.PaPlanInfo()
+    # Gemma4 local layer: 2 rows per KV head on the vector ALU.
+    assert lib.pa_plan(ctypes.byref(_args(num_seqs=32)), ctypes.byref(info)) == 0
+    assert info.kernel == 0 and info.rows == 2
+    # Global layer: 16 query heads on one KV head go to the matrix cores.
+    assert lib.pa_plan(ctypes.byref(_args(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768,
+                                          max_blocks_per_seq=2048)), ctypes.byref(info)) == 0
+    assert info.kernel == 1 and info.rows == 16 and info.splits > 1
+    # Verify step: 4 heads x 5 tokens = 20 rows.
+    assert lib.pa_plan(ctypes.byref(_args(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                          window=0, max_seq_len=16384, max_blocks_per_seq=1024)),
+                       ctypes.byref(info)) == 0
+    assert info.kernel == 1 and info.rows == 20
+    # A forced split count is honoured (capped by the blocks a sequence can span).
+    assert lib.pa_plan(ctypes.byref(_args(num_splits=3)), ctypes.byref(info)) == 0
+    assert info.splits == 3
+
+
+def test_zero_sequences_enqueue_nothing(lib):
+    a = _args(num_seqs=0, out=0, q=0, k_pool=0, v_pool=0, block_table=0, seq_lens=0)
+    assert lib.pa_decode(ctypes.byref(a), None) == 0
+
+
+def test_strerror(lib):
+    for code in range(5):
+        assert lib.pa_strerror(code)
+    assert lib.pa_version() >= 100
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
+        _lib._lib_backup = _lib._lib
+        try:
+            _lib._lib = None
+            _lib.load(str(tmp_path / "absent.so"))
+        finally:
+            _lib._lib = _lib._lib_backup

@@ -1,0 +1,218 @@
+"""GPU parity: libpa (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs, poisons every slot a correct kernel must not
+use (NaN values / NaN int8 scales; unused table entries point at a NaN
+block), runs the HIP path and compares element by element with the oracle:
+max |err| <= 1e-5 for fp32 and <= 1e-2 for bf16 and int8 caches. The block
+visit log and the debug gather must match the oracle bit for bit.
+"""
+
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_94_amd as pa
+from tests.gpu_util import TOL, Dev, max_err
+from workloads import make_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _oracle(x, rows=None):
+    return oracle.attention(oracle.Problem.from_inputs(x), rows=rows)
+
+
+# --- the five named workloads at full size, in the benchmark's launch plan -------------------
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_named_config_full_size(idx):
+    x = make_config(idx, poison=True)
+    _log(f"config {idx} {x.name}: B={x.batch} lens {x.seq_lens.min()}..{x.seq_lens.max()}")
+    dev = Dev(x)
+    got = dev.run_f64()
+    ref = _oracle(x)
+    assert not np.isnan(got).any()
+    err = max_err(got, ref)
+    _log(f"config {idx}: max|err| = {err:.3e}")
+    assert err <= TOL[x.kv_dtype if x.kv_dtype != "f32" else "f32"]
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_named_config_visits_bit_exact(idx):
+    x = make_config(idx, batch=None if idx < 5 else 64, poison=True)
+    dev = Dev(x)
+    visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
+    dev.run(debug_visits=visits)
+    got = visits.cpu().numpy()
+    expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
+    np.testing.assert_array_equal(got, np.broadcast_to(expect[:, None, :], got.shape))
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_named_config_gather_bit_exact(idx):
+    x = make_config(idx, batch={1: None, 2: None, 3: 6, 4: 16, 5: 8}[idx], poison=True)
+    dev = Dev(x)
+    tokens = x.max_seq_len if x.window <= 0 else min(x.max_seq_len, x.window + x.q_len - 1)
+    p = oracle.Problem.from_inputs(x)
+    for which, pool in ((0, dev.k), (1, dev.v)):
+        dst = torch.zeros((x.batch, tokens, x.num_kv_heads, x.head_dim), dtype=pool.dtype, device="cuda")
+        pa.debug_gather(which, dst, dev.q, dev.k, dev.v, dev.table, dev.lens, window=x.window,
+                        max_seq_len=x.max_seq_len)
+        torch.cuda.synchronize()
+        got = dst.cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if pool.dtype == torch.bfloat16 else got.numpy()
+        expect = oracle.gather(p, which, tokens, fill=0)
+        np.testing.assert_array_equal(got.view(np.uint8), expect.view(np.uint8))
+
+
+# --- small problems: several tiles, ragged tails, every kernel family ---------------------------
+
+# (lens, q_len, Hq, Hkv, D, window, q_dtype, kv_dtype, alias)
+SMALL = [
+    ([37, 70], 1, 4, 2, 64, 0, "f32", "f32", False),
+    ([1, 2, 15, 16, 17, 31, 33, 200], 1, 4, 4, 64, 0, "f32", "f32", False),
+    ([5, 100, 300], 1, 8, 1, 64, 37, "f32", "f32", False),          # 8 rows on the fp32 vector path
+    ([129, 64, 250], 1, 8, 2, 128, 0, "f32", "f32", False),
+    ([77, 250, 513], 1, 2, 1, 256, 0, "f32", "f32", False),
+    ([700, 33, 1025, 16], 1, 16, 8, 256, 64, "bf16", "bf16", False),  # local layer shape
+    ([900, 17], 1, 16, 8, 256, 1, "bf16", "bf16", False),
+    ([400, 401, 402], 1, 8, 8, 128, 0, "bf16", "bf16", False),
+    ([400, 3, 99], 1, 16, 4, 128, 50, "bf16", "bf16", False),
+    ([300, 1000, 47], 1, 16, 1, 256, 0, "bf16", "bf16", True),       # global layer shape, V = K
+    ([300, 1000, 47], 1, 16, 1, 256, 0, "bf16", "bf16", False),
+    ([300, 65, 1], 1, 16, 2, 128, 0, "bf16", "bf16", False),
+    ([200, 1, 64], 1, 16, 1, 64, 20, "bf16", "bf16", True),
+    ([1024, 100, 17], 1, 64, 8, 128, 0, "bf16", "int8", False),       # int8 cache, 8 rows
+    ([130, 50], 1, 8, 8, 128, 33, "bf16", "int8", False),           # int8, 1 row
+    ([250, 16], 1, 32, 2, 64, 0, "bf16", "int8", False),
+    ([90, 300], 1, 16, 1, 256, 0, "bf16", "int8", False),
+    ([5, 6, 40, 333], 5, 32, 8, 128, 0, "bf16", "bf16", False),     # verify, 20 rows
+    ([5, 21, 64, 90], 5, 32, 8, 128, 19, "bf16", "bf16", False),
+    ([7, 100], 3, 4, 4, 64, 0, "f32", "f32", False),                # verify on the fp32 path
+    ([12, 80], 2, 16, 2, 128, 0, "bf16", "bf16", False),             # 16 rows
+    ([12, 80], 4, 16, 2, 64, 9, "bf16", "bf16", False),              # 32 rows, D=64
+    ([8, 500], 5, 16, 4, 128, 0, "bf16", "int8", False),             # verify over int8
+]
+
+
+def _ids(c):
+    return "L%s_q%d_h%d-%d_d%d_w%d_%s_%s%s" % ("-".join(map(str, c[0][:4])), c[1], c[2], c[3], c[4], c[5], c[6],
+                                              c[7], "_alias" if c[8] else "")
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_ids)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_small_problems(case, splits):
+    lens, q_len, Hq, Hkv, D, window, qd, kvd, alias = case
+    x = make_inputs(lens, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=qd, kv_dtype=kvd,
+                    window=window, alias_v=alias, poison=True, seed=zlib.crc32(repr((case, splits)).encode()))
+    _log(f"small {_ids(case)} splits={splits}")
+    got = Dev(x).run_f64(num_splits=splits)
+    ref = _oracle(x)
+    assert not np.isnan(got).any()
+    assert max_err(got, ref) <= TOL[kvd]
+
+
+# --- invariants on the GPU path -------------------------------------------------------------------
+
+def test_block_permutation_is_bit_identical():
+    x = make_inputs([700, 33, 1025, 16], q_len=1, num_q_heads=16, num_kv_heads=8, head_dim=256,
+                    q_dtype="bf16", kv_dtype="bf16", window=300, seed=5)
+    base = Dev(x).run_f64()
+    perm = np.random.default_rng(7).permutation(x.num_blocks)
+    k = np.empty_like(x.k_pool)
+    v = np.empty_like(x.v_pool)
+    k[perm] = x.k_pool
+    v[perm] = x.v_pool
+    x.k_pool, x.v_pool = k, v
+    x.block_table = perm[x.block_table].astype(np.int32)
+    np.testing.assert_array_equal(Dev(x).run_f64(), base)
+
+
+def test_shared_kv_matches_separate_copy():
+    x = make_inputs([300, 1000, 47], q_len=1, num_q_heads=16, num_kv_heads=1, head_dim=256, q_dtype="bf16",
+                    kv_dtype="bf16", alias_v=True, seed=6)
+    shared = Dev(x).run_f64()
+    x.v_pool = x.k_pool.copy()
+    separate = Dev(x).run_f64()
+    assert max_err(shared, separate) <= 1e-2
+
+
+def test_verify_rows_match_sequential_decode():
+    x = make_inputs([5, 21, 64, 90], q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                    kv_dtype="bf16", seed=7)
+    dev = Dev(x)
+    full = dev.run_f64()
+    for t in range(5):
+        out = torch.empty_like(dev.q[:, t:t + 1])
+        lens = dev.lens - (4 - t)
+        pa.decode(out, dev.q[:, t:t + 1].contiguous(), dev.k, dev.v, dev.table, lens, window=0, scale=x.scale,
+                  max_seq_len=x.max_seq_len)
+        torch.cuda.synchronize()
+        assert max_err(out.float().cpu().numpy().astype(np.float64)[:, 0], full[:, t]) <= 1e-2
+
+
+def test_int8_path_reduces_to_bf16_on_integer_data():
+    # Unit scales and small integer codes: the int8 path must agree with the bf16
+    # path run on the same integers (exact in bf16), and both with the oracle.
+    from workloads import f32_to_bf16_bits
+    x = make_inputs([90, 300, 17], q_len=1, num_q_heads=64, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                    kv_dtype="int8", seed=8)
+    rng = np.random.default_rng(8)
+    x.k_pool = rng.integers(-3, 4, size=x.k_pool.shape).astype(np.int8)
+    x.v_pool = rng.integers(-3, 4, size=x.v_pool.shape).astype(np.int8)
+    x.k_scale[...] = 1.0
+    x.v_scale[...] = 1.0
+    got8 = Dev(x).run_f64()
+    y = make_inputs([90, 300, 17], q_len=1, num_q_heads=64, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                    kv_dtype="bf16", seed=8)
+    y.q = x.q
+    y.k_pool = f32_to_bf16_bits(x.k_pool.astype(np.float32))
+    y.v_pool = f32_to_bf16_bits(x.v_pool.astype(np.float32))
+    y.block_table = x.block_table
+    gotb = Dev(y).run_f64()
+    ref = _oracle(x)
+    assert max_err(got8, ref) <= 1e-2
+    assert max_err(gotb, ref) <= 1e-2
+
+
+# --- edge cases ------------------------------------------------------------------------------------
+
+def test_zero_sequences():
+    x = make_inputs([5], q_len=1, num_q_heads=4, num_kv_heads=2, head_dim=64, q_dtype="f32", kv_dtype="f32", seed=9)
+    dev = Dev(x)
+    out = torch.empty((0, 1, 4, 64), dtype=torch.float32, device="cuda")
+    pa.decode(out, dev.q[:0], dev.k, dev.v, dev.table[:0], dev.lens[:0], max_seq_len=5)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("window", [1, 2, 15, 16, 17, 63, 64, 65, 1000])
+def test_window_boundaries(window):
+    x = make_inputs([1, 15, 16, 17, 64, 65, 100], q_len=1, num_q_heads=16, num_kv_heads=8, head_dim=256,
+                    q_dtype="bf16", kv_dtype="bf16", window=window, poison=True, seed=10 + window)
+    got = Dev(x).run_f64()
+    assert max_err(got, _oracle(x)) <= 1e-2
+
+
+def test_single_key_returns_value_exactly():
+    x = make_inputs([1, 1, 1], q_len=1, num_q_heads=4, num_kv_heads=2, head_dim=64, q_dtype="f32",
+                    kv_dtype="f32", poison=True, seed=11)
+    got = Dev(x).run_f64()
+    np.testing.assert_array_equal(got, _oracle(x))
+
+
+def test_longest_global_context():
+    # One sequence at the global layer's longest context (32768 tokens), G = 16, V = K.
+    x = make_inputs([32768, 4096], q_len=1, num_q_heads=16, num_kv_heads=1, head_dim=256, q_dtype="bf16",
+                    kv_dtype="bf16", alias_v=True, poison=True, seed=12, max_blocks=2048)
+    got = Dev(x).run_f64()
+    assert max_err(got, _oracle(x)) <= 1e-2

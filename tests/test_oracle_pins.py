@@ -14,6 +14,8 @@
 
 from __future__ import annotations
 
+import zlib
+
 import glob
 import json
 import os
@@ -58,7 +60,7 @@ SDPA_CASES = [
 def test_matches_torch_sdpa(case):
     lens, q_len, Hq, Hkv, D, window, qd, kvd = case
     x = make_inputs(lens, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
-                    q_dtype=qd, kv_dtype=kvd, window=window, seed=hash(str(case)) % 2**31,
+                    q_dtype=qd, kv_dtype=kvd, window=window, seed=zlib.crc32(repr(case).encode()),
                     poison=True)
     got = run(x)
     ref = dense_sdpa(x)
