@@ -92,7 +92,8 @@ typedef struct {
   int32_t q_dtype;            /* PA_F32 or PA_BF16 (also the output type) */
   int32_t kv_dtype;           /* PA_F32, PA_BF16 or PA_INT8 */
   int32_t num_splits;         /* 0: the library picks the context split; > 0: split each sequence's
-                                 key range into at most this many parts */
+                                 key range into this many parts (more if a part would exceed
+                                 64 blocks per wavefront of the chosen kernel) */
   void* workspace;            /* device scratch for split partials, caller-owned; may be NULL
                                  when pa_workspace_size() returns 0 */
   size_t workspace_bytes;     /* size of workspace */
@@ -107,16 +108,20 @@ typedef struct {
   int32_t kernel;             /* 0: vector-ALU kernel, 1: matrix-core (MFMA) kernel */
   int32_t rows;               /* query rows per KV head = (Hq/Hkv) * q_len */
   int32_t waves_per_group;    /* wavefronts cooperating on one (sequence, KV head, split) */
-  int32_t splits;             /* context splits per sequence (1: no combine kernel) */
-  int32_t blocks_per_split;   /* logical blocks per split */
+  int32_t splits;             /* aligned partition: context splits per sequence (1: no combine kernel) */
+  int32_t blocks_per_split;   /* aligned partition: logical blocks per split */
   int32_t grid;               /* workgroups of the attention kernel */
+  int32_t balanced;           /* 1: every workgroup takes an equal share of the flattened
+                                 (sequence, KV head, block) list, cut where a sequence ends;
+                                 0: each workgroup owns one split of one (sequence, KV head) */
   size_t workspace_bytes;     /* == pa_workspace_size() */
 } pa_plan_info;
 
 /*
  * Bytes of workspace the call needs for these arguments (0 when the key
  * range is not split). Depends on the shapes, max_seq_len, window,
- * num_splits and the device's compute-unit count, never on device data.
+ * num_splits, the device's compute-unit count and the tuning variables
+ * PA_WAVES / PA_BLOCKS_PER_WAVE (read at every call), never on device data.
  * Returns (size_t)-1 if the arguments are invalid.
  */
 size_t pa_workspace_size(const pa_args* args);

@@ -56,6 +56,7 @@ class PaPlanInfo(ctypes.Structure):
         ("splits", ctypes.c_int32),
         ("blocks_per_split", ctypes.c_int32),
         ("grid", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

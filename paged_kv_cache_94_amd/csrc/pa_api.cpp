@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -52,9 +53,14 @@ struct Plan {
   int splits = 1;
   int bps = 1;
   int n_blk_max = 0;
+  int balanced = 0;     // 1: work-balanced partition over nwg workgroups
+  int nwg = 0;
+  int64_t slots = 0;    // workspace partial slots
   int64_t grid = 0;
   size_t ws_bytes = 0;
 };
+
+constexpr int kMaxBalancedSeqs = 4096;   // must match the kernel's LDS prefix array
 
 enum Entry { kDecode, kDecodeInt8, kVerify, kAny, kGather };
 
@@ -117,7 +123,7 @@ int make_plan(const pa_args* a, Plan* pl) {
     P.rows_t = 1;
     while (P.rows_t < P.rows) P.rows_t *= 2;
   }
-  P.nw = 4;
+  P.nw = 8;
 
   const int bs = a->block_size;
   int n_blk_max = (a->max_seq_len + bs - 1) / bs;
@@ -129,17 +135,26 @@ int make_plan(const pa_args* a, Plan* pl) {
   if (n_blk_max < 1) n_blk_max = 1;
   P.n_blk_max = n_blk_max;
 
+  // Tuning knobs for experiments: waves per workgroup (4 or 8), blocks per wave.
+  int bpw_force = 0;
+  if (const char* e = getenv("PA_WAVES")) { const int v = atoi(e); if (v == 4 || v == 8) P.nw = v; }
+  if (const char* e = getenv("PA_BLOCKS_PER_WAVE")) bpw_force = atoi(e);
+
   const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
   int S;
   if (a->num_splits > 0) {
     S = a->num_splits < n_blk_max ? a->num_splits : n_blk_max;
   } else {
-    // Aim for about two rounds of resident wavefronts (8 per CU), at least
-    // two blocks per wavefront; a short context is not split.
-    const int64_t target_waves = (int64_t)cu_count() * 8 * 2;
-    const int64_t total_blocks = units * n_blk_max;
-    int64_t bpw = (total_blocks + target_waves - 1) / (target_waves > 0 ? target_waves : 1);
-    if (bpw < 2) bpw = 2;
+    // Each wavefront should stream 4..16 blocks (enough to keep its two-deep
+    // pipeline busy, few enough that long sequences are cut into workgroups
+    // the dispatcher can balance). Work is estimated from max_seq_len alone
+    // (no device read): every sequence spans the window when there is one,
+    // otherwise half the longest context on average.
+    const int64_t slots = (int64_t)cu_count() * 8;           // resident wavefronts at 2 per SIMD
+    const int64_t per_unit = a->window > 0 ? n_blk_max : (n_blk_max + 1) / 2;
+    int64_t bpw = (units * per_unit + slots - 1) / (slots > 0 ? slots : 1);
+    bpw = bpw < 4 ? 4 : (bpw > 16 ? 16 : bpw);
+    if (bpw_force > 0) bpw = bpw_force;
     const int64_t bps = bpw * P.nw;
     S = (int)((n_blk_max + bps - 1) / bps);
     if (S < 1) S = 1;
@@ -147,8 +162,27 @@ int make_plan(const pa_args* a, Plan* pl) {
   P.bps = (n_blk_max + S - 1) / S;
   P.splits = (n_blk_max + P.bps - 1) / P.bps;
   P.grid = units * P.splits;
+  P.slots = P.splits > 1 ? units * P.splits : 0;
+
+  // The matrix-core kernel defaults to the work-balanced partition: one
+  // workgroup per compute unit (two when they are 4 waves), each streaming
+  // the same number of blocks whatever the length mix. Forced splits, the
+  // vector kernel and very large batches keep the aligned splits.
+  bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= kMaxBalancedSeqs;
+  if (const char* e = getenv("PA_BALANCED")) balanced = balanced && atoi(e) != 0;
+  if (balanced) {
+    P.balanced = 1;
+    P.nwg = cu_count() * (8 / P.nw);
+    P.grid = P.nwg;
+    P.slots = P.nwg + units;
+  }
   if (P.grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
-  P.ws_bytes = P.splits > 1 ? (size_t)units * P.splits * P.rows * (size_t)(D + 2) * sizeof(float) : 0;
+  if (P.slots > 0) {
+    P.ws_bytes = (size_t)P.slots * P.rows * (size_t)(D + 2) * sizeof(float);
+    if (P.balanced) P.ws_bytes += (size_t)(a->num_seqs + 1) * sizeof(int32_t);
+  } else {
+    P.ws_bytes = 0;
+  }
   *pl = P;
   return PA_OK;
 }
@@ -163,9 +197,16 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   p.v_scale = a->v_scale;
   p.block_table = a->block_table;
   p.seq_lens = a->seq_lens;
-  const size_t acc_bytes = (size_t)a->num_seqs * a->num_kv_heads * P.splits * P.rows * a->head_dim * sizeof(float);
-  p.ws_acc = P.ws_bytes ? reinterpret_cast<float*>(a->workspace) : nullptr;
-  p.ws_ml = P.ws_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + acc_bytes) : nullptr;
+  // Workspace: acc [slots][rows][D] f32, then (m, l) [slots][rows][2] f32,
+  // then (balanced mode) the block prefix sums [B+1] int32.
+  const size_t acc_bytes = (size_t)P.slots * P.rows * a->head_dim * sizeof(float);
+  const size_t ml_bytes = (size_t)P.slots * P.rows * 2 * sizeof(float);
+  char* ws = reinterpret_cast<char*>(a->workspace);
+  p.ws_acc = P.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_ml = P.ws_bytes ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
+  p.ws_prefix = (P.ws_bytes && P.balanced) ? reinterpret_cast<int32_t*>(ws + acc_bytes + ml_bytes) : nullptr;
+  p.balanced = P.balanced;
+  p.nwg = P.nwg;
   p.visits = a->debug_visits;
   p.B = a->num_seqs;
   p.q_len = a->q_len;
@@ -212,7 +253,7 @@ int run(const pa_args* a, pa_stream_t stream, Entry entry) {
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
   if (a->timing_stop && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(a->timing_stop), st)) != hipSuccess)
     return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if (P.splits > 1) {
+  if (P.slots > 0) {
     e = pa::launch_combine(p, a->q_dtype, a->head_dim, st);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   }
@@ -245,6 +286,7 @@ int pa_plan(const pa_args* a, pa_plan_info* info) {
   info->splits = P.splits;
   info->blocks_per_split = P.bps;
   info->grid = (int32_t)P.grid;
+  info->balanced = P.balanced;
   info->workspace_bytes = P.ws_bytes;
   return PA_OK;
 }

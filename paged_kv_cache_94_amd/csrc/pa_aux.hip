@@ -5,54 +5,80 @@
 // unnormalised output. The merge is the online-softmax rule of the Lab 5
 // handout ("Flash Attention") applied across splits:
 //   M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One wavefront per output row; lanes cover the head dimension.
+// One workgroup per output row; one thread per dim of the head.
 #include "pa_common.h"
 
 namespace pa {
 
 template <typename OutT, int D>
-__global__ void __launch_bounds__(256) pa_combine_kernel(const Params p) {
-  constexpr int PER = D / 64;   // dims per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t total = (int64_t)p.B * p.Hkv * p.rows;
-  if (wid >= total) return;
-  const int r = (int)(wid % p.rows);
-  const int32_t unit = (int32_t)(wid / p.rows);
+__global__ void __launch_bounds__(D) pa_combine_kernel(const Params p) {
+  // One workgroup per output row (unit, r); thread d owns dim d. The split's
+  // (m, l) pair is the same for the whole workgroup (a uniform load).
+  const int32_t row_id = blockIdx.x;
+  const int r = row_id % p.rows;
+  const int32_t unit = row_id / p.rows;
   const int32_t b = unit / p.Hkv;
   const int32_t g = unit % p.Hkv;
   const int32_t L = p.seq_lens[b];
   if (!len_ok(L, p)) return;
-  const KeyRange kr = key_range(L, p.q_len, p.window);
-  const int32_t ns = min(live_splits(kr, p.bps), p.splits);
-
-  const size_t base = (size_t)unit * p.splits * p.rows + r;   // slot of split 0
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_ml[(base + (size_t)s * p.rows) * 2]);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t slot = base + (size_t)s * p.rows;
-    const float w = fast_exp2(p.ws_ml[slot * 2] - Ms);
-    den += w * p.ws_ml[slot * 2 + 1];
-    const float* src = p.ws_acc + slot * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += w * src[e];
+  // Slots holding this unit's partials: contiguous in both partitions.
+  int64_t slot_first;
+  int32_t ns;
+  if (p.balanced) {
+    // Workgroups w0..w1 each left a partial in slot w + unit; a unit inside a
+    // single workgroup's slice was written out directly.
+    const int32_t* pre = p.ws_prefix;
+    const int32_t nb = pre[b + 1] - pre[b];
+    if (nb == 0) return;
+    const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
+    const int64_t off = (int64_t)p.Hkv * pre[b] + (int64_t)g * nb;
+    const int64_t w0 = off / bal.per, w1 = (off + nb - 1) / bal.per;
+    if (w0 == w1) return;
+    slot_first = w0 + unit;
+    ns = (int32_t)(w1 - w0 + 1);
+  } else {
+    const KeyRange kr = key_range(L, p.q_len, p.window);
+    slot_first = (int64_t)unit * p.splits;
+    ns = min(live_splits(kr, p.bps), p.splits);
   }
-  const float inv = 1.f / den;
+
+  const size_t slot0 = (size_t)slot_first * p.rows + r;
+  const size_t step = (size_t)p.rows;
+  const float* ml = p.ws_ml + slot0 * 2;
+  const float* acc = p.ws_acc + slot0 * D + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+
+  // Split s's (m, l) sits in lane s % 64: the max and the weights come from
+  // wave reductions, and every split's accumulator load below is independent.
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[s * step * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  const float Ms = M == -INFINITY ? 0.f : M;
+  float num = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += 64) {
+    const int s = c0 + lane;
+    float w = 0.f;
+    if (s < ns) {
+      w = fast_exp2(ml[s * step * 2] - Ms);
+      den += w * ml[s * step * 2 + 1];
+    }
+    const int cnt = min(64, ns - c0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+      num += wj * acc[(size_t)(c0 + j) * step * D];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += shfl_xor(den, off);
   const int t = r / p.G;
   const int h = g * p.G + r % p.G;
-  OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if constexpr (sizeof(OutT) == 4) {
-      out[e] = num[e] * inv;
-    } else {
-      out[e] = (__bf16)(num[e] * inv);
-    }
+  OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + threadIdx.x;
+  if constexpr (sizeof(OutT) == 4) {
+    *out = num / den;
+  } else {
+    *out = (__bf16)(num / den);
   }
 }
 
@@ -80,22 +106,23 @@ __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const ch
 }
 
 hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
-  const int64_t waves = (int64_t)p.B * p.Hkv * p.rows;
-  const int grid = (int)((waves + 3) / 4);
-  if (grid == 0) return hipSuccess;
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.rows;
+  if (rows == 0) return hipSuccess;
+  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)rows);
   const bool bf16 = q_dtype == 1;
   switch (D) {
     case 64:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 64>), dim3(grid), dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 64>), dim3(grid), dim3(256), 0, st, p);
+      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 64>), grid, dim3(64), 0, st, p);
+      else hipLaunchKernelGGL((pa_combine_kernel<float, 64>), grid, dim3(64), 0, st, p);
       break;
     case 128:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 128>), dim3(grid), dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 128>), dim3(grid), dim3(256), 0, st, p);
+      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 128>), grid, dim3(128), 0, st, p);
+      else hipLaunchKernelGGL((pa_combine_kernel<float, 128>), grid, dim3(128), 0, st, p);
       break;
     case 256:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 256>), dim3(grid), dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 256>), dim3(grid), dim3(256), 0, st, p);
+      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 256>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((pa_combine_kernel<float, 256>), grid, dim3(256), 0, st, p);
       break;
     default:
       return hipErrorInvalidValue;

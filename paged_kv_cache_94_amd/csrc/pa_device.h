@@ -36,7 +36,10 @@ struct Params {
   int32_t B, q_len, Hq, Hkv, G, rows, maxb;
   int32_t window;
   float scale_log2;     // caller's scale times log2(e): scores live in base-2 exponent units
-  int32_t splits, bps;  // splits per sequence and logical blocks per split
+  int32_t splits, bps;  // aligned mode: splits per sequence and logical blocks per split
+  int32_t balanced;     // 1: work-balanced partition over nwg workgroups, 0: aligned splits
+  int32_t nwg;          // balanced mode: workgroups sharing the flattened work list
+  int32_t* ws_prefix;   // balanced mode: [B+1] prefix sums of blocks per sequence (workgroup 0 writes)
 };
 
 // Keys a step touches for one sequence (Lab 5 handout, "Sliding Window
@@ -82,6 +85,65 @@ __device__ __forceinline__ int32_t live_splits(const KeyRange& r, int32_t bps) {
   return (r.blk_hi - r.blk_lo + bps) / bps;
 }
 
+// Logical blocks a step loads for one sequence (0 for a length the table cannot map).
+template <typename P>
+__device__ __forceinline__ int32_t seq_blocks(int32_t L, const P& p) {
+  if (!len_ok(L, p)) return 0;
+  const KeyRange r = key_range(L, p.q_len, p.window);
+  return r.blk_hi - r.blk_lo + 1;
+}
+
+// Work-balanced partition. The work list is every (unit, block) pair, units
+// u = b*Hkv + g in order, unit u's blocks contiguous: unit (b, g) starts at
+// item Hkv*pre[b] + g*n_b where pre[b] = n_0 + ... + n_{b-1}. Workgroup w of
+// nwg takes items [w*per, min(T, (w+1)*per)), per = ceil(T / nwg), so every
+// workgroup streams the same number of blocks whatever the lengths are.
+struct Balanced {
+  int64_t total;  // T
+  int64_t per;    // items per workgroup
+};
+
+__device__ __forceinline__ Balanced balanced_split(const int32_t* pre, int32_t B, int32_t Hkv, int32_t nwg) {
+  Balanced s;
+  s.total = (int64_t)Hkv * pre[B];
+  s.per = (s.total + nwg - 1) / nwg;
+  if (s.per < 1) s.per = 1;
+  return s;
+}
+
+// The sequence whose units hold item x (0 <= x < T): the largest b with Hkv*pre[b] <= x.
+__device__ __forceinline__ int32_t balanced_seq(const int32_t* pre, int32_t B, int32_t Hkv, int64_t x) {
+  int32_t lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)Hkv * pre[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// pre[0..B] = prefix sums of seq_blocks over the batch, computed by wave 0
+// of the workgroup (64 sequences per step, DPP/ds_bpermute scan); the caller
+// synchronises the workgroup before reading pre.
+template <typename P>
+__device__ __forceinline__ void block_prefix(const P& p, int32_t* pre) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  if (lane == 0) pre[0] = 0;
+  int32_t carry = 0;
+  for (int32_t base = 0; base < p.B; base += 64) {
+    const int32_t b = base + lane;
+    int32_t v = b < p.B ? seq_blocks(p.seq_lens[b], p) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t t = __shfl_up(v, off);
+      if (lane >= off) v += t;
+    }
+    if (b < p.B) pre[b + 1] = carry + v;
+    carry += __shfl(v, 63);
+  }
+}
+
 // Byte offset of (physical block, slot, kv head) row inside a pool laid out
 // [num_blocks][16][Hkv][D] (tiniestgpt notes, "PagedAttention").
 __device__ __forceinline__ size_t row_offset_bytes(int32_t phys, int32_t slot, int32_t g, int32_t Hkv,
@@ -105,23 +167,30 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
 }
 
-// Sum over the 8 lanes of an aligned lane octet; every lane gets the total.
-__device__ __forceinline__ float octet_sum(float x) {
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15-i inside each 16-lane row
+
+// Sum over an aligned group of N (8 or 16) lanes; every lane of the group gets the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "lane groups of 8 or 16");
   x += dpp<kDppXor1>(x);
   x += dpp<kDppXor2>(x);
   x += dpp<kDppHalfMirror>(x);
+  if constexpr (N == 16) x += dpp<kDppRowMirror>(x);
   return x;
 }
 
-// Max / sum over the 8 octets of the wavefront (lanes that agree in bits 0..2).
-__device__ __forceinline__ float octets_max(float x) {
-  x = fmaxf(x, dpp<kDppRor8>(x));
+// Max / sum across the 64/N groups of N lanes (lanes that agree in the low log2(N) bits).
+template <int N>
+__device__ __forceinline__ float across_groups_max(float x) {
+  if constexpr (N == 8) x = fmaxf(x, dpp<kDppRor8>(x));
   x = fmaxf(x, shfl_xor(x, 16));
   x = fmaxf(x, shfl_xor(x, 32));
   return x;
 }
-__device__ __forceinline__ float octets_sum(float x) {
-  x += dpp<kDppRor8>(x);
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float x) {
+  if constexpr (N == 8) x += dpp<kDppRor8>(x);
   x += shfl_xor(x, 16);
   x += shfl_xor(x, 32);
   return x;
@@ -154,6 +223,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Copy a freshly loaded value into a register written by a VALU move (a DPP
+// identity permutation). The wait for the load happens once, here; later
+// reads of the copy inside a software-pipelined loop then never make the
+// compiler wait on vector-memory loads issued after it (which it otherwise
+// does conservatively across the loop's back edge).
+__device__ __forceinline__ int32_t settle(int32_t v) {
+  return __builtin_amdgcn_mov_dpp(v, 0xE4, 0xF, 0xF, true);   // quad_perm [0,1,2,3]
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// 16-byte load with the non-temporal hint: cache rows are read exactly once
+// per step, so they should not displace anything in L2 / the Infinity Cache.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 }  // namespace pa

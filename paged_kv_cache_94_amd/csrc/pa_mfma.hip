@@ -9,24 +9,28 @@
 // Layouts (lane l of the 64-lane wavefront; n = l & 15, q4 = l >> 4):
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16 over D/32 chunks. The A operand is the K tile
-//    as loaded: lane l holds token n, 8 consecutive dims of chunk c. The B
-//    operand is Q^T held in registers for the whole kernel. The result gives
-//    lane l query row n and tokens 4*q4 .. 4*q4+3 -- exactly the B-operand
-//    layout P^T needs for the PV product, and the row is lane-local, so the
-//    running max / sum and the accumulator rescale need no lane exchange
-//    except the max over the four lanes sharing a row.
-//  * V has to be read with tokens along the contraction depth. The V tile is
-//    loaded like K (token per lane) and transposed on the matrix core itself:
-//    multiplying a 16x16 slice by the identity with v_mfma_f32_16x16x16_bf16
-//    returns it with lane l holding one dim and four tokens, the A layout of
-//    O^T = V^T P^T. The product is exact (bf16 values times 1.0).
-//  * O^T accumulates in fp32; lane l ends with query row n and, per chunk,
-//    8 consecutive dims.
+//    exactly as loaded from HBM (lane l: token n, 8 consecutive dims of the
+//    chunk); the B operand is Q^T, held in registers for the whole kernel.
+//    The result gives lane l query row n and tokens 4*q4 .. 4*q4+3 -- the
+//    B-operand layout P^T needs for the PV product, and the row is
+//    lane-local, so the softmax needs lane exchanges only for the max over
+//    the four lanes sharing a row.
+//  * V must be read with tokens along the contraction depth. Each wavefront
+//    stages its V tile row-major in its own LDS slice and reads it back with
+//    ds_read_b64_tr_b16: in each 16-lane group, lanes 4k..4k+3 address row k
+//    (token 4*q4+k, 16 consecutive dims) and lane i receives element i of
+//    the four rows -- the A operand of O^T = V^T P^T for 16 dims.
+//  * P is split into bf16 hi and lo parts; O^T += V^T [P_hi; P_lo] is one
+//    v_mfma_f32_16x16x32_bf16 whose 32-deep contraction holds both parts
+//    against the V^T slice read twice, so the weights keep ~16 bits while V
+//    stays in its stored type.
+//  * O^T accumulates in fp32: lane l ends with query row n and, per 16-dim
+//    tile j, dims 16j + 4*q4 .. +3.
 //  * int8 caches (tiniestgpt notes, KV cache quantization): codes are
 //    gathered first, widened to bf16 (exact for |code| <= 127), the key scale
 //    multiplies the score of its token and the value scale is folded into P.
 //  * When v_pool == k_pool (Gemma4 global layer, shared W_K / W_V) the tile
-//    is read from HBM once and used as both K and V.
+//    is read from HBM once and serves as both K and V.
 #include "pa_common.h"
 
 namespace pa {
@@ -49,37 +53,47 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16(uint32_t w, int byte0) {
   return pack_bf16(a, b);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ds_read_b64_tr_b16 at LDS address p (see the layout note above).
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<lds_char*>((const lds_char*)p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 }  // namespace
 
+template <int D, int MT, int NW>
+struct MfmaLds {
+  static constexpr int ROWS = 16 * MT;
+  static constexpr int VSTRIDE = D * 2 + 32;                 // bytes per staged V row (32-byte skew against bank conflicts)
+  static constexpr int STAGE = NW * 16 * VSTRIDE;            // one V tile per wavefront
+  static constexpr int MERGE = (NW > 1 ? NW / 2 : 1) * ROWS * (D + 2) * 4;
+  static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
+};
+
+// Attention of query rows (b, g) over logical blocks [first, last] of sequence
+// b. slot < 0: write the normalised output; else write (m, l, o) to
+// workspace slot `slot`. Called uniformly by every wavefront of the workgroup.
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-pa_mfma_kernel(const Params p) {
-  constexpr int ROWS = 16 * MT;
+__device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t L,
+                                             const KeyRange& kr, int32_t first, int32_t last, int64_t slot) {
+  using Lds = MfmaLds<D, MT, NW>;
+  constexpr int ROWS = Lds::ROWS;
   constexpr int C = D / 32;                           // contraction chunks of 32 dims
+  constexpr int TJ = D / 16;                          // 16-dim output tiles
   constexpr int EB = INT8 ? 1 : 2;
   constexpr int ROW_BYTES = D * EB;
   constexpr int NLOAD = ROW_BYTES / 64;               // 16-byte loads per lane per tile
   static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
 
-  __shared__ float lds_acc[(NW > 1 ? NW - 1 : 1) * ROWS * D];
-  __shared__ float lds_ml[NW * ROWS * 2];
-
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: block indices stay scalar
   const int n = lane & 15;
   const int q4 = lane >> 4;
-
-  const int32_t g = blockIdx.x % p.Hkv;
-  const int32_t bsplit = blockIdx.x / p.Hkv;
-  const int32_t b = bsplit % p.B;
-  const int32_t split = bsplit / p.B;
-
-  const int32_t L = p.seq_lens[b];
-  if (!len_ok(L, p)) return;   // broken precondition: touch nothing outside the arrays
-  const KeyRange kr = key_range(L, p.q_len, p.window);
-  const int32_t first = kr.blk_lo + split * p.bps;
-  if (first > kr.blk_hi) return;
-  const int32_t last = min(kr.blk_hi, first + p.bps - 1);
+  __syncthreads();   // the previous segment's merge is done with the shared buffer
 
   // Q^T as the B operand: lane l holds query row n (+16 per tile), 8 dims per chunk.
   bf16x8 qt[MT][C];
@@ -101,20 +115,14 @@ pa_mfma_kernel(const Params p) {
     row_hi[tile] = live ? kr.p0 + t : -1;
   }
 
-  // Identity B operand for the transposing product: lane l holds column n,
-  // contraction rows 4*q4 .. 4*q4+3.
-  i16x4 ident;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == n) ? (short)0x3F80 : (short)0;
-
-  f32x4 o[MT][C][2];
+  f32x4 o[MT][TJ];
   float m[MT], l[MT];
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
     m[tile] = -INFINITY;
     l[tile] = 0.f;
 #pragma unroll
-    for (int c = 0; c < C; ++c) o[tile][c][0] = o[tile][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; ++j) o[tile][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const size_t tok_stride = (size_t)p.Hkv * ROW_BYTES;
@@ -123,85 +131,97 @@ pa_mfma_kernel(const Params p) {
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
-  for (int32_t i = first + wave; i <= last; i += NW) {
-    const int32_t phys = table[i];
+  // This wavefront's V staging tile, [16 tokens][D dims] bf16, row stride VSTRIDE,
+  // and its transposed-read address for 16-dim tile 0: row 4*q4 + (n>>2), dims 4*(n&3).
+  char* vstage = smem + wave * 16 * Lds::VSTRIDE;
+  const char* vread = vstage + (4 * q4 + (n >> 2)) * Lds::VSTRIDE + 8 * (n & 3);
+
+  // One 16-token block as loaded: this lane's token row (n) of K (and V), plus
+  // the four per-token scales of its score rows for int8 caches.
+  struct Fetched {
+    uint4 k[NLOAD];
+    uint4 v[ALIAS ? 1 : NLOAD];
+    float ks[INT8 ? 4 : 1], vs[INT8 ? 4 : 1];
+  };
+  // The k-th block of this wavefront is first + wave + NW*k; lane k holds its
+  // physical id (one coalesced read up front, then v_readlane per block, so no
+  // block waits on a table read behind the K/V loads already in flight).
+  int32_t cfirst = first;   // first block of the current chunk (at most 64 blocks per wavefront)
+  int32_t nmine = 0;
+  int32_t tbl = 0;
+
+  auto fetch = [&](int32_t k, Fetched& f) __attribute__((always_inline)) {
+    const int32_t phys = __builtin_amdgcn_readlane(tbl, k);
     const size_t blk_off = (size_t)phys * kBlock * tok_stride;
-    uint4 kraw[NLOAD], vraw[NLOAD];
 #pragma unroll
-    for (int u = 0; u < NLOAD; ++u) kraw[u] = load16(kbase + blk_off + (INT8 ? 16 * q4 + 64 * u : 16 * q4 + 64 * u));
+    for (int u = 0; u < NLOAD; ++u) f.k[u] = load16_stream(kbase + blk_off + 16 * q4 + 64 * u);
     if constexpr (!ALIAS) {
 #pragma unroll
-      for (int u = 0; u < NLOAD; ++u) vraw[u] = load16(vbase + blk_off + 16 * q4 + 64 * u);
+      for (int u = 0; u < NLOAD; ++u) f.v[u] = load16_stream(vbase + blk_off + 16 * q4 + 64 * u);
     }
-    float ksc[4], vsc[4];
     if constexpr (INT8) {
       const float* ks = p.k_scale + ((size_t)phys * kBlock + 4 * q4) * p.Hkv + g;
       const float* vs = p.v_scale + ((size_t)phys * kBlock + 4 * q4) * p.Hkv + g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        ksc[e] = ks[(size_t)e * p.Hkv];
-        vsc[e] = vs[(size_t)e * p.Hkv];
+        f.ks[e] = ks[(size_t)e * p.Hkv];
+        f.vs[e] = vs[(size_t)e * p.Hkv];
       }
     }
+  };
+
+  // Chunk c of the K tile as a bf16x8 MFMA operand (int8 codes widened, exact).
+  auto k_operand = [&](const Fetched& f, int c) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (INT8) {
+      const uint4 w = f.k[c >> 1];
+      const uint32_t w0 = (c & 1) ? w.z : w.x, w1 = (c & 1) ? w.w : w.y;
+      return __builtin_bit_cast(bf16x8, make_uint4(i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 2),
+                                                   i8pair_to_bf16(w1, 0), i8pair_to_bf16(w1, 2)));
+    } else {
+      return __builtin_bit_cast(bf16x8, f.k[c]);
+    }
+  };
+
+  auto consume = [&](int32_t k, const Fetched& f) __attribute__((always_inline)) {
+    const int32_t i = cfirst + wave + NW * k;   // logical block
     if (visits && lane == 0) atomicAdd(visits + i, 1);
-    if constexpr (ALIAS) {
-#pragma unroll
-      for (int u = 0; u < NLOAD; ++u) vraw[u] = kraw[u];
-    }
 
-    // Rows nobody may see can hold anything: zero this lane's V row (lane = token n).
-    {
-      const int32_t j = i * kBlock + n;
-      const bool ok = j < L && j >= kr.lo0;
+    // Stage this lane's V row (token n) in LDS as bf16. A row nobody may see
+    // can hold anything and is written as zeros (only edge blocks have such rows).
+    const bool edge = i * kBlock < kr.lo0 || i * kBlock + kBlock > L;
+    const int32_t jv = i * kBlock + n;
+    const bool v_ok = !edge || (jv < L && jv >= kr.lo0);
+    __builtin_amdgcn_wave_barrier();   // the previous block's transposed reads stay before these writes
 #pragma unroll
-      for (int u = 0; u < NLOAD; ++u) {
-        vraw[u].x = ok ? vraw[u].x : 0u;
-        vraw[u].y = ok ? vraw[u].y : 0u;
-        vraw[u].z = ok ? vraw[u].z : 0u;
-        vraw[u].w = ok ? vraw[u].w : 0u;
+    for (int u = 0; u < NLOAD; ++u) {
+      uint4 w = ALIAS ? f.k[u] : f.v[ALIAS ? 0 : u];
+      if (edge) {
+        w.x = v_ok ? w.x : 0u;
+        w.y = v_ok ? w.y : 0u;
+        w.z = v_ok ? w.z : 0u;
+        w.w = v_ok ? w.w : 0u;
       }
-    }
-
-    // Operands of chunk c as bf16x8 (int8 caches are widened here).
-    bf16x8 ka[C], va[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
       if constexpr (INT8) {
-        const uint4 kw = kraw[c >> 1];
-        const uint4 vw = vraw[c >> 1];
-        const uint32_t k0 = (c & 1) ? kw.z : kw.x, k1 = (c & 1) ? kw.w : kw.y;
-        const uint32_t v0 = (c & 1) ? vw.z : vw.x, v1 = (c & 1) ? vw.w : vw.y;
-        uint4 kb = make_uint4(i8pair_to_bf16(k0, 0), i8pair_to_bf16(k0, 2), i8pair_to_bf16(k1, 0), i8pair_to_bf16(k1, 2));
-        uint4 vb = make_uint4(i8pair_to_bf16(v0, 0), i8pair_to_bf16(v0, 2), i8pair_to_bf16(v1, 0), i8pair_to_bf16(v1, 2));
-        ka[c] = __builtin_bit_cast(bf16x8, kb);
-        va[c] = __builtin_bit_cast(bf16x8, vb);
+        // 16 codes: dims 64u + 16*q4 .. +15
+        char* dst = vstage + n * Lds::VSTRIDE + (64 * u + 16 * q4) * 2;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(i8pair_to_bf16(w.x, 0), i8pair_to_bf16(w.x, 2),
+                                                    i8pair_to_bf16(w.y, 0), i8pair_to_bf16(w.y, 2));
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(i8pair_to_bf16(w.z, 0), i8pair_to_bf16(w.z, 2),
+                                                         i8pair_to_bf16(w.w, 0), i8pair_to_bf16(w.w, 2));
       } else {
-        ka[c] = __builtin_bit_cast(bf16x8, kraw[c]);
-        va[c] = __builtin_bit_cast(bf16x8, vraw[c]);
+        // 8 bf16: dims 32u + 8*q4 .. +7
+        *reinterpret_cast<uint4*>(vstage + n * Lds::VSTRIDE + (32 * u + 8 * q4) * 2) = w;
       }
     }
+    __builtin_amdgcn_wave_barrier();   // these writes stay before this block's transposed reads
 
-    // Transpose the V tile on the matrix core: vt[c][hh] holds dim slot n, tokens 4*q4..4*q4+3.
-    uint32_t vt[C][2][2];
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint4 w = __builtin_bit_cast(uint4, va[c]);
-        i16x4 a;
-        const uint32_t w0 = hh ? w.z : w.x, w1 = hh ? w.w : w.y;
-        a[0] = (short)(w0 & 0xFFFF); a[1] = (short)(w0 >> 16);
-        a[2] = (short)(w1 & 0xFFFF); a[3] = (short)(w1 >> 16);
-        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        vt[c][hh][0] = pack_bf16(t[0], t[1]);
-        vt[c][hh][1] = pack_bf16(t[2], t[3]);
-      }
-
+    // Scores and softmax for every row tile; P leaves as hi/lo bf16 parts.
+    bf16x8 pbv[MT];
 #pragma unroll
     for (int tile = 0; tile < MT; ++tile) {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < C; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qt[tile][c], s, 0, 0, 0);
+      for (int c = 0; c < C; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(f, c), qt[tile][c], s, 0, 0, 0);
 
       // s[e] = score of query row n (+16*tile) against token 4*q4+e of block i.
       float sc[4];
@@ -211,7 +231,7 @@ pa_mfma_kernel(const Params p) {
         const int32_t j = i * kBlock + 4 * q4 + e;
         const bool ok = j <= row_hi[tile] && j >= row_lo[tile];
         float x = s[e] * p.scale_log2;
-        if constexpr (INT8) x *= ksc[e];
+        if constexpr (INT8) x *= f.ks[e];
         sc[e] = ok ? x : -INFINITY;
         mb = fmaxf(mb, sc[e]);
       }
@@ -222,9 +242,7 @@ pa_mfma_kernel(const Params p) {
         const float a = grow ? fast_exp2(m[tile] - mn) : 1.f;
         l[tile] *= a;
 #pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) o[tile][c][hh] *= a;
+        for (int j = 0; j < TJ; ++j) o[tile][j] *= a;
         m[tile] = mn;
       }
       const float msafe = m[tile] == -INFINITY ? 0.f : m[tile];
@@ -236,25 +254,54 @@ pa_mfma_kernel(const Params p) {
         if constexpr (INT8) {
           const int32_t j = i * kBlock + 4 * q4 + e;
           const bool vis = j < L && j >= kr.lo0;
-          pe[e] *= vis ? vsc[e] : 0.f;
+          pe[e] *= vis ? f.vs[e] : 0.f;
         }
       }
-      i16x4 pb;
-      {
-        const uint32_t p01 = pack_bf16(pe[0], pe[1]);
-        const uint32_t p23 = pack_bf16(pe[2], pe[3]);
-        pb[0] = (short)(p01 & 0xFFFF); pb[1] = (short)(p01 >> 16);
-        pb[2] = (short)(p23 & 0xFFFF); pb[3] = (short)(p23 >> 16);
+      // P as hi + lo bf16 parts for the 32-deep PV contraction.
+      float lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        lo[e] = pe[e] - __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)pe[e]) << 16);
+      pbv[tile] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(pe[0], pe[1]), pack_bf16(pe[2], pe[3]),
+                                                        pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])));
+    }
+
+    // O^T += V^T [P_hi; P_lo], one 16-dim tile at a time, V^T read transposed from LDS.
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const uint2 a = lds_read_tr16(vread + 32 * j);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, a.x, a.y));
+#pragma unroll
+      for (int tile = 0; tile < MT; ++tile)
+        o[tile][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv[tile], o[tile][j], 0, 0, 0);
+    }
+  };
+
+  // Two-deep software pipeline (block k+1 in flight while block k is consumed)
+  // when both fetch buffers fit beside the accumulators; else one buffer.
+  constexpr int FETCH_WORDS = NLOAD * 4 * (ALIAS ? 1 : 2) + (INT8 ? 8 : 0);
+  constexpr bool PIPE = MT == 1 && 2 * FETCH_WORDS <= 64;
+  for (; cfirst <= last; cfirst += 64 * NW) {
+    const int32_t clast = min(last, cfirst + 64 * NW - 1);
+    nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
+    tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
+    if constexpr (PIPE) {
+      Fetched fa, fb;
+      if (nmine > 0) fetch(0, fa);
+      for (int32_t k = 0; k < nmine; k += 2) {
+        const bool has_b = k + 1 < nmine;
+        if (has_b) fetch(k + 1, fb);
+        consume(k, fa);
+        if (!has_b) break;
+        if (k + 2 < nmine) fetch(k + 2, fa);
+        consume(k + 1, fb);
       }
-#pragma unroll
-      for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          i16x4 a;
-          a[0] = (short)(vt[c][hh][0] & 0xFFFF); a[1] = (short)(vt[c][hh][0] >> 16);
-          a[2] = (short)(vt[c][hh][1] & 0xFFFF); a[3] = (short)(vt[c][hh][1] >> 16);
-          o[tile][c][hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[tile][c][hh], 0, 0, 0);
-        }
+    } else {
+      Fetched fa;
+      for (int32_t k = 0; k < nmine; ++k) {
+        fetch(k, fa);
+        consume(k, fa);
+      }
     }
   }
 
@@ -262,78 +309,130 @@ pa_mfma_kernel(const Params p) {
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) l[tile] = quads16_sum(l[tile]);
 
-  // Merge the wavefronts: waves 1..NW-1 park their state in LDS, wave 0 folds it in.
-  if (wave > 0) {
+  // Merge the wavefronts pairwise through LDS (reusing the staging area): in
+  // each round the upper half parks its (m, l, o) and the lower half folds it
+  // in with the online-softmax rule.
+  float* lds_acc = reinterpret_cast<float*>(smem);
+  float* lds_ml = lds_acc + (NW > 1 ? NW / 2 : 1) * ROWS * D;
 #pragma unroll
-    for (int tile = 0; tile < MT; ++tile) {
-      const int r = n + 16 * tile;
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    __syncthreads();
+    if (wave >= half && wave < 2 * half) {
+      const int slot = wave - half;
 #pragma unroll
-      for (int c = 0; c < C; ++c)
+      for (int tile = 0; tile < MT; ++tile) {
+        const int r = n + 16 * tile;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int j = 0; j < TJ; ++j)
+          *reinterpret_cast<f32x4*>(lds_acc + (slot * ROWS + r) * D + 16 * j + 4 * q4) = o[tile][j];
+        if (q4 == 0) {
+          lds_ml[(slot * ROWS + r) * 2] = m[tile];
+          lds_ml[(slot * ROWS + r) * 2 + 1] = l[tile];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave < half) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            lds_acc[((wave - 1) * ROWS + r) * D + chunk_dim<INT8>(c, q4, 4 * hh + e)] = o[tile][c][hh][e];
-      if (q4 == 0) {
-        lds_ml[(wave * ROWS + r) * 2] = m[tile];
-        lds_ml[(wave * ROWS + r) * 2 + 1] = l[tile];
+      for (int tile = 0; tile < MT; ++tile) {
+        const int r = n + 16 * tile;
+        const float m1 = lds_ml[(wave * ROWS + r) * 2];
+        const float l1 = lds_ml[(wave * ROWS + r) * 2 + 1];
+        const float M = fmaxf(m[tile], m1);
+        const float Ms = M == -INFINITY ? 0.f : M;
+        const float a0 = fast_exp2(m[tile] - Ms);
+        const float a1 = fast_exp2(m1 - Ms);
+        m[tile] = M;
+        l[tile] = a0 * l[tile] + a1 * l1;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          o[tile][j] = a0 * o[tile][j] +
+                       a1 * *reinterpret_cast<const f32x4*>(lds_acc + (wave * ROWS + r) * D + 16 * j + 4 * q4);
       }
     }
   }
-  __syncthreads();
   if (wave != 0) return;
 
-  const int32_t unit = b * p.Hkv + g;
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
     const int r = n + 16 * tile;
-    float M = m[tile];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, lds_ml[(w * ROWS + r) * 2]);
-    const float Ms = M == -INFINITY ? 0.f : M;
-    float wsc[NW];
-    float den = 0.f;
-    wsc[0] = fast_exp2(m[tile] - Ms);
-    den = wsc[0] * l[tile];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      wsc[w] = fast_exp2(lds_ml[(w * ROWS + r) * 2] - Ms);
-      den += wsc[w] * lds_ml[(w * ROWS + r) * 2 + 1];
-    }
     if (r >= p.rows) continue;
     const int t = r / p.G;
     const int h = g * p.G + r % p.G;
+    if (slot >= 0) {
+      const size_t row_slot = (size_t)slot * p.rows + r;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      float v[8];
+      for (int j = 0; j < TJ; ++j) {
+        const f32x4 v = o[tile][j];
+        *reinterpret_cast<float4*>(p.ws_acc + row_slot * D + 16 * j + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (q4 == 0) {
+        p.ws_ml[row_slot * 2] = m[tile];
+        p.ws_ml[row_slot * 2 + 1] = l[tile];
+      }
+    } else {
+      const float inv = 1.f / l[tile];
+      __bf16* out = reinterpret_cast<__bf16*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + 4 * q4;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = wsc[0] * o[tile][c][hh][e];
-#pragma unroll
-          for (int w = 1; w < NW; ++w)
-            x += wsc[w] * lds_acc[((w - 1) * ROWS + r) * D + chunk_dim<INT8>(c, q4, 4 * hh + e)];
-          v[4 * hh + e] = x;
-        }
-      const int d0 = chunk_dim<INT8>(c, q4, 0);
-      if (p.splits > 1) {
-        const size_t slot = ((size_t)unit * p.splits + split) * p.rows + r;
-        float4* dst = reinterpret_cast<float4*>(p.ws_acc + slot * D + d0);
-        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-        if (c == 0 && q4 == 0) {
-          p.ws_ml[slot * 2] = M;
-          p.ws_ml[slot * 2 + 1] = den;
-        }
-      } else {
-        const float inv = 1.f / den;
-        uint4 pk = make_uint4(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv),
-                              pack_bf16(v[4] * inv, v[5] * inv), pack_bf16(v[6] * inv, v[7] * inv));
-        __bf16* out = reinterpret_cast<__bf16*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + d0;
-        *reinterpret_cast<uint4*>(out) = pk;
+      for (int j = 0; j < TJ; ++j) {
+        const f32x4 v = o[tile][j];
+        *reinterpret_cast<uint2*>(out + 16 * j) =
+            make_uint2(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv));
       }
     }
+  }
+}
+
+constexpr int kMaxBalancedSeqs = 4096;   // sequences the balanced partition handles (prefix sums in LDS)
+
+template <bool INT8, bool ALIAS, int D, int MT, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+pa_mfma_kernel(const Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[MfmaLds<D, MT, NW>::BYTES];
+  if (!p.balanced) {
+    // Aligned splits: workgroup (split, b, g) takes blocks [blk_lo + split*bps, ...] of sequence b.
+    const int32_t g = blockIdx.x % p.Hkv;
+    const int32_t bsplit = blockIdx.x / p.Hkv;
+    const int32_t b = bsplit % p.B;
+    const int32_t split = bsplit / p.B;
+    const int32_t L = p.seq_lens[b];
+    if (!len_ok(L, p)) return;   // broken precondition: touch nothing outside the arrays
+    const KeyRange kr = key_range(L, p.q_len, p.window);
+    const int32_t first = kr.blk_lo + split * p.bps;
+    if (first > kr.blk_hi) return;
+    const int32_t last = min(kr.blk_hi, first + p.bps - 1);
+    const int64_t slot = p.splits > 1 ? (int64_t)(b * p.Hkv + g) * p.splits + split : -1;
+    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, L, kr, first, last, slot);
+    return;
+  }
+  // Balanced partition: this workgroup's slice of the flattened (unit, block)
+  // list, cut at unit boundaries into segments. A segment holding a whole
+  // unit writes the output directly; the others leave a partial in slot
+  // (workgroup + unit), which is unique because both indices only grow
+  // along the list.
+  __shared__ int32_t pre[kMaxBalancedSeqs + 1];
+  block_prefix(p, pre);
+  __syncthreads();
+  if (blockIdx.x == 0 && p.ws_prefix)
+    for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
+  const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
+  int64_t x = (int64_t)blockIdx.x * bal.per;
+  const int64_t hi = min(bal.total, x + bal.per);
+  while (x < hi) {
+    const int32_t b = balanced_seq(pre, p.B, p.Hkv, x);
+    const int32_t nb = pre[b + 1] - pre[b];
+    const int64_t base = (int64_t)p.Hkv * pre[b];
+    const int32_t g = (int32_t)((x - base) / nb);
+    const int64_t off = base + (int64_t)g * nb;
+    const int64_t seg_hi = min(hi, off + nb);
+    const int32_t L = p.seq_lens[b];
+    const KeyRange kr = key_range(L, p.q_len, p.window);
+    const int32_t first = kr.blk_lo + (int32_t)(x - off);
+    const int32_t last = kr.blk_lo + (int32_t)(seg_hi - off) - 1;
+    const bool whole = x == off && seg_hi == off + nb;
+    const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)b * p.Hkv + g;
+    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, L, kr, first, last, slot);
+    x = seg_hi;
   }
 }
 
@@ -343,6 +442,7 @@ hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, bool* o
   *ok = true;
   switch (nw) {
     case 4: hipLaunchKernelGGL((pa_mfma_kernel<INT8, ALIAS, D, MT, 4>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((pa_mfma_kernel<INT8, ALIAS, D, MT, 8>), dim3(grid), dim3(512), 0, st, p); break;
     default: *ok = false; return hipSuccess;
   }
   return hipGetLastError();

@@ -4,20 +4,22 @@
 // One workgroup owns one (sequence, KV head, context split); its NW
 // wavefronts take the split's logical blocks round-robin. Per block a
 // wavefront reads the 16 cached rows of its KV head straight from HBM into
-// registers: eight lanes cover one 128-byte line of a row with 16-byte
-// loads, so one load instruction moves 8 rows x 128 B and a 16-token block
-// is 2 x (row bytes / 128) instructions per tensor. The K rows are used
+// registers: a group of LPT lanes (16 for rows of 256 bytes or more, else 8)
+// covers LPT*16 bytes of one row with 16-byte loads, so every load
+// instruction moves whole 128-byte lines of 64/LPT rows. The K rows are used
 // for every query row of the group from registers (grouped-query attention,
-// Lab 5 handout: heads share K/V without repeating them).
+// Lab 5 handout: heads share K/V without repeating them). Loads of the next
+// block are issued before the current one is consumed (two register
+// buffers per wavefront).
 //
 // Scores: each lane dots its slice of the row with the matching slice of
-// every query row (bf16 pairs through v_dot2, fp32 through FMA), then an
-// octet sum over DPP (quad_perm x2 + half-row mirror) gives every lane of
-// the octet the full score. The online softmax (Lab 5 handout, "Flash
-// Attention": running max m, running sum l, unnormalised output o, O = o/l;
-// base-2 exponents, fp32 state) rescales o only when a row's max grows. A
-// key no query may see is removed by select, never by multiplying with 0,
-// so garbage in unused slots cannot leak in.
+// every query row (bf16 pairs through v_dot2, fp32 through FMA), then a DPP
+// sum over the lane group (quad_perm x2, half-row and row mirrors) gives
+// every lane of the group the full score. The online softmax (Lab 5
+// handout, "Flash Attention": running max m, running sum l, unnormalised
+// output o, O = o/l; base-2 exponents, fp32 state) rescales o only when a
+// row's max grows. A key no query may see is removed by select, never by
+// multiplying with 0, so garbage in unused slots cannot leak in.
 #include "pa_common.h"
 
 namespace pa {
@@ -27,18 +29,21 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
 pa_valu_kernel(const Params p) {
   constexpr int EB = BF16 ? 2 : 4;          // bytes per cache element
   constexpr int ROW_BYTES = D * EB;
-  constexpr int LPT = 8;                    // lanes per 128-byte line of a row
+  constexpr int LPT = ROW_BYTES >= 256 ? 16 : 8;   // lanes sharing one row: 16 B each, whole lines
   constexpr int TPI = 64 / LPT;             // rows per load instruction
   constexpr int TPL = kBlock / TPI;         // rows per lane per block
   constexpr int COLS = ROW_BYTES / (LPT * 16);
   constexpr int EPC = 16 / EB;              // elements per 16-byte chunk
   static_assert(COLS >= 1 && ROW_BYTES % (LPT * 16) == 0, "row must be whole 128-byte lines");
+  // Two register buffers for K/V tiles when they fit next to q and the accumulators.
+  constexpr int TILE_WORDS = TPL * COLS * 4;
+  constexpr bool PIPE = 4 * TILE_WORDS + ROWS * COLS * (4 + EPC) <= 180;
 
   __shared__ float lds_acc[NW * ROWS * D];
   __shared__ float lds_ml[NW * ROWS * 2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: block indices and table reads stay scalar
   const int tsub = lane / LPT;
   const int part = lane % LPT;
 
@@ -99,21 +104,33 @@ pa_valu_kernel(const Params p) {
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
-  for (int32_t i = first + wave; i <= last; i += NW) {
-    const int32_t phys = table[i];
+  // One 16-token block: this lane's 16-byte slices of the K and V rows.
+  using Tile = uint4[TPL][COLS];
+  // The k-th block of this wavefront is first + wave + NW*k; lane k holds its
+  // physical id (one coalesced read up front, then v_readlane per block, so no
+  // block waits on a table read behind the K/V loads already in flight).
+  int32_t cfirst = first;   // first block of the current chunk (at most 64 blocks per wavefront)
+  int32_t nmine = 0;
+  int32_t tbl = 0;
+
+  auto fetch = [&](int32_t k, Tile& kr_, Tile& vr_) __attribute__((always_inline)) {
+    const int32_t phys = __builtin_amdgcn_readlane(tbl, k);
     const size_t blk_off = (size_t)phys * kBlock * tok_stride;
-    uint4 kr_[TPL][COLS], vr_[TPL][COLS];
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
-      for (int c = 0; c < COLS; ++c) kr_[u][c] = load16(kbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+      for (int c = 0; c < COLS; ++c) kr_[u][c] = load16_stream(kbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
-      for (int c = 0; c < COLS; ++c) vr_[u][c] = load16(vbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+      for (int c = 0; c < COLS; ++c) vr_[u][c] = load16_stream(vbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+  };
+
+  auto consume = [&](int32_t k, const Tile& kr_, const Tile& vr_) __attribute__((always_inline)) {
+    const int32_t i = cfirst + wave + NW * k;   // logical block
     if (visits && lane == 0) atomicAdd(visits + i, 1);
 
-    // q . k for every (row slot u, query row r), summed over the octet.
+    // q . k for every (row slot u, query row r), summed over the lanes sharing the row.
     float s[TPL][ROWS];
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
@@ -133,7 +150,7 @@ pa_valu_kernel(const Params p) {
             }
           }
         }
-        s[u][r] = octet_sum(acc_s);
+        s[u][r] = group_sum<LPT>(acc_s);
       }
 
     // Mask by select, scale to base-2 exponent units, per-row block max.
@@ -155,7 +172,7 @@ pa_valu_kernel(const Params p) {
       float mb = s[0][r];
 #pragma unroll
       for (int u = 1; u < TPL; ++u) mb = fmaxf(mb, s[u][r]);
-      mb = octets_max(mb);
+      mb = across_groups_max<LPT>(mb);
       const float mn = fmaxf(m[r], mb);
       if (__builtin_amdgcn_readfirstlane((int)(mn > m[r]))) {
         const float a = fast_exp2(m[r] - mn);   // 0 when m was -inf
@@ -198,16 +215,41 @@ pa_valu_kernel(const Params p) {
           }
         }
       }
+  };
+
+  // Two-deep software pipeline: block k+1 is in flight while block k is consumed.
+  for (; cfirst <= last; cfirst += 64 * NW) {
+    const int32_t clast = min(last, cfirst + 64 * NW - 1);
+    nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
+    tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
+    if constexpr (PIPE) {
+      Tile ka, va, kb, vb;
+      if (nmine > 0) fetch(0, ka, va);
+      for (int32_t k = 0; k < nmine; k += 2) {
+        const bool has_b = k + 1 < nmine;
+        if (has_b) fetch(k + 1, kb, vb);
+        consume(k, ka, va);
+        if (!has_b) break;
+        if (k + 2 < nmine) fetch(k + 2, ka, va);
+        consume(k + 1, kb, vb);
+      }
+    } else {
+      Tile ka, va;
+      for (int32_t k = 0; k < nmine; ++k) {
+        fetch(k, ka, va);
+        consume(k, ka, va);
+      }
+    }
   }
 
-  // Sum the eight octets (different rows, same slices), then hand off to LDS.
+  // Sum the lane groups (different rows, same slices), then hand off to LDS.
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    l[r] = octets_sum(l[r]);
+    l[r] = across_groups_sum<LPT>(l[r]);
 #pragma unroll
     for (int c = 0; c < COLS; ++c)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[r][c][e] = octets_sum(acc[r][c][e]);
+      for (int e = 0; e < EPC; ++e) acc[r][c][e] = across_groups_sum<LPT>(acc[r][c][e]);
   }
   if (tsub == 0) {
 #pragma unroll
@@ -234,12 +276,12 @@ pa_valu_kernel(const Params p) {
 namespace {
 template <bool BF16, int D, int ROWS>
 hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, bool* ok) {
-  if (nw != 4) {
-    *ok = false;
-    return hipSuccess;
-  }
   *ok = true;
-  hipLaunchKernelGGL((pa_valu_kernel<BF16, D, ROWS, 4>), dim3(grid), dim3(4 * 64), 0, st, p);
+  switch (nw) {
+    case 4: hipLaunchKernelGGL((pa_valu_kernel<BF16, D, ROWS, 4>), dim3(grid), dim3(4 * 64), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((pa_valu_kernel<BF16, D, ROWS, 8>), dim3(grid), dim3(8 * 64), 0, st, p); break;
+    default: *ok = false; return hipSuccess;
+  }
   return hipGetLastError();
 }
 

@@ -131,7 +131,7 @@ def test_plan_choices(lib):
     # Global layer: 16 query heads on one KV head go to the matrix cores.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768,
                                           max_blocks_per_seq=2048)), ctypes.byref(info)) == 0
-    assert info.kernel == 1 and info.rows == 16 and info.splits > 1
+    assert info.kernel == 1 and info.rows == 16 and info.balanced == 1
     # Verify step: 4 heads x 5 tokens = 20 rows.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
                                           window=0, max_seq_len=16384, max_blocks_per_seq=1024)),

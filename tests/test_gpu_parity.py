@@ -152,13 +152,18 @@ def test_verify_rows_match_sequential_decode():
                     kv_dtype="bf16", seed=7)
     dev = Dev(x)
     full = dev.run_f64()
+    ref = _oracle(x)
+    assert max_err(full, ref) <= 1e-2
     for t in range(5):
         out = torch.empty_like(dev.q[:, t:t + 1])
         lens = dev.lens - (4 - t)
         pa.decode(out, dev.q[:, t:t + 1].contiguous(), dev.k, dev.v, dev.table, lens, window=0, scale=x.scale,
                   max_seq_len=x.max_seq_len)
         torch.cuda.synchronize()
-        assert max_err(out.float().cpu().numpy().astype(np.float64)[:, 0], full[:, t]) <= 1e-2
+        row = out.float().cpu().numpy().astype(np.float64)[:, 0]
+        assert max_err(row, ref[:, t]) <= 1e-2
+        # Two kernels, each rounding its own fp32 result to bf16: one bf16 ulp apart at most.
+        assert max_err(row, full[:, t]) <= 2e-2
 
 
 def test_int8_path_reduces_to_bf16_on_integer_data():
