@@ -17,7 +17,9 @@ Prints ONE JSON line on stdout (the run's record); diagnostics go to stderr.
   value     = queries per second over the K timed steps (query = one token of
               one sequence through all heads of the layer)
   roofline  = algorithmic bytes of a step / mean duration of the attention
-              kernel, timed with HIP events recorded on the launch stream
+              kernel; the library stamps a pair of HIP events from that
+              kernel's own dispatch on the launch stream (hipExtLaunchKernel),
+              the same start/end timestamps a kernel trace reports
   cpu_baseline = the fp64 oracle on the host's cores, same workload
 """
 
@@ -35,6 +37,39 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention queries/s and achieved KV HBM GB/s (% of MI355X peak)"
+
+# HBM bytes per launch of the timed kernel, from two rocprofv3 counter passes
+# over this benchmark (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, mean
+# over the run's launches of the kernel). Each is scaled by what the same
+# counter read, in the same run, for a plain 1 GiB device-to-device copy
+# (--calibrate-copy): FETCH_SIZE read 524314 KiB for 1048576 KiB read (factor
+# 2.0), WRITE_SIZE 1048576 KiB for 1048576 KiB written (factor 1.0). A figure
+# holds only for the kernel sources and the launch plan it was taken with;
+# for anything else the record's traffic is null.
+MEASURED_TRAFFIC = {
+    2: {"kernel_sources": "b00dcd1793c606ef",
+        "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256},
+        "fetch_kib": 132879, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
+}
+KERNEL_SOURCES = {0: ("pa_device.h", "pa_common.h", "pa_valu.hip"), 1: ("pa_device.h", "pa_common.h", "pa_mfma.hip")}
+
+
+def kernel_sources_sha(kernel: int) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "paged_kv_cache_94_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: int, plan: dict):
+    m = MEASURED_TRAFFIC.get(config)
+    if m is None or kernel_sources_sha(plan["kernel"]) != m["kernel_sources"]:
+        return None
+    if any(plan[k] != v for k, v in m["plan"].items()):
+        return None
+    return (m["fetch_kib"] * m["fetch_factor"] + m["write_kib"] * m["write_factor"]) * 1024
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 
@@ -141,12 +176,15 @@ def main() -> int:
 
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    srt = sorted(kern_ms)
+    pct = {k: srt[min(len(srt) - 1, int(f * len(srt)))] * 1e3 for k, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
     ms_per_step = elapsed / args.steps * 1e3
     queries = acct["queries"]
     value = queries * args.steps / elapsed
     achieved = acct["alg_bytes"] / kern_s / 1e9
     step_gbs = acct["alg_bytes"] / (elapsed / args.steps) / 1e9
-    log(f"attention kernel: mean {kern_s * 1e6:.2f} us (min {min(kern_ms) * 1e3:.2f}, max {max(kern_ms) * 1e3:.2f}) "
+    log(f"attention kernel: mean {kern_s * 1e6:.2f} us (p10 {pct['p10']:.2f}, median {pct['p50']:.2f}, "
+        f"p90 {pct['p90']:.2f}, min {min(kern_ms) * 1e3:.2f}, max {max(kern_ms) * 1e3:.2f}) "
         f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS * 100:.1f}% of peak; "
         f"whole step {ms_per_step * 1e3:.2f} us -> {step_gbs:.0f} GB/s, {value:.4g} queries/s")
 
@@ -196,12 +234,13 @@ def main() -> int:
             "batch": x.batch,
             "q_len": x.q_len,
             "alg_bytes_per_step": acct["alg_bytes"],
+            "kernel_us": {"mean": kern_s * 1e6, **pct},
             "step_GBps": step_gbs,
             "cache_copies": copies,
             "splits": plan["splits"],
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, plan)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -99,8 +99,10 @@ typedef struct {
   size_t workspace_bytes;     /* size of workspace */
   int32_t* debug_visits;      /* NULL, or [B][Hkv][max_blocks_per_seq] zeroed by the caller: the
                                  kernels add 1 for every (sequence, KV head, logical block) they load */
-  pa_event_t timing_start;    /* NULL, or an event recorded on `stream` just before the attention kernel */
-  pa_event_t timing_stop;     /* NULL, or an event recorded just after it (before any combine kernel) */
+  pa_event_t timing_start;    /* NULL, or a timing-enabled event: stamped when the attention kernel starts */
+  pa_event_t timing_stop;     /* NULL, or a timing-enabled event: stamped when it completes (before any combine
+                                 kernel). Both come from the kernel's own dispatch (hipExtLaunchKernel), so
+                                 their interval is the kernel's execution time with no marker overhead. */
 } pa_args;
 
 /* Plan the library would use for these arguments (informational). */

@@ -239,20 +239,19 @@ int run(const pa_args* a, pa_stream_t stream, Entry entry) {
   }
   const pa::Params p = make_params(a, P);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  pa::Timing tm;
+  tm.start = reinterpret_cast<hipEvent_t>(a->timing_start);
+  tm.stop = reinterpret_cast<hipEvent_t>(a->timing_stop);
   hipError_t e;
-  if (a->timing_start && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(a->timing_start), st)) != hipSuccess)
-    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   bool supported = false;
   if (P.kernel == 0)
-    e = pa::launch_valu(p, a->q_dtype, a->kv_dtype, a->head_dim, P.rows_t, P.nw, (int)P.grid, st, &supported);
+    e = pa::launch_valu(p, a->q_dtype, a->kv_dtype, a->head_dim, P.rows_t, P.nw, (int)P.grid, st, tm, &supported);
   else
-    e = pa::launch_mfma(p, a->kv_dtype, a->head_dim, P.row_tiles, P.nw, (int)P.grid, st, &supported);
+    e = pa::launch_mfma(p, a->kv_dtype, a->head_dim, P.row_tiles, P.nw, (int)P.grid, st, tm, &supported);
   if (!supported)
     return fail(PA_ERR_UNSUPPORTED, "no kernel built for D=%d rows=%d q_dtype=%d kv_dtype=%d", a->head_dim, P.rows,
                 a->q_dtype, a->kv_dtype);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
-  if (a->timing_stop && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(a->timing_stop), st)) != hipSuccess)
-    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   if (P.slots > 0) {
     e = pa::launch_combine(p, a->q_dtype, a->head_dim, st);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));

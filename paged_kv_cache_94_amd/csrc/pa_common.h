@@ -4,6 +4,8 @@
 // host dispatcher instantiates.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -74,10 +76,25 @@ struct LaunchShape {
   int nw;       // waves per workgroup
   int grid;     // workgroups
 };
+// Optional timing of the attention kernel. The kernel goes through
+// hipExtLaunchKernel, which stamps the two events from the kernel's own
+// dispatch (its start and its completion) rather than from separate marker
+// commands queued around it, so the interval is the kernel's execution time.
+struct Timing {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename K>
+inline hipError_t launch_timed(K kernel, int grid, int threads, hipStream_t st, const Timing& tm, const Params& p) {
+  hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, tm.start, tm.stop, 0, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_valu(const Params& p, int q_dtype, int kv_dtype, int D, int rows_t, int nw, int grid,
-                       hipStream_t st, bool* supported);
+                       hipStream_t st, const Timing& tm, bool* supported);
 hipError_t launch_mfma(const Params& p, int kv_dtype, int D, int row_tiles, int nw, int grid,
-                       hipStream_t st, bool* supported);
+                       hipStream_t st, const Timing& tm, bool* supported);
 hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st);
 hipError_t launch_gather(const Params& p, int kv_dtype, int D, int which, void* dst, int64_t dst_tokens,
                          hipStream_t st);

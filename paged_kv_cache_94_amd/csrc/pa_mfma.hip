@@ -438,42 +438,42 @@ pa_mfma_kernel(const Params p) {
 
 namespace {
 template <bool INT8, bool ALIAS, int D, int MT>
-hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, bool* ok) {
+hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
   *ok = true;
   switch (nw) {
-    case 4: hipLaunchKernelGGL((pa_mfma_kernel<INT8, ALIAS, D, MT, 4>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((pa_mfma_kernel<INT8, ALIAS, D, MT, 8>), dim3(grid), dim3(512), 0, st, p); break;
-    default: *ok = false; return hipSuccess;
+    case 4: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 4>, grid, 256, st, tm, p);
+    case 8: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 8>, grid, 512, st, tm, p);
   }
-  return hipGetLastError();
+  *ok = false;
+  return hipSuccess;
 }
 
 template <bool INT8, bool ALIAS>
-hipError_t by_shape(const Params& p, int D, int mt, int nw, int grid, hipStream_t st, bool* ok) {
+hipError_t by_shape(const Params& p, int D, int mt, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
   *ok = false;
   if (mt == 1) {
-    if (D == 64) return launch_one<INT8, ALIAS, 64, 1>(p, nw, grid, st, ok);
-    if (D == 128) return launch_one<INT8, ALIAS, 128, 1>(p, nw, grid, st, ok);
-    if (D == 256) return launch_one<INT8, ALIAS, 256, 1>(p, nw, grid, st, ok);
+    if (D == 64) return launch_one<INT8, ALIAS, 64, 1>(p, nw, grid, st, tm, ok);
+    if (D == 128) return launch_one<INT8, ALIAS, 128, 1>(p, nw, grid, st, tm, ok);
+    if (D == 256) return launch_one<INT8, ALIAS, 256, 1>(p, nw, grid, st, tm, ok);
   } else if (mt == 2) {
-    if (D == 64) return launch_one<INT8, ALIAS, 64, 2>(p, nw, grid, st, ok);
-    if (D == 128) return launch_one<INT8, ALIAS, 128, 2>(p, nw, grid, st, ok);
+    if (D == 64) return launch_one<INT8, ALIAS, 64, 2>(p, nw, grid, st, tm, ok);
+    if (D == 128) return launch_one<INT8, ALIAS, 128, 2>(p, nw, grid, st, tm, ok);
   }
   return hipSuccess;
 }
 }  // namespace
 
 hipError_t launch_mfma(const Params& p, int kv_dtype, int D, int row_tiles, int nw, int grid,
-                       hipStream_t st, bool* supported) {
+                       hipStream_t st, const Timing& tm, bool* supported) {
   *supported = false;
   const bool alias = p.v_pool == p.k_pool;
   if (kv_dtype == 2) {
-    return alias ? by_shape<true, true>(p, D, row_tiles, nw, grid, st, supported)
-                 : by_shape<true, false>(p, D, row_tiles, nw, grid, st, supported);
+    return alias ? by_shape<true, true>(p, D, row_tiles, nw, grid, st, tm, supported)
+                 : by_shape<true, false>(p, D, row_tiles, nw, grid, st, tm, supported);
   }
   if (kv_dtype == 1) {
-    return alias ? by_shape<false, true>(p, D, row_tiles, nw, grid, st, supported)
-                 : by_shape<false, false>(p, D, row_tiles, nw, grid, st, supported);
+    return alias ? by_shape<false, true>(p, D, row_tiles, nw, grid, st, tm, supported)
+                 : by_shape<false, false>(p, D, row_tiles, nw, grid, st, tm, supported);
   }
   return hipSuccess;
 }

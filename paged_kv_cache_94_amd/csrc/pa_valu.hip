@@ -275,24 +275,24 @@ pa_valu_kernel(const Params p) {
 
 namespace {
 template <bool BF16, int D, int ROWS>
-hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, bool* ok) {
+hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
   *ok = true;
   switch (nw) {
-    case 4: hipLaunchKernelGGL((pa_valu_kernel<BF16, D, ROWS, 4>), dim3(grid), dim3(4 * 64), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((pa_valu_kernel<BF16, D, ROWS, 8>), dim3(grid), dim3(8 * 64), 0, st, p); break;
-    default: *ok = false; return hipSuccess;
+    case 4: return launch_timed(pa_valu_kernel<BF16, D, ROWS, 4>, grid, 4 * 64, st, tm, p);
+    case 8: return launch_timed(pa_valu_kernel<BF16, D, ROWS, 8>, grid, 8 * 64, st, tm, p);
   }
-  return hipGetLastError();
+  *ok = false;
+  return hipSuccess;
 }
 
 template <bool BF16, int D>
-hipError_t by_rows(const Params& p, int rows_t, int nw, int grid, hipStream_t st, bool* ok) {
+hipError_t by_rows(const Params& p, int rows_t, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
   // Query rows live in registers next to a row slice of D/8 elements: keep rows * D / 8 <= 64.
   switch (rows_t) {
-    case 1: return launch_one<BF16, D, 1>(p, nw, grid, st, ok);
-    case 2: return launch_one<BF16, D, 2>(p, nw, grid, st, ok);
-    case 4: if constexpr (D <= 128) return launch_one<BF16, D, 4>(p, nw, grid, st, ok); break;
-    case 8: if constexpr (D <= 64) return launch_one<BF16, D, 8>(p, nw, grid, st, ok); break;
+    case 1: return launch_one<BF16, D, 1>(p, nw, grid, st, tm, ok);
+    case 2: return launch_one<BF16, D, 2>(p, nw, grid, st, tm, ok);
+    case 4: if constexpr (D <= 128) return launch_one<BF16, D, 4>(p, nw, grid, st, tm, ok); break;
+    case 8: if constexpr (D <= 64) return launch_one<BF16, D, 8>(p, nw, grid, st, tm, ok); break;
   }
   *ok = false;
   return hipSuccess;
@@ -300,17 +300,17 @@ hipError_t by_rows(const Params& p, int rows_t, int nw, int grid, hipStream_t st
 }  // namespace
 
 hipError_t launch_valu(const Params& p, int q_dtype, int kv_dtype, int D, int rows_t, int nw, int grid,
-                       hipStream_t st, bool* supported) {
+                       hipStream_t st, const Timing& tm, bool* supported) {
   *supported = false;
   const bool bf16 = kv_dtype == 1;
   if (q_dtype != kv_dtype || kv_dtype > 1) return hipSuccess;
   switch (D) {
-    case 64: return bf16 ? by_rows<true, 64>(p, rows_t, nw, grid, st, supported)
-                         : by_rows<false, 64>(p, rows_t, nw, grid, st, supported);
-    case 128: return bf16 ? by_rows<true, 128>(p, rows_t, nw, grid, st, supported)
-                          : by_rows<false, 128>(p, rows_t, nw, grid, st, supported);
-    case 256: return bf16 ? by_rows<true, 256>(p, rows_t, nw, grid, st, supported)
-                          : by_rows<false, 256>(p, rows_t, nw, grid, st, supported);
+    case 64: return bf16 ? by_rows<true, 64>(p, rows_t, nw, grid, st, tm, supported)
+                         : by_rows<false, 64>(p, rows_t, nw, grid, st, tm, supported);
+    case 128: return bf16 ? by_rows<true, 128>(p, rows_t, nw, grid, st, tm, supported)
+                          : by_rows<false, 128>(p, rows_t, nw, grid, st, tm, supported);
+    case 256: return bf16 ? by_rows<true, 256>(p, rows_t, nw, grid, st, tm, supported)
+                          : by_rows<false, 256>(p, rows_t, nw, grid, st, tm, supported);
   }
   return hipSuccess;
 }
