@@ -113,9 +113,11 @@ typedef struct {
   int32_t splits;             /* aligned partition: context splits per sequence (1: no combine kernel) */
   int32_t blocks_per_split;   /* aligned partition: logical blocks per split */
   int32_t grid;               /* workgroups of the attention kernel */
-  int32_t balanced;           /* 1: every workgroup takes an equal share of the flattened
-                                 (sequence, KV head, block) list, cut where a sequence ends;
-                                 0: each workgroup owns one split of one (sequence, KV head) */
+  int32_t balanced;           /* 0: each workgroup owns one split of one (sequence, KV head);
+                                 1: every workgroup takes an equal share of the flattened
+                                 (sequence, KV head, block) list, cut where a unit ends;
+                                 2: every workgroup takes one near-equal piece of one unit
+                                 (few units: long contexts on one or two KV heads) */
   size_t workspace_bytes;     /* == pa_workspace_size() */
 } pa_plan_info;
 

@@ -53,14 +53,13 @@ struct Plan {
   int splits = 1;
   int bps = 1;
   int n_blk_max = 0;
-  int balanced = 0;     // 1: work-balanced partition over nwg workgroups
+  int balanced = 0;     // 1: flattened-list partition, 2: piece partition (both over nwg workgroups)
   int nwg = 0;
   int64_t slots = 0;    // workspace partial slots
   int64_t grid = 0;
   size_t ws_bytes = 0;
 };
 
-constexpr int kMaxBalancedSeqs = 4096;   // must match the kernel's LDS prefix array
 
 enum Entry { kDecode, kDecodeInt8, kVerify, kAny, kGather };
 
@@ -123,7 +122,7 @@ int make_plan(const pa_args* a, Plan* pl) {
     P.rows_t = 1;
     while (P.rows_t < P.rows) P.rows_t *= 2;
   }
-  P.nw = 8;
+  P.nw = P.kernel == 1 ? 4 : 8;   // matrix-core: two 4-wave workgroups per CU measured faster than one of 8
 
   const int bs = a->block_size;
   int n_blk_max = (a->max_seq_len + bs - 1) / bs;
@@ -164,17 +163,24 @@ int make_plan(const pa_args* a, Plan* pl) {
   P.grid = units * P.splits;
   P.slots = P.splits > 1 ? units * P.splits : 0;
 
-  // The matrix-core kernel defaults to the work-balanced partition: one
-  // workgroup per compute unit (two when they are 4 waves), each streaming
-  // the same number of blocks whatever the length mix. Forced splits, the
-  // vector kernel and very large batches keep the aligned splits.
-  bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= kMaxBalancedSeqs;
+  // The matrix-core kernel defaults to a work-balanced partition over as
+  // many workgroups as are resident at once (two per compute unit at 4
+  // waves, one at 8), each streaming about the same number of blocks
+  // whatever the length mix. With few units (long contexts on one or two KV
+  // heads) each workgroup takes one piece of one unit (partition 2); with
+  // many, a slice of the flattened (unit, block) list that may span several
+  // units (partition 1). Forced splits, the vector kernel and very large
+  // batches keep the aligned splits. PA_BALANCED=0 / PA_PIECES=0 turn the
+  // balanced partitions / the piece partition off (for tests and experiments).
+  bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= pa::kMaxBalancedSeqs;
   if (const char* e = getenv("PA_BALANCED")) balanced = balanced && atoi(e) != 0;
   if (balanced) {
-    P.balanced = 1;
     P.nwg = cu_count() * (8 / P.nw);
+    bool pieces = 2 * units <= P.nwg && a->num_seqs <= pa::kMaxPieceSeqs;
+    if (const char* e = getenv("PA_PIECES")) pieces = pieces && atoi(e) != 0;
+    P.balanced = pieces ? 2 : 1;
     P.grid = P.nwg;
-    P.slots = P.nwg + units;
+    P.slots = pieces ? P.nwg : P.nwg + units;
   }
   if (P.grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
   if (P.slots > 0) {

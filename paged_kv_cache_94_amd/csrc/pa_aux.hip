@@ -10,68 +10,100 @@
 
 namespace pa {
 
+// Number of combine workgroups per output row: one per unit for aligned
+// splits and the piece partition, one per workgroup boundary for the
+// flattened-list partition (only units cut by a boundary have partials).
+__host__ __device__ inline int64_t combine_groups(const Params& p) {
+  return p.balanced == 1 ? (int64_t)(p.nwg > 1 ? p.nwg - 1 : 0) : (int64_t)p.B * p.Hkv;
+}
+
+constexpr int kCombineChunk = 64;   // partials whose loads are in flight together
+
 template <typename OutT, int D>
 __global__ void __launch_bounds__(D) pa_combine_kernel(const Params p) {
-  // One workgroup per output row (unit, r); thread d owns dim d. The split's
-  // (m, l) pair is the same for the whole workgroup (a uniform load).
-  const int32_t row_id = blockIdx.x;
-  const int r = row_id % p.rows;
-  const int32_t unit = row_id / p.rows;
-  const int32_t b = unit / p.Hkv;
-  const int32_t g = unit % p.Hkv;
-  const int32_t L = p.seq_lens[b];
-  if (!len_ok(L, p)) return;
-  // Slots holding this unit's partials: contiguous in both partitions.
+  // Workgroup (group, r): output row r of one unit; thread d owns dim d.
+  const int r = blockIdx.x % p.rows;
+  const int32_t grp = blockIdx.x / p.rows;
+  const int lane = threadIdx.x & 63;
+  int32_t b, g;
   int64_t slot_first;
   int32_t ns;
-  if (p.balanced) {
-    // Workgroups w0..w1 each left a partial in slot w + unit; a unit inside a
-    // single workgroup's slice was written out directly.
-    const int32_t* pre = p.ws_prefix;
-    const int32_t nb = pre[b + 1] - pre[b];
-    if (nb == 0) return;
+  if (p.balanced == 1) {
+    // Boundary grp lies between workgroups grp and grp+1, at item x of the
+    // flattened list. The unit holding x is merged here if it starts inside
+    // workgroup grp (it is then cut by this boundary first); workgroups
+    // w0..w1 left its partials in slots w + unit. The block prefix sums are
+    // staged in LDS so the search below costs no memory round trips.
+    __shared__ int32_t pre[kMaxBalancedSeqs + 1];
+    for (int32_t i = threadIdx.x; i <= p.B; i += D) pre[i] = p.ws_prefix[i];
+    __syncthreads();
     const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
-    const int64_t off = (int64_t)p.Hkv * pre[b] + (int64_t)g * nb;
-    const int64_t w0 = off / bal.per, w1 = (off + nb - 1) / bal.per;
-    if (w0 == w1) return;
-    slot_first = w0 + unit;
-    ns = (int32_t)(w1 - w0 + 1);
+    const int64_t x = (int64_t)(grp + 1) * bal.per;
+    if (x >= bal.total) return;
+    b = balanced_seq(pre, p.B, p.Hkv, x);
+    const int32_t nb = pre[b + 1] - pre[b];
+    const int64_t base = (int64_t)p.Hkv * pre[b];
+    g = (int32_t)((x - base) / nb);
+    const int64_t off = base + (int64_t)g * nb;
+    if (off >= x || off < (int64_t)grp * bal.per) return;
+    const int64_t w1 = (off + nb - 1) / bal.per;
+    slot_first = grp + (int64_t)b * p.Hkv + g;
+    ns = (int32_t)(w1 - grp + 1);
   } else {
-    const KeyRange kr = key_range(L, p.q_len, p.window);
-    slot_first = (int64_t)unit * p.splits;
-    ns = min(live_splits(kr, p.bps), p.splits);
+    b = grp / p.Hkv;
+    g = grp % p.Hkv;
+    const int32_t L = p.seq_lens[b];
+    if (!len_ok(L, p)) return;
+    if (p.balanced == 2) {
+      // Piece partition: unit (b, g) was cut into k pieces, owned by
+      // workgroups kp[b] + g*k .. + k-1, each of which left its partial in
+      // the slot of its own index; a unit of one piece was written out directly.
+      const int32_t k = (p.ws_prefix[b + 1] - p.ws_prefix[b]) / p.Hkv;
+      if (k <= 1) return;
+      slot_first = p.ws_prefix[b] + (int64_t)g * k;
+      ns = k;
+    } else {
+      const KeyRange kr = key_range(L, p.q_len, p.window);
+      slot_first = (int64_t)grp * p.splits;
+      ns = min(live_splits(kr, p.bps), p.splits);
+    }
   }
 
   const size_t slot0 = (size_t)slot_first * p.rows + r;
   const size_t step = (size_t)p.rows;
   const float* ml = p.ws_ml + slot0 * 2;
   const float* acc = p.ws_acc + slot0 * D + threadIdx.x;
-  const int lane = threadIdx.x & 63;
 
-  // Split s's (m, l) sits in lane s % 64: the max and the weights come from
-  // wave reductions, and every split's accumulator load below is independent.
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[s * step * 2]);
+  // Chunks of up to 64 partials: every load of a chunk is issued before any
+  // is used. Partial s's (m, l) sits in lane s % 64; the chunk max and the
+  // weights come from wave reductions and v_readlane. Chunks after the first
+  // rescale the running sums (online-softmax rule).
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int32_t c0 = 0; c0 < ns; c0 += kCombineChunk) {
+    const int32_t cnt = min(kCombineChunk, ns - c0);
+    float a[kCombineChunk];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float num = 0.f, den = 0.f;
-  for (int c0 = 0; c0 < ns; c0 += 64) {
-    const int s = c0 + lane;
-    float w = 0.f;
-    if (s < ns) {
-      w = fast_exp2(ml[s * step * 2] - Ms);
-      den += w * ml[s * step * 2 + 1];
-    }
-    const int cnt = min(64, ns - c0);
-#pragma unroll 8
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      num += wj * acc[(size_t)(c0 + j) * step * D];
-    }
+    for (int j = 0; j < kCombineChunk; ++j) a[j] = j < cnt ? acc[(size_t)(c0 + j) * step * D] : 0.f;
+    const float ms = lane < cnt ? ml[(size_t)(c0 + lane) * step * 2] : -INFINITY;
+    const float ls = lane < cnt ? ml[(size_t)(c0 + lane) * step * 2 + 1] : 0.f;
+    float cm = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor(cm, off));
+    const float Mn = fmaxf(M, cm);
+    const float Ms = Mn == -INFINITY ? 0.f : Mn;
+    const float resc = fast_exp2(M - Ms);   // 0 on the first chunk (M = -inf)
+    num *= resc;
+    den *= resc;
+    M = Mn;
+    const float w = lane < cnt ? fast_exp2(ms - Ms) : 0.f;
+    float dl = w * ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dl += shfl_xor(dl, off);
+    den += dl;
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j)
+      num += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j)) * a[j];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += shfl_xor(den, off);
   const int t = r / p.G;
   const int h = g * p.G + r % p.G;
   OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + threadIdx.x;
@@ -106,7 +138,7 @@ __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const ch
 }
 
 hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
-  const int64_t rows = (int64_t)p.B * p.Hkv * p.rows;
+  const int64_t rows = combine_groups(p) * p.rows;
   if (rows == 0) return hipSuccess;
   if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)rows);

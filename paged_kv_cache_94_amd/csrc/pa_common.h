@@ -70,6 +70,10 @@ __device__ __forceinline__ void merge_and_store(const Params& p, const float* ld
 
 // Host-side launchers, one per kernel family (defined in the .hip files).
 namespace pa {
+// Batch limits of the balanced partitions (their per-sequence tables live in LDS).
+constexpr int kMaxBalancedSeqs = 4096;   // flattened-list partition: block prefix sums
+constexpr int kMaxPieceSeqs = 512;       // piece partition: blocks per sequence
+
 struct LaunchShape {
   int kernel;   // 0 valu, 1 mfma
   int rows_t;   // compiled row count (>= rows)

@@ -37,9 +37,9 @@ struct Params {
   int32_t window;
   float scale_log2;     // caller's scale times log2(e): scores live in base-2 exponent units
   int32_t splits, bps;  // aligned mode: splits per sequence and logical blocks per split
-  int32_t balanced;     // 1: work-balanced partition over nwg workgroups, 0: aligned splits
-  int32_t nwg;          // balanced mode: workgroups sharing the flattened work list
-  int32_t* ws_prefix;   // balanced mode: [B+1] prefix sums of blocks per sequence (workgroup 0 writes)
+  int32_t balanced;     // 0: aligned splits; 1: flattened-list partition; 2: piece partition
+  int32_t nwg;          // modes 1 and 2: workgroups of the launch
+  int32_t* ws_prefix;   // mode 1: [B+1] block prefix sums; mode 2: [B+1] piece prefix sums (workgroup 0 writes)
 };
 
 // Keys a step touches for one sequence (Lab 5 handout, "Sliding Window
@@ -144,6 +144,96 @@ __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre) {
   }
 }
 
+// Piece partition, for batches with few (sequence, KV head) units compared
+// with the workgroups that fit on the device (long contexts, one or two KV
+// heads). Unit (b, g) with n_b blocks is cut into k_b = ceil(n_b / per)
+// pieces of ceil(n_b / k_b) blocks; `per` is the smallest count for which
+// every unit's pieces fit in nwg workgroups. Workgroup w owns piece w of the
+// list ordered by (b, g, piece), so every workgroup streams one run of one
+// unit with a single start-up, and none streams more than `per` blocks.
+//
+// Wave 0 fills nbs[b] = n_b and kp[0..B] = Hkv * (k_0 + ... + k_{b-1}); the
+// caller synchronises the workgroup before reading them. `per` is at least
+// min_per (enough blocks for every wavefront of the workgroup). Needs
+// nwg >= 2 * B * Hkv (checked on the host), which bounds the search below.
+template <typename P>
+__device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* kp, int32_t min_per) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int64_t total = 0;
+  for (int32_t b = lane; b < p.B; b += 64) {
+    const int32_t nb = seq_blocks(p.seq_lens[b], p);
+    nbs[b] = nb;
+    total += nb;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
+  total *= p.Hkv;
+  // Pieces needed with at most `per` blocks each: sum over units of ceil(n / per).
+  auto pieces = [&](int32_t per) {
+    int32_t c = 0;
+    for (int32_t b = lane; b < p.B; b += 64) c += (nbs[b] + per - 1) / per;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+    return (int64_t)c * p.Hkv;
+  };
+  // pieces(per) <= total / per + B*Hkv, so per_hi = ceil(total / (nwg - B*Hkv)) always fits.
+  const int64_t spare = (int64_t)p.nwg - (int64_t)p.B * p.Hkv;
+  int64_t lo = (total + p.nwg - 1) / p.nwg;
+  int64_t hi = spare > 0 ? (total + spare - 1) / spare : total;
+  if (lo < min_per) lo = min_per;
+  if (hi < lo) hi = lo;   // pieces() only falls as per grows
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (pieces((int32_t)mid) <= p.nwg) hi = mid;
+    else lo = mid + 1;
+  }
+  const int32_t per = (int32_t)lo;
+  if (lane == 0) kp[0] = 0;
+  int32_t carry = 0;
+  for (int32_t base = 0; base < p.B; base += 64) {
+    const int32_t b = base + lane;
+    int32_t v = b < p.B ? (nbs[b] + per - 1) / per * p.Hkv : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t t = __shfl_up(v, off);
+      if (lane >= off) v += t;
+    }
+    if (b < p.B) kp[b + 1] = carry + v;
+    carry += __shfl(v, 63);
+  }
+}
+
+// The piece of work a workgroup owns in the piece partition.
+struct Piece {
+  int32_t b, g;
+  int32_t k;       // pieces of this unit (1: the workgroup writes the output itself)
+  int32_t first;   // offset of its first block inside the unit's key range
+  int32_t count;   // blocks it streams (>= 1)
+};
+
+// Piece w (< kp[B]) of the list: the largest b with kp[b] <= w owns it.
+__device__ __forceinline__ Piece piece_of(const int32_t* nbs, const int32_t* kp, int32_t B, int32_t Hkv,
+                                          int32_t w) {
+  int32_t lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (kp[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  Piece pc;
+  pc.b = lo;
+  pc.k = (kp[lo + 1] - kp[lo]) / Hkv;
+  const int32_t r = w - kp[lo];
+  pc.g = r / pc.k;
+  const int32_t i = r % pc.k;
+  const int32_t nb = nbs[lo];
+  const int32_t len = (nb + pc.k - 1) / pc.k;   // (k-1)*len < nb: every piece is non-empty
+  pc.first = i * len;
+  pc.count = min(nb, pc.first + len) - pc.first;
+  return pc;
+}
+
 // Byte offset of (physical block, slot, kv head) row inside a pool laid out
 // [num_blocks][16][Hkv][D] (tiniestgpt notes, "PagedAttention").
 __device__ __forceinline__ size_t row_offset_bytes(int32_t phys, int32_t slot, int32_t g, int32_t Hkv,
@@ -233,6 +323,36 @@ __device__ __forceinline__ int32_t settle(int32_t v) {
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes at `base` (gfx9 family: stride 0,
+// descriptor word 3 = 0x00020000). A load at an offset past `bytes` returns 0
+// and touches no memory, so a descriptor of zero bytes turns a load into a
+// no-op that still counts as an issued load: a software pipeline can then
+// issue the same loads on every path, which keeps the compiler's wait counts
+// exact (a load issued on only some paths makes it wait for everything).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+constexpr int kCacheNonTemporal = 2;   // buffer cache policy: NT (data read once)
+
+// voff: per-lane byte offset; soff: wave-uniform byte offset (a scalar register).
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff = 0) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCacheNonTemporal);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Mark a loaded value as used. A pipeline's last prefetch is dead once the
+// loop exits; without a use on the exit path the compiler moves those loads
+// behind the exit branch, which makes them conditional again (and its wait
+// counts conservative).
+__device__ __forceinline__ void keep_loaded(const uint4& v) {
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void keep_loaded(float v) { asm volatile("" ::"v"(v)); }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 

@@ -70,7 +70,10 @@ struct MfmaLds {
   static constexpr int ROWS = 16 * MT;
   static constexpr int VSTRIDE = D * 2 + 32;                 // bytes per staged V row (32-byte skew against bank conflicts)
   static constexpr int STAGE = NW * 16 * VSTRIDE;            // one V tile per wavefront
-  static constexpr int MERGE = (NW > 1 ? NW / 2 : 1) * ROWS * (D + 2) * 4;
+  // Merge: waves 1..NW-1 park o [ROWS][D] (row stride D + 4 floats: the 16
+  // rows a 16-lane group writes start in 16 different 4-bank groups) and (m, l).
+  static constexpr int MSTRIDE = D + 4;
+  static constexpr int MERGE = (NW - 1) * ROWS * (MSTRIDE + 2) * 4;
   static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
 };
 
@@ -125,9 +128,13 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     for (int j = 0; j < TJ; ++j) o[tile][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t tok_stride = (size_t)p.Hkv * ROW_BYTES;
-  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES + n * tok_stride;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES + n * tok_stride;
+  // A (block, KV head) tile: 16 rows of ROW_BYTES, tok_stride apart. Lane l
+  // reads row n at byte offsets 16*q4 + 64*u of it.
+  const int32_t tok_stride = p.Hkv * ROW_BYTES;
+  const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
+  const int32_t lane_off = n * tok_stride + 16 * q4;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
@@ -150,22 +157,46 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   int32_t nmine = 0;
   int32_t tbl = 0;
 
-  auto fetch = [&](int32_t k, Fetched& f) __attribute__((always_inline)) {
-    const int32_t phys = __builtin_amdgcn_readlane(tbl, k);
-    const size_t blk_off = (size_t)phys * kBlock * tok_stride;
+  // Block k of this wavefront (k >= nmine: a no-op load of zero bytes, so
+  // every path through the pipeline issues the same loads).
+  auto keep = [&](const Fetched& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < NLOAD; ++u) f.k[u] = load16_stream(kbase + blk_off + 16 * q4 + 64 * u);
+    for (int u = 0; u < NLOAD; ++u) keep_loaded(f.k[u]);
     if constexpr (!ALIAS) {
 #pragma unroll
-      for (int u = 0; u < NLOAD; ++u) f.v[u] = load16_stream(vbase + blk_off + 16 * q4 + 64 * u);
+      for (int u = 0; u < NLOAD; ++u) keep_loaded(f.v[u]);
     }
     if constexpr (INT8) {
-      const float* ks = p.k_scale + ((size_t)phys * kBlock + 4 * q4) * p.Hkv + g;
-      const float* vs = p.v_scale + ((size_t)phys * kBlock + 4 * q4) * p.Hkv + g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        f.ks[e] = ks[(size_t)e * p.Hkv];
-        f.vs[e] = vs[(size_t)e * p.Hkv];
+        keep_loaded(f.ks[e]);
+        keep_loaded(f.vs[e]);
+      }
+    }
+  };
+
+  auto fetch = [&](int32_t k, Fetched& f) __attribute__((always_inline)) {
+    const bool valid = k < nmine;
+    const int32_t phys = __builtin_amdgcn_readlane(tbl, valid ? k : 0);
+    const size_t tile = (size_t)phys * kBlock * (size_t)tok_stride;
+    const auto kd = buffer_rsrc(kpool + tile, valid ? tile_bytes : 0);
+#pragma unroll
+    for (int u = 0; u < NLOAD; ++u) f.k[u] = buffer_load16(kd, lane_off + 64 * u);
+    if constexpr (!ALIAS) {
+      const auto vd = buffer_rsrc(vpool + tile, valid ? tile_bytes : 0);
+#pragma unroll
+      for (int u = 0; u < NLOAD; ++u) f.v[u] = buffer_load16(vd, lane_off + 64 * u);
+    }
+    if constexpr (INT8) {
+      // Scales of tokens 4*q4 .. 4*q4+3 (the score rows of this lane), Hkv floats apart.
+      const size_t s0 = (size_t)phys * kBlock * p.Hkv + g;
+      const int32_t sbytes = valid ? ((kBlock - 1) * p.Hkv + 1) * 4 : 0;
+      const auto ksd = buffer_rsrc(p.k_scale + s0, sbytes);
+      const auto vsd = buffer_rsrc(p.v_scale + s0, sbytes);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f.ks[e] = buffer_load_f32(ksd, (4 * q4 + e) * p.Hkv * 4);
+        f.vs[e] = buffer_load_f32(vsd, (4 * q4 + e) * p.Hkv * 4);
       }
     }
   };
@@ -184,7 +215,6 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 
   auto consume = [&](int32_t k, const Fetched& f) __attribute__((always_inline)) {
     const int32_t i = cfirst + wave + NW * k;   // logical block
-    if (visits && lane == 0) atomicAdd(visits + i, 1);
 
     // Stage this lane's V row (token n) in LDS as bf16. A row nobody may see
     // can hold anything and is written as zeros (only edge blocks have such rows).
@@ -285,17 +315,26 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     const int32_t clast = min(last, cfirst + 64 * NW - 1);
     nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
     tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
+    // Debug load counts, kept out of the pipelined loop below.
+    if (visits && lane < nmine) atomicAdd(visits + cfirst + wave + NW * lane, 1);
     if constexpr (PIPE) {
+      // Block k+1 is in flight while block k is consumed. The loop body has no
+      // exit and its fetches are unconditional (past the end they load zero
+      // bytes), so every path into its head has the same loads outstanding
+      // and the compiler waits only for the block it consumes.
       Fetched fa, fb;
-      if (nmine > 0) fetch(0, fa);
-      for (int32_t k = 0; k < nmine; k += 2) {
-        const bool has_b = k + 1 < nmine;
-        if (has_b) fetch(k + 1, fb);
+      fetch(0, fa);
+      const int32_t pairs = nmine >> 1;
+      for (int32_t k = 0; k < 2 * pairs; k += 2) {
+        fetch(k + 1, fb);
         consume(k, fa);
-        if (!has_b) break;
-        if (k + 2 < nmine) fetch(k + 2, fa);
+        __builtin_amdgcn_sched_barrier(0);   // refill a buffer only once it is consumed
+        fetch(k + 2, fa);
         consume(k + 1, fb);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (nmine & 1) consume(nmine - 1, fa);
+      keep(fa);
     } else {
       Fetched fa;
       for (int32_t k = 0; k < nmine; ++k) {
@@ -309,47 +348,48 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) l[tile] = quads16_sum(l[tile]);
 
-  // Merge the wavefronts pairwise through LDS (reusing the staging area): in
-  // each round the upper half parks its (m, l, o) and the lower half folds it
-  // in with the online-softmax rule.
+  // Merge the wavefronts through LDS (reusing the staging area): waves
+  // 1..NW-1 park (m, l, o), wave 0 folds them in with the online-softmax rule.
+  constexpr int MS = Lds::MSTRIDE;
   float* lds_acc = reinterpret_cast<float*>(smem);
-  float* lds_ml = lds_acc + (NW > 1 ? NW / 2 : 1) * ROWS * D;
+  float* lds_ml = lds_acc + (NW - 1) * ROWS * MS;
+  __syncthreads();   // every wavefront is done with its staging tile
+  if (wave > 0) {
+    const int slot = wave - 1;
 #pragma unroll
-  for (int half = NW / 2; half >= 1; half /= 2) {
-    __syncthreads();
-    if (wave >= half && wave < 2 * half) {
-      const int slot = wave - half;
+    for (int tile = 0; tile < MT; ++tile) {
+      const int r = n + 16 * tile;
 #pragma unroll
-      for (int tile = 0; tile < MT; ++tile) {
-        const int r = n + 16 * tile;
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          *reinterpret_cast<f32x4*>(lds_acc + (slot * ROWS + r) * D + 16 * j + 4 * q4) = o[tile][j];
-        if (q4 == 0) {
-          lds_ml[(slot * ROWS + r) * 2] = m[tile];
-          lds_ml[(slot * ROWS + r) * 2 + 1] = l[tile];
-        }
+      for (int j = 0; j < TJ; ++j)
+        *reinterpret_cast<f32x4*>(lds_acc + (slot * ROWS + r) * MS + 16 * j + 4 * q4) = o[tile][j];
+      if (q4 == 0) {
+        lds_ml[(slot * ROWS + r) * 2] = m[tile];
+        lds_ml[(slot * ROWS + r) * 2 + 1] = l[tile];
       }
     }
-    __syncthreads();
-    if (wave < half) {
+  }
+  __syncthreads();
+  if (wave != 0) return;
 #pragma unroll
-      for (int tile = 0; tile < MT; ++tile) {
-        const int r = n + 16 * tile;
-        const float m1 = lds_ml[(wave * ROWS + r) * 2];
-        const float l1 = lds_ml[(wave * ROWS + r) * 2 + 1];
-        const float M = fmaxf(m[tile], m1);
-        const float Ms = M == -INFINITY ? 0.f : M;
-        const float a0 = fast_exp2(m[tile] - Ms);
-        const float a1 = fast_exp2(m1 - Ms);
-        m[tile] = M;
-        l[tile] = a0 * l[tile] + a1 * l1;
+  for (int tile = 0; tile < MT; ++tile) {
+    const int r = n + 16 * tile;
+    float M = m[tile];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          o[tile][j] = a0 * o[tile][j] +
-                       a1 * *reinterpret_cast<const f32x4*>(lds_acc + (wave * ROWS + r) * D + 16 * j + 4 * q4);
-      }
+    for (int s = 0; s < NW - 1; ++s) M = fmaxf(M, lds_ml[(s * ROWS + r) * 2]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    const float a0 = fast_exp2(m[tile] - Ms);
+    l[tile] *= a0;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) o[tile][j] *= a0;
+#pragma unroll 1
+    for (int s = 0; s < NW - 1; ++s) {   // one slot at a time keeps the loads' registers bounded
+      const float a = fast_exp2(lds_ml[(s * ROWS + r) * 2] - Ms);
+      l[tile] += a * lds_ml[(s * ROWS + r) * 2 + 1];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        o[tile][j] += a * *reinterpret_cast<const f32x4*>(lds_acc + (s * ROWS + r) * MS + 16 * j + 4 * q4);
     }
+    m[tile] = M;
   }
   if (wave != 0) return;
 
@@ -383,7 +423,6 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   }
 }
 
-constexpr int kMaxBalancedSeqs = 4096;   // sequences the balanced partition handles (prefix sums in LDS)
 
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -405,12 +444,30 @@ pa_mfma_kernel(const Params p) {
     mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, L, kr, first, last, slot);
     return;
   }
-  // Balanced partition: this workgroup's slice of the flattened (unit, block)
+  __shared__ int32_t pre[kMaxBalancedSeqs + 1];
+  if (p.balanced == 2) {
+    // Piece partition: one run of one unit per workgroup; the slot of a
+    // partial is the workgroup's own index.
+    __shared__ int32_t nbs[kMaxPieceSeqs];
+    piece_prefix(p, nbs, pre, 2 * NW);
+    __syncthreads();
+    if (blockIdx.x == 0 && p.ws_prefix)
+      for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
+    const int32_t w = blockIdx.x;
+    if (w >= pre[p.B]) return;
+    const Piece pc = piece_of(nbs, pre, p.B, p.Hkv, w);
+    const int32_t L = p.seq_lens[pc.b];
+    const KeyRange kr = key_range(L, p.q_len, p.window);
+    const int32_t first = kr.blk_lo + pc.first;
+    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, pc.b, pc.g, L, kr, first, first + pc.count - 1,
+                                         pc.k > 1 ? (int64_t)w : -1);
+    return;
+  }
+  // Flattened-list partition: this workgroup's slice of the flattened (unit, block)
   // list, cut at unit boundaries into segments. A segment holding a whole
   // unit writes the output directly; the others leave a partial in slot
   // (workgroup + unit), which is unique because both indices only grow
   // along the list.
-  __shared__ int32_t pre[kMaxBalancedSeqs + 1];
   block_prefix(p, pre);
   __syncthreads();
   if (blockIdx.x == 0 && p.ws_prefix)

@@ -98,9 +98,13 @@ pa_valu_kernel(const Params p) {
     row_hi[r] = r < p.rows ? kr.p0 + t : -1;
   }
 
-  const size_t tok_stride = (size_t)p.Hkv * ROW_BYTES;
-  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES + part * 16;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES + part * 16;
+  // A (block, KV head) tile: 16 rows of ROW_BYTES, tok_stride apart. Lane
+  // (tsub, part) reads 16 bytes at column part*16 (+ c*LPT*16) of rows tsub + TPI*u.
+  const int32_t tok_stride = p.Hkv * ROW_BYTES;
+  const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
+  const int32_t lane_off = tsub * tok_stride + part * 16;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
@@ -113,22 +117,35 @@ pa_valu_kernel(const Params p) {
   int32_t nmine = 0;
   int32_t tbl = 0;
 
+  // Block k of this wavefront (k >= nmine: a no-op load of zero bytes, so
+  // every path through the pipeline issues the same loads).
   auto fetch = [&](int32_t k, Tile& kr_, Tile& vr_) __attribute__((always_inline)) {
-    const int32_t phys = __builtin_amdgcn_readlane(tbl, k);
-    const size_t blk_off = (size_t)phys * kBlock * tok_stride;
+    const bool valid = k < nmine;
+    const int32_t phys = __builtin_amdgcn_readlane(tbl, valid ? k : 0);
+    const size_t tile = (size_t)phys * kBlock * (size_t)tok_stride;
+    const auto kd = buffer_rsrc(kpool + tile, valid ? tile_bytes : 0);
+    const auto vd = buffer_rsrc(vpool + tile, valid ? tile_bytes : 0);
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
-      for (int c = 0; c < COLS; ++c) kr_[u][c] = load16_stream(kbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+      for (int c = 0; c < COLS; ++c) kr_[u][c] = buffer_load16(kd, lane_off + c * LPT * 16, TPI * u * tok_stride);
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
-      for (int c = 0; c < COLS; ++c) vr_[u][c] = load16_stream(vbase + blk_off + (tsub + TPI * u) * tok_stride + c * LPT * 16);
+      for (int c = 0; c < COLS; ++c) vr_[u][c] = buffer_load16(vd, lane_off + c * LPT * 16, TPI * u * tok_stride);
+  };
+  auto keep = [&](const Tile& kr_, const Tile& vr_) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) {
+        keep_loaded(kr_[u][c]);
+        keep_loaded(vr_[u][c]);
+      }
   };
 
   auto consume = [&](int32_t k, const Tile& kr_, const Tile& vr_) __attribute__((always_inline)) {
     const int32_t i = cfirst + wave + NW * k;   // logical block
-    if (visits && lane == 0) atomicAdd(visits + i, 1);
 
     // q . k for every (row slot u, query row r), summed over the lanes sharing the row.
     float s[TPL][ROWS];
@@ -222,17 +239,26 @@ pa_valu_kernel(const Params p) {
     const int32_t clast = min(last, cfirst + 64 * NW - 1);
     nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
     tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
+    // Debug load counts, kept out of the pipelined loop below.
+    if (visits && lane < nmine) atomicAdd(visits + cfirst + wave + NW * lane, 1);
     if constexpr (PIPE) {
+      // Block k+1 is in flight while block k is consumed. The fetches are
+      // unconditional (past the end they load zero bytes), so every path into
+      // the loop head has the same loads outstanding and the compiler waits
+      // only for the block it consumes.
       Tile ka, va, kb, vb;
-      if (nmine > 0) fetch(0, ka, va);
+      fetch(0, ka, va);
       for (int32_t k = 0; k < nmine; k += 2) {
-        const bool has_b = k + 1 < nmine;
-        if (has_b) fetch(k + 1, kb, vb);
+        fetch(k + 1, kb, vb);
         consume(k, ka, va);
-        if (!has_b) break;
-        if (k + 2 < nmine) fetch(k + 2, ka, va);
+        if (k + 1 >= nmine) break;
+        __builtin_amdgcn_sched_barrier(0);   // refill a buffer only once it is consumed
+        fetch(k + 2, ka, va);
         consume(k + 1, kb, vb);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      keep(ka, va);
+      keep(kb, vb);
     } else {
       Tile ka, va;
       for (int32_t k = 0; k < nmine; ++k) {

@@ -46,6 +46,13 @@ class Dev:
         torch.cuda.synchronize()
         return out
 
+    def plan(self, **kw) -> dict:
+        x = self.x
+        kw.setdefault("window", x.window)
+        kw.setdefault("scale", x.scale)
+        kw.setdefault("max_seq_len", x.max_seq_len)
+        return pa.plan(self.q, self.k, self.v, self.table, self.lens, k_scale=self.ks, v_scale=self.vs, **kw)
+
     def run_f64(self, **kw) -> np.ndarray:
         return self.run(**kw).float().cpu().numpy().astype(np.float64)
 

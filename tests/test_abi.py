@@ -131,12 +131,14 @@ def test_plan_choices(lib):
     # Global layer: 16 query heads on one KV head go to the matrix cores.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768,
                                           max_blocks_per_seq=2048)), ctypes.byref(info)) == 0
-    assert info.kernel == 1 and info.rows == 16 and info.balanced == 1
+    # Few long units: each workgroup owns one piece of one unit.
+    assert info.kernel == 1 and info.rows == 16 and info.balanced == 2 and info.waves_per_group == 4
     # Verify step: 4 heads x 5 tokens = 20 rows.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
                                           window=0, max_seq_len=16384, max_blocks_per_seq=1024)),
                        ctypes.byref(info)) == 0
-    assert info.kernel == 1 and info.rows == 20
+    # Many units (256 sequences x 8 KV heads): slices of the flattened list.
+    assert info.kernel == 1 and info.rows == 20 and info.balanced == 1
     # A forced split count is honoured (capped by the blocks a sequence can span).
     assert lib.pa_plan(ctypes.byref(_args(num_splits=3)), ctypes.byref(info)) == 0
     assert info.splits == 3

@@ -122,6 +122,42 @@ def test_small_problems(case, splits):
     assert max_err(got, ref) <= TOL[kvd]
 
 
+# --- the matrix-core kernel's three partitions ----------------------------------------------------
+# Pieces (one run of one unit per workgroup), slices of the flattened list (a
+# workgroup may span several units) and aligned splits must each match the
+# oracle; PA_PIECES / PA_BALANCED switch the library's choice off.
+
+PARTITION_CASES = [
+    ([300, 1000, 47], 1, 16, 1, 256, 0, "bf16", "bf16", True),
+    ([4096, 2000, 77, 16, 1], 1, 16, 2, 128, 0, "bf16", "bf16", False),
+    ([1500, 600, 3000], 1, 64, 8, 128, 0, "bf16", "int8", False),
+    ([700, 90, 2048], 5, 32, 8, 128, 40, "bf16", "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", PARTITION_CASES, ids=_ids)
+@pytest.mark.parametrize("mode", ["pieces", "list", "aligned"])
+def test_mfma_partitions(case, mode, monkeypatch):
+    if mode != "pieces":
+        monkeypatch.setenv("PA_PIECES", "0")
+    if mode == "aligned":
+        monkeypatch.setenv("PA_BALANCED", "0")
+    lens, q_len, Hq, Hkv, D, window, qd, kvd, alias = case
+    x = make_inputs(lens, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=qd, kv_dtype=kvd,
+                    window=window, alias_v=alias, poison=True, seed=zlib.crc32(repr((case, mode)).encode()))
+    _log(f"partition {mode} {_ids(case)}")
+    dev = Dev(x)
+    plan = dev.plan()
+    assert plan["kernel"] == 1 and plan["balanced"] == {"pieces": 2, "list": 1, "aligned": 0}[mode]
+    got = dev.run_f64()
+    assert not np.isnan(got).any()
+    assert max_err(got, _oracle(x)) <= TOL[kvd]
+    visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
+    dev.run(debug_visits=visits)
+    expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
+    np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
+
+
 # --- invariants on the GPU path -------------------------------------------------------------------
 
 def test_block_permutation_is_bit_identical():
