@@ -136,7 +136,10 @@ int make_plan(const pa_args* a, Plan* pl) {
 
   // Tuning knobs for experiments: waves per workgroup (4 or 8), blocks per wave.
   int bpw_force = 0;
-  if (const char* e = getenv("PA_WAVES")) { const int v = atoi(e); if (v == 4 || v == 8) P.nw = v; }
+  if (const char* e = getenv("PA_WAVES")) {
+    const int v = atoi(e);
+    if (v == 4 || v == 8 || (P.kernel == 1 && (v == 1 || v == 2))) P.nw = v;
+  }
   if (const char* e = getenv("PA_BLOCKS_PER_WAVE")) bpw_force = atoi(e);
 
   const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
@@ -172,11 +175,12 @@ int make_plan(const pa_args* a, Plan* pl) {
   // units (partition 1). Forced splits, the vector kernel and very large
   // batches keep the aligned splits. PA_BALANCED=0 / PA_PIECES=0 turn the
   // balanced partitions / the piece partition off (for tests and experiments).
-  bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= pa::kMaxBalancedSeqs;
+  bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= pa::balanced_seq_limit(P.nw);
   if (const char* e = getenv("PA_BALANCED")) balanced = balanced && atoi(e) != 0;
   if (balanced) {
     P.nwg = cu_count() * (8 / P.nw);
-    bool pieces = 2 * units <= P.nwg && a->num_seqs <= pa::kMaxPieceSeqs;
+    if (const char* e = getenv("PA_OVERSUB")) { const int v = atoi(e); if (v >= 1 && v <= 64) P.nwg *= v; }
+    bool pieces = 2 * units <= P.nwg && a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4;
     if (const char* e = getenv("PA_PIECES")) pieces = pieces && atoi(e) != 0;
     P.balanced = pieces ? 2 : 1;
     P.grid = P.nwg;

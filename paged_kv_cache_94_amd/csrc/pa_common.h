@@ -72,6 +72,9 @@ __device__ __forceinline__ void merge_and_store(const Params& p, const float* ld
 namespace pa {
 // Batch limits of the balanced partitions (their per-sequence tables live in LDS).
 constexpr int kMaxBalancedSeqs = 4096;   // flattened-list partition: block prefix sums
+// Workgroups of one or two wavefronts run four to eight to a compute unit, so
+// their LDS share is smaller: their prefix table holds fewer sequences.
+constexpr int balanced_seq_limit(int nw) { return nw >= 4 ? kMaxBalancedSeqs : 1024; }
 constexpr int kMaxPieceSeqs = 512;       // piece partition: blocks per sequence
 
 struct LaunchShape {

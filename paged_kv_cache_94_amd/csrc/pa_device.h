@@ -122,6 +122,38 @@ __device__ __forceinline__ int32_t balanced_seq(const int32_t* pre, int32_t B, i
   return lo;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: shifts by
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of a row
+// is broadcast into the rows after it (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3). A lane whose source falls outside its
+// row, or whose row is masked off, adds 0. Every step is a VALU operation;
+// nothing goes through LDS.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int32_t dpp_i32(int32_t x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ int32_t wave_scan_incl(int32_t x) {
+  x += dpp_i32<0x111>(x);          // row_shr:1
+  x += dpp_i32<0x112>(x);          // row_shr:2
+  x += dpp_i32<0x114>(x);          // row_shr:4
+  x += dpp_i32<0x118>(x);          // row_shr:8
+  x += dpp_i32<0x142, 0xA>(x);     // row_bcast:15
+  x += dpp_i32<0x143, 0xC>(x);     // row_bcast:31
+  return x;
+}
+// Sum over the wavefront, the same value in every lane.
+__device__ __forceinline__ int32_t wave_sum(int32_t x) {
+  return __builtin_amdgcn_readlane(wave_scan_incl(x), 63);
+}
+// 64-bit sum of per-lane 32-bit values: the low and high 16-bit halves are
+// summed separately (each total stays below 2^22 for 64 lanes).
+__device__ __forceinline__ int64_t wave_sum_wide(int32_t x) {
+  const uint32_t u = (uint32_t)x;
+  const int64_t lo = wave_sum((int32_t)(u & 0xFFFFu));
+  const int64_t hi = wave_sum((int32_t)(u >> 16));
+  return lo + (hi << 16);
+}
+
 // pre[0..B] = prefix sums of seq_blocks over the batch, computed by wave 0
 // of the workgroup (64 sequences per step, DPP/ds_bpermute scan); the caller
 // synchronises the workgroup before reading pre.
@@ -133,14 +165,9 @@ __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre) {
   int32_t carry = 0;
   for (int32_t base = 0; base < p.B; base += 64) {
     const int32_t b = base + lane;
-    int32_t v = b < p.B ? seq_blocks(p.seq_lens[b], p) : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t t = __shfl_up(v, off);
-      if (lane >= off) v += t;
-    }
+    const int32_t v = wave_scan_incl(b < p.B ? seq_blocks(p.seq_lens[b], p) : 0);
     if (b < p.B) pre[b + 1] = carry + v;
-    carry += __shfl(v, 63);
+    carry += __builtin_amdgcn_readlane(v, 63);
   }
 }
 
@@ -161,21 +188,19 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   int64_t total = 0;
-  for (int32_t b = lane; b < p.B; b += 64) {
-    const int32_t nb = seq_blocks(p.seq_lens[b], p);
-    nbs[b] = nb;
-    total += nb;
+  for (int32_t base = 0; base < p.B; base += 64) {
+    const int32_t b = base + lane;
+    const int32_t nb = b < p.B ? seq_blocks(p.seq_lens[b], p) : 0;
+    if (b < p.B) nbs[b] = nb;
+    total += wave_sum_wide(nb);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
   total *= p.Hkv;
   // Pieces needed with at most `per` blocks each: sum over units of ceil(n / per).
+  // B <= kMaxPieceSeqs keeps the count far below 2^31.
   auto pieces = [&](int32_t per) {
     int32_t c = 0;
     for (int32_t b = lane; b < p.B; b += 64) c += (nbs[b] + per - 1) / per;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-    return (int64_t)c * p.Hkv;
+    return (int64_t)wave_sum(c) * p.Hkv;
   };
   // pieces(per) <= total / per + B*Hkv, so per_hi = ceil(total / (nwg - B*Hkv)) always fits.
   const int64_t spare = (int64_t)p.nwg - (int64_t)p.B * p.Hkv;
@@ -193,14 +218,9 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
   int32_t carry = 0;
   for (int32_t base = 0; base < p.B; base += 64) {
     const int32_t b = base + lane;
-    int32_t v = b < p.B ? (nbs[b] + per - 1) / per * p.Hkv : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t t = __shfl_up(v, off);
-      if (lane >= off) v += t;
-    }
+    const int32_t v = wave_scan_incl(b < p.B ? (nbs[b] + per - 1) / per * p.Hkv : 0);
     if (b < p.B) kp[b + 1] = carry + v;
-    carry += __shfl(v, 63);
+    carry += __builtin_amdgcn_readlane(v, 63);
   }
 }
 
@@ -336,8 +356,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 constexpr int kCacheNonTemporal = 2;   // buffer cache policy: NT (data read once)
 
 // voff: per-lane byte offset; soff: wave-uniform byte offset (a scalar register).
+template <int CPOL = kCacheNonTemporal>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff = 0) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCacheNonTemporal);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CPOL);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int32_t off) {

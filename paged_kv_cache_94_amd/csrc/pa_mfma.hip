@@ -7,19 +7,25 @@
 // the vector ALU in fp32.
 //
 // Layouts (lane l of the 64-lane wavefront; n = l & 15, q4 = l >> 4):
+//  * Loads run along the cached rows: each group of D*e/16 lanes reads one
+//    row of the (block, KV head) tile front to back in 16-byte pieces, so
+//    every quad of lanes touches one cache line. (Reading the tile directly
+//    in MFMA operand order -- 16 rows per instruction, 64 bytes each -- was
+//    measured 15-40% slower on the same addresses.) Each wavefront writes
+//    the block into its own LDS staging area as bf16 [16 tokens][D], rows
+//    2D+32 bytes apart, and reads the operands back from there.
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_16x16x32_bf16 over D/32 chunks. The A operand is the K tile
-//    exactly as loaded from HBM (lane l: token n, 8 consecutive dims of the
-//    chunk); the B operand is Q^T, held in registers for the whole kernel.
-//    The result gives lane l query row n and tokens 4*q4 .. 4*q4+3 -- the
-//    B-operand layout P^T needs for the PV product, and the row is
-//    lane-local, so the softmax needs lane exchanges only for the max over
-//    the four lanes sharing a row.
-//  * V must be read with tokens along the contraction depth. Each wavefront
-//    stages its V tile row-major in its own LDS slice and reads it back with
-//    ds_read_b64_tr_b16: in each 16-lane group, lanes 4k..4k+3 address row k
-//    (token 4*q4+k, 16 consecutive dims) and lane i receives element i of
-//    the four rows -- the A operand of O^T = V^T P^T for 16 dims.
+//    v_mfma_f32_16x16x32_bf16 over D/32 chunks. The A operand is read from
+//    the staged K tile (lane l: token n, dims 32c + 8*q4 .. +7, one 16-byte
+//    LDS read per chunk); the B operand is Q^T, held in registers for the
+//    whole segment. The result gives lane l query row n and tokens
+//    4*q4 .. 4*q4+3 -- the B-operand layout P^T needs for the PV product,
+//    and the row is lane-local, so the softmax needs lane exchanges only for
+//    the max over the four lanes sharing a row.
+//  * V is read with tokens along the contraction depth by ds_read_b64_tr_b16:
+//    in each 16-lane group, lanes 4k..4k+3 address row k (token 4*q4+k, 16
+//    consecutive dims) and lane i receives element i of the four rows -- the
+//    A operand of O^T = V^T P^T for 16 dims.
 //  * P is split into bf16 hi and lo parts; O^T += V^T [P_hi; P_lo] is one
 //    v_mfma_f32_16x16x32_bf16 whose 32-deep contraction holds both parts
 //    against the V^T slice read twice, so the weights keep ~16 bits while V
@@ -27,30 +33,28 @@
 //  * O^T accumulates in fp32: lane l ends with query row n and, per 16-dim
 //    tile j, dims 16j + 4*q4 .. +3.
 //  * int8 caches (tiniestgpt notes, KV cache quantization): codes are
-//    gathered first, widened to bf16 (exact for |code| <= 127), the key scale
-//    multiplies the score of its token and the value scale is folded into P.
+//    gathered first and widened to bf16 while staging (exact for
+//    |code| <= 127); the key scale multiplies the score of its token and the
+//    value scale is folded into P. Each block's 16 key and 16 value scales
+//    come in with one load each and pass through the staging area.
 //  * When v_pool == k_pool (Gemma4 global layer, shared W_K / W_V) the tile
-//    is read from HBM once and serves as both K and V.
+//    is read from HBM once and staged once; it serves as both K and V.
 #include "pa_common.h"
 
 namespace pa {
 
 namespace {
 
-// dim held by lane-group q4, element e (0..7) of 32-wide contraction chunk c.
-template <bool INT8>
-__device__ __forceinline__ int chunk_dim(int c, int q4, int e) {
-  if constexpr (INT8) {
-    return 64 * (c >> 1) + 16 * q4 + 8 * (c & 1) + e;   // 16-byte loads carry 16 dims
-  } else {
-    return 32 * c + 8 * q4 + e;                         // 16-byte loads carry 8 dims
-  }
-}
-
 __device__ __forceinline__ uint32_t i8pair_to_bf16(uint32_t w, int byte0) {
   const float a = (float)(int32_t)(int8_t)(w >> (8 * byte0));
   const float b = (float)(int32_t)(int8_t)(w >> (8 * byte0 + 8));
   return pack_bf16(a, b);
+}
+
+// 16 int8 codes widened to 16 bf16 values (exact for |code| <= 127), in order.
+__device__ __forceinline__ void i8x16_to_bf16(const uint4& w, uint4& lo, uint4& hi) {
+  lo = make_uint4(i8pair_to_bf16(w.x, 0), i8pair_to_bf16(w.x, 2), i8pair_to_bf16(w.y, 0), i8pair_to_bf16(w.y, 2));
+  hi = make_uint4(i8pair_to_bf16(w.z, 0), i8pair_to_bf16(w.z, 2), i8pair_to_bf16(w.w, 0), i8pair_to_bf16(w.w, 2));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -65,17 +69,36 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
 
 }  // namespace
 
-template <int D, int MT, int NW>
+template <int D, int MT, int NW, bool ALIAS>
 struct MfmaLds {
   static constexpr int ROWS = 16 * MT;
-  static constexpr int VSTRIDE = D * 2 + 32;                 // bytes per staged V row (32-byte skew against bank conflicts)
-  static constexpr int STAGE = NW * 16 * VSTRIDE;            // one V tile per wavefront
-  // Merge: waves 1..NW-1 park o [ROWS][D] (row stride D + 4 floats: the 16
-  // rows a 16-lane group writes start in 16 different 4-bank groups) and (m, l).
-  static constexpr int MSTRIDE = D + 4;
-  static constexpr int MERGE = (NW - 1) * ROWS * (MSTRIDE + 2) * 4;
+  static constexpr int TJ = D / 16;                          // 16-dim output tiles per row tile
+  // Staging, per wavefront: the block's K tile and (unless V aliases K) its
+  // V tile as bf16 [16 tokens][D], rows RSTRIDE bytes apart (a 32-byte skew
+  // keeps both the row-wise K reads and the transposed V reads free of bank
+  // conflicts), then 32 floats for the int8 scales of the block.
+  static constexpr int RSTRIDE = D * 2 + 32;
+  static constexpr int TILE = 16 * RSTRIDE;
+  static constexpr int WAVE_STAGE = TILE * (ALIAS ? 1 : 2) + 128;
+  static constexpr int STAGE = NW * WAVE_STAGE;
+  // Merge: output tile j belongs to wave j % NW. Every wave parks the tiles
+  // it does not own, [MT][TJ][NW-1 slots][64 lanes] float4 (1 KiB per tile,
+  // lane-ordered, so writes and reads are conflict-free), and its (m, l)
+  // per lane, [NW][MT][64] float2.
+  static constexpr int O_BYTES = MT * TJ * (NW - 1) * 1024;
+  static constexpr int MERGE = O_BYTES + NW * MT * 64 * 8;
   static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
 };
+
+// Blocks a wavefront keeps in flight: as many as fit a register budget for
+// the fetch buffers (FETCH_WORDS 32-bit registers per block), at most 4.
+#ifndef PA_FETCH_BUDGET
+#define PA_FETCH_BUDGET 64
+#endif
+constexpr int mfma_depth(int fetch_words) {
+  const int d = PA_FETCH_BUDGET / fetch_words;
+  return d < 1 ? 1 : (d > 4 ? 4 : d);
+}
 
 // Attention of query rows (b, g) over logical blocks [first, last] of sequence
 // b. slot < 0: write the normalised output; else write (m, l, o) to
@@ -83,14 +106,22 @@ struct MfmaLds {
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
 __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t L,
                                              const KeyRange& kr, int32_t first, int32_t last, int64_t slot) {
-  using Lds = MfmaLds<D, MT, NW>;
+  using Lds = MfmaLds<D, MT, NW, ALIAS>;
   constexpr int ROWS = Lds::ROWS;
   constexpr int C = D / 32;                           // contraction chunks of 32 dims
   constexpr int TJ = D / 16;                          // 16-dim output tiles
   constexpr int EB = INT8 ? 1 : 2;
   constexpr int ROW_BYTES = D * EB;
-  constexpr int NLOAD = ROW_BYTES / 64;               // 16-byte loads per lane per tile
-  static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
+  // Tile loads run along the rows: LPR lanes cover one cached row with
+  // 16-byte pieces, RPI rows per load instruction, NLOAD instructions per tile.
+  constexpr int LPR = ROW_BYTES / 16;
+  constexpr int RPI = 64 / LPR;
+  constexpr int NLOAD = kBlock / RPI;
+  // Rows of 256 bytes or more are read with the non-temporal hint; shorter
+  // rows measured faster through the normal cache policy.
+  constexpr int CPOL = ROW_BYTES >= 256 ? kCacheNonTemporal : 0;
+  constexpr int RS = Lds::RSTRIDE;
+  static_assert(D % 64 == 0 && LPR >= 4 && LPR <= 64, "head_dim must be 64, 128 or 256");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: block indices stay scalar
@@ -111,7 +142,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (live) v = load16(qrow + chunk_dim<INT8>(c, q4, 0) * 2);
+      if (live) v = load16(qrow + (32 * c + 8 * q4) * 2);
       qt[tile][c] = __builtin_bit_cast(bf16x8, v);
     }
     row_lo[tile] = first_key(kr.p0, t, p.window);
@@ -128,27 +159,35 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     for (int j = 0; j < TJ; ++j) o[tile][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // A (block, KV head) tile: 16 rows of ROW_BYTES, tok_stride apart. Lane l
-  // reads row n at byte offsets 16*q4 + 64*u of it.
+  // A (block, KV head) tile: 16 rows of ROW_BYTES, tok_stride apart. Load
+  // instruction u gives lane l row u*RPI + l/LPR, bytes 16*(l%LPR) .. +15:
+  // every group of LPR lanes reads one row front to back.
   const int32_t tok_stride = p.Hkv * ROW_BYTES;
   const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
-  const int32_t lane_off = n * tok_stride + 16 * q4;
+  const int ld_row = lane / LPR;                      // + u*RPI
+  const int ld_chunk = lane % LPR;                    // 16-byte piece of the row
+  const int32_t lane_off = ld_row * tok_stride + 16 * ld_chunk;
   const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
   const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
-  // This wavefront's V staging tile, [16 tokens][D dims] bf16, row stride VSTRIDE,
-  // and its transposed-read address for 16-dim tile 0: row 4*q4 + (n>>2), dims 4*(n&3).
-  char* vstage = smem + wave * 16 * Lds::VSTRIDE;
-  const char* vread = vstage + (4 * q4 + (n >> 2)) * Lds::VSTRIDE + 8 * (n & 3);
+  // This wavefront's staging area (bf16 K tile, V tile unless aliased, scales).
+  // MFMA operands are read back from it: K as the A operand of S^T = K Q^T
+  // (lane l: token n, dims 32c + 8*q4 .. +7, one 16-byte read), V transposed
+  // with ds_read_b64_tr_b16 (lane l: row 4*q4 + (n>>2), dims 16j + 4*(n&3)).
+  char* kst = smem + wave * Lds::WAVE_STAGE;
+  char* vst = ALIAS ? kst : kst + Lds::TILE;
+  float* sst = reinterpret_cast<float*>(kst + Lds::TILE * (ALIAS ? 1 : 2));
+  const char* kread = kst + n * RS + 16 * q4;
+  const char* vread = vst + (4 * q4 + (n >> 2)) * RS + 8 * (n & 3);
 
-  // One 16-token block as loaded: this lane's token row (n) of K (and V), plus
-  // the four per-token scales of its score rows for int8 caches.
+  // One 16-token block as loaded: NLOAD 16-byte pieces of K (and V) rows, and
+  // for int8 caches the scale of token l & 15 (K and V).
   struct Fetched {
     uint4 k[NLOAD];
     uint4 v[ALIAS ? 1 : NLOAD];
-    float ks[INT8 ? 4 : 1], vs[INT8 ? 4 : 1];
+    float ks, vs;
   };
   // The k-th block of this wavefront is first + wave + NW*k; lane k holds its
   // physical id (one coalesced read up front, then v_readlane per block, so no
@@ -167,11 +206,8 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       for (int u = 0; u < NLOAD; ++u) keep_loaded(f.v[u]);
     }
     if constexpr (INT8) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        keep_loaded(f.ks[e]);
-        keep_loaded(f.vs[e]);
-      }
+      keep_loaded(f.ks);
+      keep_loaded(f.vs);
     }
   };
 
@@ -181,49 +217,48 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     const size_t tile = (size_t)phys * kBlock * (size_t)tok_stride;
     const auto kd = buffer_rsrc(kpool + tile, valid ? tile_bytes : 0);
 #pragma unroll
-    for (int u = 0; u < NLOAD; ++u) f.k[u] = buffer_load16(kd, lane_off + 64 * u);
+    for (int u = 0; u < NLOAD; ++u) f.k[u] = buffer_load16<CPOL>(kd, lane_off, u * RPI * tok_stride);
     if constexpr (!ALIAS) {
       const auto vd = buffer_rsrc(vpool + tile, valid ? tile_bytes : 0);
 #pragma unroll
-      for (int u = 0; u < NLOAD; ++u) f.v[u] = buffer_load16(vd, lane_off + 64 * u);
+      for (int u = 0; u < NLOAD; ++u) f.v[u] = buffer_load16<CPOL>(vd, lane_off, u * RPI * tok_stride);
     }
     if constexpr (INT8) {
-      // Scales of tokens 4*q4 .. 4*q4+3 (the score rows of this lane), Hkv floats apart.
+      // Scales of the block's 16 tokens for this KV head, Hkv floats apart.
       const size_t s0 = (size_t)phys * kBlock * p.Hkv + g;
       const int32_t sbytes = valid ? ((kBlock - 1) * p.Hkv + 1) * 4 : 0;
-      const auto ksd = buffer_rsrc(p.k_scale + s0, sbytes);
-      const auto vsd = buffer_rsrc(p.v_scale + s0, sbytes);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f.ks[e] = buffer_load_f32(ksd, (4 * q4 + e) * p.Hkv * 4);
-        f.vs[e] = buffer_load_f32(vsd, (4 * q4 + e) * p.Hkv * 4);
-      }
+      f.ks = buffer_load_f32(buffer_rsrc(p.k_scale + s0, sbytes), (lane & 15) * p.Hkv * 4);
+      f.vs = buffer_load_f32(buffer_rsrc(p.v_scale + s0, sbytes), (lane & 15) * p.Hkv * 4);
     }
   };
 
-  // Chunk c of the K tile as a bf16x8 MFMA operand (int8 codes widened, exact).
-  auto k_operand = [&](const Fetched& f, int c) __attribute__((always_inline)) -> bf16x8 {
+  // Write one loaded piece (row r, 16 bytes at byte 16*ld_chunk of the cached
+  // row) into a staging tile as bf16; int8 codes widen to 32 bytes.
+  auto stage = [&](char* dst_tile, int r, const uint4& w) __attribute__((always_inline)) {
     if constexpr (INT8) {
-      const uint4 w = f.k[c >> 1];
-      const uint32_t w0 = (c & 1) ? w.z : w.x, w1 = (c & 1) ? w.w : w.y;
-      return __builtin_bit_cast(bf16x8, make_uint4(i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 2),
-                                                   i8pair_to_bf16(w1, 0), i8pair_to_bf16(w1, 2)));
+      uint4 lo, hi;
+      i8x16_to_bf16(w, lo, hi);
+      char* dst = dst_tile + r * RS + 32 * ld_chunk;
+      *reinterpret_cast<uint4*>(dst) = lo;
+      *reinterpret_cast<uint4*>(dst + 16) = hi;
     } else {
-      return __builtin_bit_cast(bf16x8, f.k[c]);
+      *reinterpret_cast<uint4*>(dst_tile + r * RS + 16 * ld_chunk) = w;
     }
   };
 
   auto consume = [&](int32_t k, const Fetched& f) __attribute__((always_inline)) {
     const int32_t i = cfirst + wave + NW * k;   // logical block
 
-    // Stage this lane's V row (token n) in LDS as bf16. A row nobody may see
-    // can hold anything and is written as zeros (only edge blocks have such rows).
+    // Stage the block in LDS as bf16. A V row nobody may see can hold
+    // anything and is written as zeros (only edge blocks have such rows); a K
+    // row's score is masked by select, so its contents do not matter.
     const bool edge = i * kBlock < kr.lo0 || i * kBlock + kBlock > L;
-    const int32_t jv = i * kBlock + n;
-    const bool v_ok = !edge || (jv < L && jv >= kr.lo0);
-    __builtin_amdgcn_wave_barrier();   // the previous block's transposed reads stay before these writes
+    __builtin_amdgcn_wave_barrier();   // the previous block's reads stay before these writes
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) {
+      const int r = ld_row + u * RPI;
+      const int32_t jv = i * kBlock + r;
+      const bool v_ok = !edge || (jv < L && jv >= kr.lo0);
       uint4 w = ALIAS ? f.k[u] : f.v[ALIAS ? 0 : u];
       if (edge) {
         w.x = v_ok ? w.x : 0u;
@@ -231,19 +266,25 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
         w.z = v_ok ? w.z : 0u;
         w.w = v_ok ? w.w : 0u;
       }
-      if constexpr (INT8) {
-        // 16 codes: dims 64u + 16*q4 .. +15
-        char* dst = vstage + n * Lds::VSTRIDE + (64 * u + 16 * q4) * 2;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(i8pair_to_bf16(w.x, 0), i8pair_to_bf16(w.x, 2),
-                                                    i8pair_to_bf16(w.y, 0), i8pair_to_bf16(w.y, 2));
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(i8pair_to_bf16(w.z, 0), i8pair_to_bf16(w.z, 2),
-                                                         i8pair_to_bf16(w.w, 0), i8pair_to_bf16(w.w, 2));
-      } else {
-        // 8 bf16: dims 32u + 8*q4 .. +7
-        *reinterpret_cast<uint4*>(vstage + n * Lds::VSTRIDE + (32 * u + 8 * q4) * 2) = w;
-      }
+      stage(vst, r, w);
+      if constexpr (!ALIAS) stage(kst, r, f.k[u]);
     }
-    __builtin_amdgcn_wave_barrier();   // these writes stay before this block's transposed reads
+    if constexpr (INT8) {
+      if (lane < 32) sst[lane] = lane < 16 ? f.ks : f.vs;
+    }
+    __builtin_amdgcn_wave_barrier();   // these writes stay before this block's reads
+
+    // K operand chunks: token n, dims 32c + 8*q4 .. +7.
+    bf16x8 kop[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kread + 64 * c));
+    float ksc[4], vsc[4];
+    if constexpr (INT8) {
+      const float4 a = *reinterpret_cast<const float4*>(sst + 4 * q4);
+      const float4 v = *reinterpret_cast<const float4*>(sst + 16 + 4 * q4);
+      ksc[0] = a.x; ksc[1] = a.y; ksc[2] = a.z; ksc[3] = a.w;
+      vsc[0] = v.x; vsc[1] = v.y; vsc[2] = v.z; vsc[3] = v.w;
+    }
 
     // Scores and softmax for every row tile; P leaves as hi/lo bf16 parts.
     bf16x8 pbv[MT];
@@ -251,7 +292,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     for (int tile = 0; tile < MT; ++tile) {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < C; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(f, c), qt[tile][c], s, 0, 0, 0);
+      for (int c = 0; c < C; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c], qt[tile][c], s, 0, 0, 0);
 
       // s[e] = score of query row n (+16*tile) against token 4*q4+e of block i.
       float sc[4];
@@ -261,7 +302,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
         const int32_t j = i * kBlock + 4 * q4 + e;
         const bool ok = j <= row_hi[tile] && j >= row_lo[tile];
         float x = s[e] * p.scale_log2;
-        if constexpr (INT8) x *= f.ks[e];
+        if constexpr (INT8) x *= ksc[e];
         sc[e] = ok ? x : -INFINITY;
         mb = fmaxf(mb, sc[e]);
       }
@@ -284,7 +325,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
         if constexpr (INT8) {
           const int32_t j = i * kBlock + 4 * q4 + e;
           const bool vis = j < L && j >= kr.lo0;
-          pe[e] *= vis ? f.vs[e] : 0.f;
+          pe[e] *= vis ? vsc[e] : 0.f;
         }
       }
       // P as hi + lo bf16 parts for the 32-deep PV contraction.
@@ -307,91 +348,99 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     }
   };
 
-  // Two-deep software pipeline (block k+1 in flight while block k is consumed)
-  // when both fetch buffers fit beside the accumulators; else one buffer.
-  constexpr int FETCH_WORDS = NLOAD * 4 * (ALIAS ? 1 : 2) + (INT8 ? 8 : 0);
-  constexpr bool PIPE = MT == 1 && 2 * FETCH_WORDS <= 64;
+  // Software pipeline: DEPTH blocks in flight per wavefront; block k+DEPTH-1
+  // is requested before block k is consumed. The fetches are unconditional
+  // (past the end they load zero bytes), so every path into the loop head
+  // has the same loads outstanding and the compiler waits only for the
+  // block it consumes.
+  constexpr int FETCH_WORDS = NLOAD * 4 * (ALIAS ? 1 : 2) + (INT8 ? 2 : 0);
+  constexpr int DEPTH = mfma_depth(FETCH_WORDS);
   for (; cfirst <= last; cfirst += 64 * NW) {
     const int32_t clast = min(last, cfirst + 64 * NW - 1);
     nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
     tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
     // Debug load counts, kept out of the pipelined loop below.
     if (visits && lane < nmine) atomicAdd(visits + cfirst + wave + NW * lane, 1);
-    if constexpr (PIPE) {
-      // Block k+1 is in flight while block k is consumed. The loop body has no
-      // exit and its fetches are unconditional (past the end they load zero
-      // bytes), so every path into its head has the same loads outstanding
-      // and the compiler waits only for the block it consumes.
-      Fetched fa, fb;
-      fetch(0, fa);
-      const int32_t pairs = nmine >> 1;
-      for (int32_t k = 0; k < 2 * pairs; k += 2) {
-        fetch(k + 1, fb);
-        consume(k, fa);
+    if (nmine == 0) continue;
+    Fetched f[DEPTH];
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
+    for (int32_t k = 0;; k += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        fetch(k + d + DEPTH - 1, f[(d + DEPTH - 1) % DEPTH]);
+        consume(k + d, f[d]);
+        if (k + d + 1 >= nmine) goto drained;
         __builtin_amdgcn_sched_barrier(0);   // refill a buffer only once it is consumed
-        fetch(k + 2, fa);
-        consume(k + 1, fb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (nmine & 1) consume(nmine - 1, fa);
-      keep(fa);
-    } else {
-      Fetched fa;
-      for (int32_t k = 0; k < nmine; ++k) {
-        fetch(k, fa);
-        consume(k, fa);
       }
     }
+  drained:
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) keep(f[d]);
   }
 
   // Row sums: the four lanes of a row each hold a quarter of the tokens.
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) l[tile] = quads16_sum(l[tile]);
 
-  // Merge the wavefronts through LDS (reusing the staging area): waves
-  // 1..NW-1 park (m, l, o), wave 0 folds them in with the online-softmax rule.
-  constexpr int MS = Lds::MSTRIDE;
-  float* lds_acc = reinterpret_cast<float*>(smem);
-  float* lds_ml = lds_acc + (NW - 1) * ROWS * MS;
+  // Merge the wavefronts through LDS (reusing the staging area). Output
+  // tile j (dims 16j..16j+15) belongs to wave j % NW: every wave parks the
+  // tiles it does not own and its (m, l), then folds the other waves' copies
+  // of its own tiles into its registers with the online-softmax rule and
+  // writes them, so the fold and the stores are spread over all wavefronts.
+  // Lane l holds the same (row, dims) in every wave: the fold is per lane.
+  float4* lds_o = reinterpret_cast<float4*>(smem);
+  float2* lds_ml = reinterpret_cast<float2*>(smem + Lds::O_BYTES);
   __syncthreads();   // every wavefront is done with its staging tile
-  if (wave > 0) {
-    const int slot = wave - 1;
 #pragma unroll
-    for (int tile = 0; tile < MT; ++tile) {
-      const int r = n + 16 * tile;
+  for (int tile = 0; tile < MT; ++tile) {
+    lds_ml[(wave * MT + tile) * 64 + lane] = make_float2(m[tile], l[tile]);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        *reinterpret_cast<f32x4*>(lds_acc + (slot * ROWS + r) * MS + 16 * j + 4 * q4) = o[tile][j];
-      if (q4 == 0) {
-        lds_ml[(slot * ROWS + r) * 2] = m[tile];
-        lds_ml[(slot * ROWS + r) * 2 + 1] = l[tile];
-      }
+    for (int j = 0; j < TJ; ++j) {
+      const int owner = j % NW;
+      if (owner == wave) continue;
+      const int s = wave < owner ? wave : wave - 1;
+      const f32x4 v = o[tile][j];
+      lds_o[((tile * TJ + j) * (NW - 1) + s) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   __syncthreads();
-  if (wave != 0) return;
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
-    const int r = n + 16 * tile;
-    float M = m[tile];
+    float2 ml[NW];
+    float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < NW - 1; ++s) M = fmaxf(M, lds_ml[(s * ROWS + r) * 2]);
+    for (int w = 0; w < NW; ++w) {
+      ml[w] = lds_ml[(w * MT + tile) * 64 + lane];
+      M = fmaxf(M, ml[w].x);
+    }
     const float Ms = M == -INFINITY ? 0.f : M;
-    const float a0 = fast_exp2(m[tile] - Ms);
-    l[tile] *= a0;
+    float a[NW];
+    float L = 0.f;
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) o[tile][j] *= a0;
-#pragma unroll 1
-    for (int s = 0; s < NW - 1; ++s) {   // one slot at a time keeps the loads' registers bounded
-      const float a = fast_exp2(lds_ml[(s * ROWS + r) * 2] - Ms);
-      l[tile] += a * lds_ml[(s * ROWS + r) * 2 + 1];
+    for (int w = 0; w < NW; ++w) {
+      a[w] = fast_exp2(ml[w].x - Ms);   // 0 for a wave that saw no key of this row
+      L += a[w] * ml[w].y;
+    }
+    float aself = a[0];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        o[tile][j] += a * *reinterpret_cast<const f32x4*>(lds_acc + (s * ROWS + r) * MS + 16 * j + 4 * q4);
+    for (int w = 1; w < NW; ++w) aself = wave == w ? a[w] : aself;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      if (j % NW != wave) continue;
+      f32x4 acc = o[tile][j] * aself;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w == wave) continue;
+        const int s = w < wave ? w : w - 1;
+        const float4 x = lds_o[((tile * TJ + j) * (NW - 1) + s) * 64 + lane];
+        acc += a[w] * f32x4{x.x, x.y, x.z, x.w};
+      }
+      o[tile][j] = acc;
     }
     m[tile] = M;
+    l[tile] = L;
   }
-  if (wave != 0) return;
 
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
@@ -403,10 +452,11 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       const size_t row_slot = (size_t)slot * p.rows + r;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
+        if (j % NW != wave) continue;
         const f32x4 v = o[tile][j];
         *reinterpret_cast<float4*>(p.ws_acc + row_slot * D + 16 * j + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      if (q4 == 0) {
+      if (wave == 0 && q4 == 0) {
         p.ws_ml[row_slot * 2] = m[tile];
         p.ws_ml[row_slot * 2 + 1] = l[tile];
       }
@@ -415,6 +465,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       __bf16* out = reinterpret_cast<__bf16*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + 4 * q4;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
+        if (j % NW != wave) continue;
         const f32x4 v = o[tile][j];
         *reinterpret_cast<uint2*>(out + 16 * j) =
             make_uint2(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv));
@@ -427,7 +478,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 pa_mfma_kernel(const Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[MfmaLds<D, MT, NW>::BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[MfmaLds<D, MT, NW, ALIAS>::BYTES];
   if (!p.balanced) {
     // Aligned splits: workgroup (split, b, g) takes blocks [blk_lo + split*bps, ...] of sequence b.
     const int32_t g = blockIdx.x % p.Hkv;
@@ -444,7 +495,7 @@ pa_mfma_kernel(const Params p) {
     mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, L, kr, first, last, slot);
     return;
   }
-  __shared__ int32_t pre[kMaxBalancedSeqs + 1];
+  __shared__ int32_t pre[balanced_seq_limit(NW) + 1];
   if (p.balanced == 2) {
     // Piece partition: one run of one unit per workgroup; the slot of a
     // partial is the workgroup's own index.
@@ -498,6 +549,8 @@ template <bool INT8, bool ALIAS, int D, int MT>
 hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
   *ok = true;
   switch (nw) {
+    case 1: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 1>, grid, 64, st, tm, p);
+    case 2: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 2>, grid, 128, st, tm, p);
     case 4: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 4>, grid, 256, st, tm, p);
     case 8: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 8>, grid, 512, st, tm, p);
   }
