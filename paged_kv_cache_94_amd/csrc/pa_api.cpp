@@ -138,7 +138,7 @@ int make_plan(const pa_args* a, Plan* pl) {
   int bpw_force = 0;
   if (const char* e = getenv("PA_WAVES")) {
     const int v = atoi(e);
-    if (v == 4 || v == 8 || (P.kernel == 1 && (v == 1 || v == 2))) P.nw = v;
+    if (v == 4 || v == 8 || (P.kernel == 1 && v == 2)) P.nw = v;
   }
   if (const char* e = getenv("PA_BLOCKS_PER_WAVE")) bpw_force = atoi(e);
 

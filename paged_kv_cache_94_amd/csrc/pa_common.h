@@ -71,7 +71,7 @@ __device__ __forceinline__ void merge_and_store(const Params& p, const float* ld
 // Host-side launchers, one per kernel family (defined in the .hip files).
 namespace pa {
 // Batch limits of the balanced partitions (their per-sequence tables live in LDS).
-constexpr int kMaxBalancedSeqs = 4096;   // flattened-list partition: block prefix sums
+constexpr int kMaxBalancedSeqs = 2048;   // flattened-list partition: block prefix sums and first blocks
 // Workgroups of one or two wavefronts run four to eight to a compute unit, so
 // their LDS share is smaller: their prefix table holds fewer sequences.
 constexpr int balanced_seq_limit(int nw) { return nw >= 4 ? kMaxBalancedSeqs : 1024; }

@@ -154,19 +154,24 @@ __device__ __forceinline__ int64_t wave_sum_wide(int32_t x) {
   return lo + (hi << 16);
 }
 
-// pre[0..B] = prefix sums of seq_blocks over the batch, computed by wave 0
-// of the workgroup (64 sequences per step, DPP/ds_bpermute scan); the caller
-// synchronises the workgroup before reading pre.
+// pre[0..B] = prefix sums of seq_blocks over the batch and blo[0..B) = the
+// first logical block each sequence loads, computed by wave 0 of the
+// workgroup (64 sequences per step, DPP scan); the caller synchronises the
+// workgroup before reading them.
 template <typename P>
-__device__ __forceinline__ void block_prefix(const P& p, int32_t* pre) {
+__device__ __forceinline__ void block_prefix(const P& p, int32_t* pre, int32_t* blo) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   if (lane == 0) pre[0] = 0;
   int32_t carry = 0;
   for (int32_t base = 0; base < p.B; base += 64) {
     const int32_t b = base + lane;
-    const int32_t v = wave_scan_incl(b < p.B ? seq_blocks(p.seq_lens[b], p) : 0);
-    if (b < p.B) pre[b + 1] = carry + v;
+    const int32_t L = b < p.B ? p.seq_lens[b] : 0;
+    const int32_t v = wave_scan_incl(b < p.B ? seq_blocks(L, p) : 0);
+    if (b < p.B) {
+      pre[b + 1] = carry + v;
+      blo[b] = key_range(L, p.q_len, p.window).blk_lo;
+    }
     carry += __builtin_amdgcn_readlane(v, 63);
   }
 }

@@ -100,12 +100,27 @@ constexpr int mfma_depth(int fetch_words) {
   return d < 1 ? 1 : (d > 4 ? 4 : d);
 }
 
+// Physical ids of the first chunk of a wavefront's blocks in a segment:
+// lane j gets table[b][first + wave + NW*j]; lanes past the segment re-read
+// its last entry, so only table entries of loaded blocks are ever read.
+template <int NW>
+__device__ __forceinline__ int32_t chunk_table(const Params& p, int32_t b, int32_t cfirst, int32_t last) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int32_t idx = min(cfirst + wave + NW * lane, last);
+  return p.block_table[(size_t)b * p.maxb + idx];
+}
+
 // Attention of query rows (b, g) over logical blocks [first, last] of sequence
 // b. slot < 0: write the normalised output; else write (m, l, o) to
-// workspace slot `slot`. Called uniformly by every wavefront of the workgroup.
+// workspace slot `slot`. tbl0 = chunk_table(b, first, last), which the caller
+// may have loaded ahead. pf is a load the caller issued for a later segment:
+// it is waited for right after this segment's block loop, when nothing else
+// is in flight, so it reaches the caller as a settled value. Called uniformly
+// by every wavefront of the workgroup.
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
-__device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t L,
-                                             const KeyRange& kr, int32_t first, int32_t last, int64_t slot) {
+__device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t first,
+                                             int32_t last, int64_t slot, int32_t tbl0, int32_t& pf) {
   using Lds = MfmaLds<D, MT, NW, ALIAS>;
   constexpr int ROWS = Lds::ROWS;
   constexpr int C = D / 32;                           // contraction chunks of 32 dims
@@ -127,11 +142,17 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: block indices stay scalar
   const int n = lane & 15;
   const int q4 = lane >> 4;
-  __syncthreads();   // the previous segment's merge is done with the shared buffer
+  // Wait for the first chunk's table entries before issuing this segment's
+  // query loads: a prefetched chunk then waits on nothing newer than itself.
+  const int32_t tbl_first = settle(tbl0);
+  // The sequence's length comes in with the queries and the first blocks;
+  // only the masks need it.
+  const int32_t L = p.seq_lens[b];
+  KeyRange kr;                        // set once L has arrived (after the first loads are issued)
+  int32_t row_lo[MT], row_hi[MT];     // per-row visible keys: [row_lo, row_hi]
 
   // Q^T as the B operand: lane l holds query row n (+16 per tile), 8 dims per chunk.
   bf16x8 qt[MT][C];
-  int32_t row_lo[MT], row_hi[MT];
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
     const int r = n + 16 * tile;
@@ -145,8 +166,6 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       if (live) v = load16(qrow + (32 * c + 8 * q4) * 2);
       qt[tile][c] = __builtin_bit_cast(bf16x8, v);
     }
-    row_lo[tile] = first_key(kr.p0, t, p.window);
-    row_hi[tile] = live ? kr.p0 + t : -1;
   }
 
   f32x4 o[MT][TJ];
@@ -355,29 +374,56 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   // block it consumes.
   constexpr int FETCH_WORDS = NLOAD * 4 * (ALIAS ? 1 : 2) + (INT8 ? 2 : 0);
   constexpr int DEPTH = mfma_depth(FETCH_WORDS);
-  for (; cfirst <= last; cfirst += 64 * NW) {
+  // Blocks come in chunks of at most 64 per wavefront (one table entry per
+  // lane); the next chunk's entries are loaded while this one streams. The
+  // first chunk's loads are issued before the barrier that waits for the
+  // previous segment's merge to release the staging area, so they overlap it.
+  Fetched f[DEPTH];
+  auto chunk_size = [&]() __attribute__((always_inline)) {
     const int32_t clast = min(last, cfirst + 64 * NW - 1);
-    nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
-    tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
+    return clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
+  };
+  nmine = chunk_size();
+  tbl = tbl_first;
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
+  __syncthreads();
+  // Per-row visibility: row r (query t) sees keys [first_key(t), p0 + t].
+  kr = key_range(L, p.q_len, p.window);
+#pragma unroll
+  for (int tile = 0; tile < MT; ++tile) {
+    const int r = n + 16 * tile;
+    const bool live = r < p.rows;
+    const int t = live ? r / p.G : 0;
+    row_lo[tile] = first_key(kr.p0, t, p.window);
+    row_hi[tile] = live ? kr.p0 + t : -1;
+  }
+  while (true) {
+    const int32_t tbl_next = chunk_table<NW>(p, b, cfirst + 64 * NW, last);
     // Debug load counts, kept out of the pipelined loop below.
     if (visits && lane < nmine) atomicAdd(visits + cfirst + wave + NW * lane, 1);
-    if (nmine == 0) continue;
-    Fetched f[DEPTH];
+    if (nmine > 0) {
+      for (int32_t k = 0;; k += DEPTH) {
 #pragma unroll
-    for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
-    for (int32_t k = 0;; k += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        fetch(k + d + DEPTH - 1, f[(d + DEPTH - 1) % DEPTH]);
-        consume(k + d, f[d]);
-        if (k + d + 1 >= nmine) goto drained;
-        __builtin_amdgcn_sched_barrier(0);   // refill a buffer only once it is consumed
+        for (int d = 0; d < DEPTH; ++d) {
+          fetch(k + d + DEPTH - 1, f[(d + DEPTH - 1) % DEPTH]);
+          consume(k + d, f[d]);
+          if (k + d + 1 >= nmine) goto drained;
+          __builtin_amdgcn_sched_barrier(0);   // refill a buffer only once it is consumed
+        }
       }
     }
   drained:
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) keep(f[d]);
+    cfirst += 64 * NW;
+    if (cfirst > last) break;
+    nmine = chunk_size();
+    tbl = settle(tbl_next);
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
   }
+  pf = settle(pf);
 
   // Row sums: the four lanes of a row each hold a quarter of the tokens.
 #pragma unroll
@@ -475,11 +521,14 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 }
 
 
-template <bool INT8, bool ALIAS, int D, int MT, int NW>
+// MODE is the partition (Params::balanced): 0 aligned splits, 1 flattened
+// list, 2 pieces. Each partition is its own kernel, which keeps the scalar
+// registers of the other two out of its allocation.
+template <bool INT8, bool ALIAS, int D, int MT, int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 pa_mfma_kernel(const Params p) {
   __shared__ __attribute__((aligned(16))) char smem[MfmaLds<D, MT, NW, ALIAS>::BYTES];
-  if (!p.balanced) {
+  if constexpr (MODE == 0) {
     // Aligned splits: workgroup (split, b, g) takes blocks [blk_lo + split*bps, ...] of sequence b.
     const int32_t g = blockIdx.x % p.Hkv;
     const int32_t bsplit = blockIdx.x / p.Hkv;
@@ -492,11 +541,12 @@ pa_mfma_kernel(const Params p) {
     if (first > kr.blk_hi) return;
     const int32_t last = min(kr.blk_hi, first + p.bps - 1);
     const int64_t slot = p.splits > 1 ? (int64_t)(b * p.Hkv + g) * p.splits + split : -1;
-    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, L, kr, first, last, slot);
+    int32_t none = 0;
+    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, first, last, slot, chunk_table<NW>(p, b, first, last), none);
     return;
   }
   __shared__ int32_t pre[balanced_seq_limit(NW) + 1];
-  if (p.balanced == 2) {
+  if constexpr (MODE == 2) {
     // Piece partition: one run of one unit per workgroup; the slot of a
     // partial is the workgroup's own index.
     __shared__ int32_t nbs[kMaxPieceSeqs];
@@ -510,51 +560,93 @@ pa_mfma_kernel(const Params p) {
     const int32_t L = p.seq_lens[pc.b];
     const KeyRange kr = key_range(L, p.q_len, p.window);
     const int32_t first = kr.blk_lo + pc.first;
-    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, pc.b, pc.g, L, kr, first, first + pc.count - 1,
-                                         pc.k > 1 ? (int64_t)w : -1);
+    const int32_t last = first + pc.count - 1;
+    int32_t none = 0;
+    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, pc.b, pc.g, first, last, pc.k > 1 ? (int64_t)w : -1,
+                                         chunk_table<NW>(p, pc.b, first, last), none);
     return;
   }
-  // Flattened-list partition: this workgroup's slice of the flattened (unit, block)
-  // list, cut at unit boundaries into segments. A segment holding a whole
-  // unit writes the output directly; the others leave a partial in slot
-  // (workgroup + unit), which is unique because both indices only grow
-  // along the list.
-  block_prefix(p, pre);
-  __syncthreads();
-  if (blockIdx.x == 0 && p.ws_prefix)
-    for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
-  const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
-  int64_t x = (int64_t)blockIdx.x * bal.per;
-  const int64_t hi = min(bal.total, x + bal.per);
-  while (x < hi) {
-    const int32_t b = balanced_seq(pre, p.B, p.Hkv, x);
-    const int32_t nb = pre[b + 1] - pre[b];
-    const int64_t base = (int64_t)p.Hkv * pre[b];
-    const int32_t g = (int32_t)((x - base) / nb);
-    const int64_t off = base + (int64_t)g * nb;
-    const int64_t seg_hi = min(hi, off + nb);
-    const int32_t L = p.seq_lens[b];
-    const KeyRange kr = key_range(L, p.q_len, p.window);
-    const int32_t first = kr.blk_lo + (int32_t)(x - off);
-    const int32_t last = kr.blk_lo + (int32_t)(seg_hi - off) - 1;
-    const bool whole = x == off && seg_hi == off + nb;
-    const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)b * p.Hkv + g;
-    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, L, kr, first, last, slot);
-    x = seg_hi;
+  if constexpr (MODE == 1) {
+    // Flattened-list partition: this workgroup's slice of the flattened (unit, block)
+    // list, cut at unit boundaries into segments. A segment holding a whole
+    // unit writes the output directly; the others leave a partial in slot
+    // (workgroup + unit), which is unique because both indices only grow
+    // along the list. Each sequence's first loaded block sits in LDS next to
+    // the prefix sums, so the next segment's table entries are loaded while a
+    // segment streams, and a segment starts with one memory round trip (its
+    // first blocks, queries and length together) instead of three.
+    __shared__ int32_t blo[balanced_seq_limit(NW)];
+    block_prefix(p, pre, blo);
+    __syncthreads();
+    if (blockIdx.x == 0 && p.ws_prefix)
+      for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
+    const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
+    const int64_t x0 = (int64_t)blockIdx.x * bal.per;
+    const int64_t hi = min(bal.total, x0 + bal.per);
+    if (x0 >= hi) return;
+    // The segment starting at item x: unit (b, g), its first item `off`, and
+    // the logical blocks [first, last] it covers.
+    struct Seg {
+      int32_t b, g, first, last;
+      int64_t off, end;
+    };
+    auto segment_at = [&](int64_t x) __attribute__((always_inline)) {
+      Seg sg;
+      sg.b = balanced_seq(pre, p.B, p.Hkv, x);
+      const int32_t nb = pre[sg.b + 1] - pre[sg.b];
+      const int64_t base = (int64_t)p.Hkv * pre[sg.b];
+      sg.g = (int32_t)((x - base) / nb);
+      sg.off = base + (int64_t)sg.g * nb;
+      sg.end = min(hi, sg.off + nb);
+      sg.first = blo[sg.b] + (int32_t)(x - sg.off);
+      sg.last = blo[sg.b] + (int32_t)(sg.end - sg.off) - 1;
+      return sg;
+    };
+    int64_t x = x0;
+    Seg cur = segment_at(x);
+    int32_t tbl0 = settle(chunk_table<NW>(p, cur.b, cur.first, cur.last));
+    while (true) {
+      // The next segment's first table chunk loads while this one streams.
+      const bool more = cur.end < hi;
+      int32_t tbln = 0;
+      if (more) {
+        const Seg nx = segment_at(cur.end);
+        tbln = chunk_table<NW>(p, nx.b, nx.first, nx.last);
+      }
+      const bool whole = x == cur.off && cur.end == cur.off + (pre[cur.b + 1] - pre[cur.b]);
+      const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
+      mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln);
+      if (!more) break;
+      x = cur.end;
+      cur = segment_at(x);
+      tbl0 = tbln;
+    }
   }
 }
 
 namespace {
-template <bool INT8, bool ALIAS, int D, int MT>
-hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
+template <bool INT8, bool ALIAS, int D, int MT, int NW>
+hipError_t launch_mode(const Params& p, int grid, hipStream_t st, const Timing& tm, bool* ok) {
   *ok = true;
-  switch (nw) {
-    case 1: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 1>, grid, 64, st, tm, p);
-    case 2: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 2>, grid, 128, st, tm, p);
-    case 4: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 4>, grid, 256, st, tm, p);
-    case 8: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, 8>, grid, 512, st, tm, p);
+  switch (p.balanced) {
+    case 0: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, NW, 0>, grid, NW * 64, st, tm, p);
+    case 1: return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, NW, 1>, grid, NW * 64, st, tm, p);
+    case 2:
+      if constexpr (NW >= 4) return launch_timed(pa_mfma_kernel<INT8, ALIAS, D, MT, NW, 2>, grid, NW * 64, st, tm, p);
+      break;
   }
   *ok = false;
+  return hipSuccess;
+}
+
+template <bool INT8, bool ALIAS, int D, int MT>
+hipError_t launch_one(const Params& p, int nw, int grid, hipStream_t st, const Timing& tm, bool* ok) {
+  *ok = false;
+  switch (nw) {
+    case 2: return launch_mode<INT8, ALIAS, D, MT, 2>(p, grid, st, tm, ok);
+    case 4: return launch_mode<INT8, ALIAS, D, MT, 4>(p, grid, st, tm, ok);
+    case 8: return launch_mode<INT8, ALIAS, D, MT, 8>(p, grid, st, tm, ok);
+  }
   return hipSuccess;
 }
 
