@@ -94,8 +94,12 @@ typedef struct {
   int32_t num_splits;         /* 0: the library picks the context split; > 0: split each sequence's
                                  key range into this many parts (more if a part would exceed
                                  64 blocks per wavefront of the chosen kernel) */
-  void* workspace;            /* device scratch for split partials, caller-owned; may be NULL
-                                 when pa_workspace_size() returns 0 */
+  void* workspace;            /* device scratch for split partials and the piece queue,
+                                 caller-owned, 16-byte aligned; may be NULL when
+                                 pa_workspace_size() returns 0. Its first 4096 bytes must be
+                                 zero before the first call that uses it; every call leaves
+                                 them zero again, so one zero-fill at allocation is enough.
+                                 Calls that share a workspace must not run concurrently. */
   size_t workspace_bytes;     /* size of workspace */
   int32_t* debug_visits;      /* NULL, or [B][Hkv][max_blocks_per_seq] zeroed by the caller: the
                                  kernels add 1 for every (sequence, KV head, logical block) they load */
@@ -116,8 +120,10 @@ typedef struct {
   int32_t balanced;           /* 0: each workgroup owns one split of one (sequence, KV head);
                                  1: every workgroup takes an equal share of the flattened
                                  (sequence, KV head, block) list, cut where a unit ends;
-                                 2: every workgroup takes one near-equal piece of one unit
-                                 (few units: long contexts on one or two KV heads) */
+                                 2: units are cut into near-equal pieces, one per workgroup
+                                 or (queue != 0) handed out to the workgroups in turn */
+  int32_t pieces;             /* partition 2: most pieces the partition can produce */
+  int32_t queue;              /* partition 2: 1 if pieces go out through the workspace queue */
   size_t workspace_bytes;     /* == pa_workspace_size() */
 } pa_plan_info;
 
@@ -125,8 +131,9 @@ typedef struct {
  * Bytes of workspace the call needs for these arguments (0 when the key
  * range is not split). Depends on the shapes, max_seq_len, window,
  * num_splits, the device's compute-unit count and the tuning variables
- * PA_WAVES / PA_BLOCKS_PER_WAVE (read at every call), never on device data.
- * Returns (size_t)-1 if the arguments are invalid.
+ * PA_WAVES / PA_BLOCKS_PER_WAVE / PA_QUEUE / PA_PIECES_PER_WG (read at every
+ * call), never on device data. Returns (size_t)-1 if the arguments are
+ * invalid.
  */
 size_t pa_workspace_size(const pa_args* args);
 

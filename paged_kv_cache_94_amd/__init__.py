@@ -113,7 +113,9 @@ def _attach_workspace(a: _lib.PaArgs, workspace, device) -> object:
         return None
     if workspace is None:
         torch = _torch()
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        # Zero-filled: the library keeps the header words of the piece queue
+        # at zero between calls but needs them zero before the first one.
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     _require(workspace.numel() * workspace.element_size() >= need, f"workspace needs {need} bytes")
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()

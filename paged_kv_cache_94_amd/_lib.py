@@ -57,6 +57,8 @@ class PaPlanInfo(ctypes.Structure):
         ("blocks_per_split", ctypes.c_int32),
         ("grid", ctypes.c_int32),
         ("balanced", ctypes.c_int32),
+        ("pieces", ctypes.c_int32),
+        ("queue", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

@@ -44,6 +44,8 @@ int cu_count() {
   return n;
 }
 
+using pa::kWsHeader;
+
 struct Plan {
   int kernel = 0;       // 0 valu, 1 mfma
   int rows = 0;         // G * q_len
@@ -55,6 +57,8 @@ struct Plan {
   int n_blk_max = 0;
   int balanced = 0;     // 1: flattened-list partition, 2: piece partition (both over nwg workgroups)
   int nwg = 0;
+  int64_t pieces = 0;   // piece partition: pieces aimed for
+  bool queue = false;   // piece partition: pieces handed out through the workspace queue
   int64_t slots = 0;    // workspace partial slots
   int64_t grid = 0;
   size_t ws_bytes = 0;
@@ -168,27 +172,60 @@ int make_plan(const pa_args* a, Plan* pl) {
 
   // The matrix-core kernel defaults to a work-balanced partition over as
   // many workgroups as are resident at once (two per compute unit at 4
-  // waves, one at 8), each streaming about the same number of blocks
-  // whatever the length mix. With few units (long contexts on one or two KV
-  // heads) each workgroup takes one piece of one unit (partition 2); with
-  // many, a slice of the flattened (unit, block) list that may span several
-  // units (partition 1). Forced splits, the vector kernel and very large
-  // batches keep the aligned splits. PA_BALANCED=0 / PA_PIECES=0 turn the
-  // balanced partitions / the piece partition off (for tests and experiments).
+  // waves, one at 8). With few units (sequence, KV head) -- long contexts on
+  // one or two KV heads -- units are cut on the device into near-equal
+  // pieces, one per workgroup (partition 2). With many, pieces are handed out
+  // to the workgroups through a sharded queue in the workspace (partition 2
+  // with the queue). In between, and for batches beyond the piece
+  // partition's LDS tables, each workgroup takes an equal share of the
+  // flattened (unit, block) list (partition 1). Forced splits and the vector
+  // kernel keep the aligned splits. For tests and experiments:
+  // PA_BALANCED=0 / PA_PIECES=0|1 turn the balanced partitions off / the
+  // piece partition off or on, PA_QUEUE=0|1 forces the queue off or on, and
+  // PA_PIECES_PER_WG sets the pieces per workgroup the queue aims for.
   bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= pa::balanced_seq_limit(P.nw);
   if (const char* e = getenv("PA_BALANCED")) balanced = balanced && atoi(e) != 0;
   if (balanced) {
     P.nwg = cu_count() * (8 / P.nw);
     if (const char* e = getenv("PA_OVERSUB")) { const int v = atoi(e); if (v >= 1 && v <= 64) P.nwg *= v; }
-    bool pieces = 2 * units <= P.nwg && a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4;
-    if (const char* e = getenv("PA_PIECES")) pieces = pieces && atoi(e) != 0;
+    // Measured on MI355X: one piece per workgroup is best for few units
+    // (<= nwg/2: 16 long contexts on one KV head), the flattened list for
+    // about as many units as workgroups (512 units of 1-4K tokens: 90 us vs
+    // 102 us through the queue), the queue for many (2048 units of lognormal
+    // length: 333 us vs 347 us for the flattened list).
+    const bool few = 2 * units <= P.nwg;
+    const bool many = units >= 2 * (int64_t)P.nwg;
+    bool pieces = a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4 && (few || many);
+    if (const char* e = getenv("PA_PIECES")) pieces = a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4 && atoi(e) != 0;
     P.balanced = pieces ? 2 : 1;
     P.grid = P.nwg;
-    P.slots = pieces ? P.nwg : P.nwg + units;
+    if (pieces) {
+      bool queue = !few;
+      int64_t per_wg = 4;
+      if (const char* e = getenv("PA_QUEUE")) queue = atoi(e) != 0;
+      if (const char* e = getenv("PA_PIECES_PER_WG")) { const int v = atoi(e); if (v >= 1 && v <= 64) per_wg = v; }
+      P.queue = queue && P.nwg >= pa::kQueueShards;
+      P.pieces = queue ? per_wg * P.nwg : P.nwg;
+      if (P.pieces < 2 * units) P.pieces = 2 * units;   // the device's search for the piece size needs this
+      if (!P.queue && P.pieces > P.nwg) {               // one piece per workgroup: more pieces need the queue
+        P.queue = P.nwg >= pa::kQueueShards;
+        if (!P.queue) pieces = false;                     // (a device too small for the queue)
+      }
+      if (pieces) P.slots = P.pieces;
+    }
+    if (!pieces) {
+      P.balanced = 1;
+      P.queue = false;
+      P.pieces = 0;
+      P.slots = P.nwg + units;
+    }
   }
-  if (P.grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
+  if (P.grid > 0x7FFFFFFF || P.pieces > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
+  // Workspace: a 4 KiB header holding the piece-queue counters (zero between
+  // calls; no other partition writes the header), then the partials and the
+  // prefix sums.
   if (P.slots > 0) {
-    P.ws_bytes = (size_t)P.slots * P.rows * (size_t)(D + 2) * sizeof(float);
+    P.ws_bytes = kWsHeader + (size_t)P.slots * P.rows * (size_t)(D + 2) * sizeof(float);
     if (P.balanced) P.ws_bytes += (size_t)(a->num_seqs + 1) * sizeof(int32_t);
   } else {
     P.ws_bytes = 0;
@@ -207,14 +244,17 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   p.v_scale = a->v_scale;
   p.block_table = a->block_table;
   p.seq_lens = a->seq_lens;
-  // Workspace: acc [slots][rows][D] f32, then (m, l) [slots][rows][2] f32,
-  // then (balanced mode) the block prefix sums [B+1] int32.
+  // Workspace: the header (queue words), acc [slots][rows][D] f32, then
+  // (m, l) [slots][rows][2] f32, then (balanced mode) the prefix sums [B+1] int32.
   const size_t acc_bytes = (size_t)P.slots * P.rows * a->head_dim * sizeof(float);
   const size_t ml_bytes = (size_t)P.slots * P.rows * 2 * sizeof(float);
   char* ws = reinterpret_cast<char*>(a->workspace);
-  p.ws_acc = P.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  p.ws_ml = P.ws_bytes ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
-  p.ws_prefix = (P.ws_bytes && P.balanced) ? reinterpret_cast<int32_t*>(ws + acc_bytes + ml_bytes) : nullptr;
+  char* body = ws + kWsHeader;
+  p.ws_acc = P.ws_bytes ? reinterpret_cast<float*>(body) : nullptr;
+  p.ws_ml = P.ws_bytes ? reinterpret_cast<float*>(body + acc_bytes) : nullptr;
+  p.ws_prefix = (P.ws_bytes && P.balanced) ? reinterpret_cast<int32_t*>(body + acc_bytes + ml_bytes) : nullptr;
+  p.ws_queue = (P.ws_bytes && P.queue) ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  p.pieces = (int32_t)P.pieces;
   p.balanced = P.balanced;
   p.nwg = P.nwg;
   p.visits = a->debug_visits;
@@ -296,6 +336,8 @@ int pa_plan(const pa_args* a, pa_plan_info* info) {
   info->blocks_per_split = P.bps;
   info->grid = (int32_t)P.grid;
   info->balanced = P.balanced;
+  info->pieces = (int32_t)P.pieces;
+  info->queue = P.queue ? 1 : 0;
   info->workspace_bytes = P.ws_bytes;
   return PA_OK;
 }

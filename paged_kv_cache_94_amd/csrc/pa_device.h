@@ -40,6 +40,8 @@ struct Params {
   int32_t balanced;     // 0: aligned splits; 1: flattened-list partition; 2: piece partition
   int32_t nwg;          // modes 1 and 2: workgroups of the launch
   int32_t* ws_prefix;   // mode 1: [B+1] block prefix sums; mode 2: [B+1] piece prefix sums (workgroup 0 writes)
+  int32_t pieces;       // mode 2: pieces the partition aims for (nwg, or more when they are handed out)
+  int32_t* ws_queue;    // mode 2, non-null: hand pieces out through this [2] counter pair (zero between calls)
 };
 
 // Keys a step touches for one sequence (Lab 5 handout, "Sliding Window
@@ -176,27 +178,32 @@ __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre, int32_t* 
   }
 }
 
-// Piece partition, for batches with few (sequence, KV head) units compared
-// with the workgroups that fit on the device (long contexts, one or two KV
-// heads). Unit (b, g) with n_b blocks is cut into k_b = ceil(n_b / per)
-// pieces of ceil(n_b / k_b) blocks; `per` is the smallest count for which
-// every unit's pieces fit in nwg workgroups. Workgroup w owns piece w of the
-// list ordered by (b, g, piece), so every workgroup streams one run of one
-// unit with a single start-up, and none streams more than `per` blocks.
+// Piece partition. Unit (b, g) with n_b blocks is cut into
+// k_b = ceil(n_b / per) pieces of ceil(n_b / k_b) blocks; `per` is the
+// smallest count for which all pieces number at most p.pieces. Pieces are
+// ordered by (b, g, piece). With p.pieces == nwg each workgroup owns the
+// piece of its own index (few units: long contexts on one or two KV heads);
+// with more, workgroups take pieces from a queue until none are left, which
+// evens out the time workgroups take for the same number of blocks.
 //
-// Wave 0 fills nbs[b] = n_b and kp[0..B] = Hkv * (k_0 + ... + k_{b-1}); the
-// caller synchronises the workgroup before reading them. `per` is at least
-// min_per (enough blocks for every wavefront of the workgroup). Needs
-// nwg >= 2 * B * Hkv (checked on the host), which bounds the search below.
+// Wave 0 fills nbs[b] = n_b, blo[b] = the first logical block sequence b
+// loads, and kp[0..B] = Hkv * (k_0 + ... + k_{b-1}); the caller synchronises
+// the workgroup before reading them. `per` is at least min_per (enough
+// blocks for every wavefront of the workgroup). Needs p.pieces >= 2 * B * Hkv
+// (checked on the host), which bounds the search below.
 template <typename P>
-__device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* kp, int32_t min_per) {
+__device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* blo, int32_t* kp, int32_t min_per) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   int64_t total = 0;
   for (int32_t base = 0; base < p.B; base += 64) {
     const int32_t b = base + lane;
-    const int32_t nb = b < p.B ? seq_blocks(p.seq_lens[b], p) : 0;
-    if (b < p.B) nbs[b] = nb;
+    const int32_t L = b < p.B ? p.seq_lens[b] : 0;
+    const int32_t nb = b < p.B ? seq_blocks(L, p) : 0;
+    if (b < p.B) {
+      nbs[b] = nb;
+      blo[b] = key_range(L, p.q_len, p.window).blk_lo;
+    }
     total += wave_sum_wide(nb);
   }
   total *= p.Hkv;
@@ -207,15 +214,16 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
     for (int32_t b = lane; b < p.B; b += 64) c += (nbs[b] + per - 1) / per;
     return (int64_t)wave_sum(c) * p.Hkv;
   };
-  // pieces(per) <= total / per + B*Hkv, so per_hi = ceil(total / (nwg - B*Hkv)) always fits.
-  const int64_t spare = (int64_t)p.nwg - (int64_t)p.B * p.Hkv;
-  int64_t lo = (total + p.nwg - 1) / p.nwg;
+  // pieces(per) <= total / per + B*Hkv, so per_hi = ceil(total / (target - B*Hkv)) always fits.
+  const int64_t target = p.pieces;
+  const int64_t spare = target - (int64_t)p.B * p.Hkv;
+  int64_t lo = (total + target - 1) / target;
   int64_t hi = spare > 0 ? (total + spare - 1) / spare : total;
   if (lo < min_per) lo = min_per;
   if (hi < lo) hi = lo;   // pieces() only falls as per grows
   while (lo < hi) {
     const int64_t mid = (lo + hi) >> 1;
-    if (pieces((int32_t)mid) <= p.nwg) hi = mid;
+    if (pieces((int32_t)mid) <= target) hi = mid;
     else lo = mid + 1;
   }
   const int32_t per = (int32_t)lo;

@@ -114,13 +114,16 @@ __device__ __forceinline__ int32_t chunk_table(const Params& p, int32_t b, int32
 // Attention of query rows (b, g) over logical blocks [first, last] of sequence
 // b. slot < 0: write the normalised output; else write (m, l, o) to
 // workspace slot `slot`. tbl0 = chunk_table(b, first, last), which the caller
-// may have loaded ahead. pf is a load the caller issued for a later segment:
-// it is waited for right after this segment's block loop, when nothing else
-// is in flight, so it reaches the caller as a settled value. Called uniformly
-// by every wavefront of the workgroup.
+// may have loaded ahead. pf and pf_claim are loads the caller issued for a
+// later segment: they are waited for right after this segment's block loop,
+// when nothing else is in flight, so they reach the caller as settled values.
+// pf_claim is thread 0's claim on the piece queue; it is handed to every
+// wavefront through *claim_lds (read after this call returns). Called
+// uniformly by every wavefront of the workgroup.
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
 __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t first,
-                                             int32_t last, int64_t slot, int32_t tbl0, int32_t& pf) {
+                                             int32_t last, int64_t slot, int32_t tbl0, int32_t& pf,
+                                             int32_t& pf_claim, int32_t* claim_lds) {
   using Lds = MfmaLds<D, MT, NW, ALIAS>;
   constexpr int ROWS = Lds::ROWS;
   constexpr int C = D / 32;                           // contraction chunks of 32 dims
@@ -424,6 +427,8 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
   }
   pf = settle(pf);
+  pf_claim = settle(pf_claim);
+  if (claim_lds && threadIdx.x == 0) *claim_lds = pf_claim;   // read by all after the merge's barriers
 
   // Row sums: the four lanes of a row each hold a quarter of the tokens.
 #pragma unroll
@@ -541,29 +546,92 @@ pa_mfma_kernel(const Params p) {
     if (first > kr.blk_hi) return;
     const int32_t last = min(kr.blk_hi, first + p.bps - 1);
     const int64_t slot = p.splits > 1 ? (int64_t)(b * p.Hkv + g) * p.splits + split : -1;
-    int32_t none = 0;
-    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, first, last, slot, chunk_table<NW>(p, b, first, last), none);
+    int32_t none = 0, none_c = 0;
+    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, first, last, slot, chunk_table<NW>(p, b, first, last), none,
+                                         none_c, nullptr);
     return;
   }
   __shared__ int32_t pre[balanced_seq_limit(NW) + 1];
   if constexpr (MODE == 2) {
-    // Piece partition: one run of one unit per workgroup; the slot of a
-    // partial is the workgroup's own index.
+    // Piece partition: each piece is one run of one unit; the slot of a
+    // partial is the piece's own index.
     __shared__ int32_t nbs[kMaxPieceSeqs];
-    piece_prefix(p, nbs, pre, 2 * NW);
+    __shared__ int32_t blo[kMaxPieceSeqs];
+    __shared__ int32_t claims[2];
+    // Queue shard of this workgroup: shard s hands out pieces s, s + kQueueShards, ...
+    // (one counter per shard: claims on a single counter serialize at ~11 ns each).
+    const int32_t shard = blockIdx.x % kQueueShards;
+    int32_t* const qnext = p.ws_queue ? p.ws_queue + shard * kQueueStride : nullptr;
+    int32_t* const qdone = qnext ? qnext + kQueueShards * kQueueStride : nullptr;
+    piece_prefix(p, nbs, blo, pre, 2 * NW);
+    if (qnext && threadIdx.x == 0) {
+      claims[0] = atomicAdd(qnext, 1);   // this workgroup's first two claims
+      claims[1] = atomicAdd(qnext, 1);
+    }
     __syncthreads();
     if (blockIdx.x == 0 && p.ws_prefix)
       for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
-    const int32_t w = blockIdx.x;
-    if (w >= pre[p.B]) return;
-    const Piece pc = piece_of(nbs, pre, p.B, p.Hkv, w);
-    const int32_t L = p.seq_lens[pc.b];
-    const KeyRange kr = key_range(L, p.q_len, p.window);
-    const int32_t first = kr.blk_lo + pc.first;
-    const int32_t last = first + pc.count - 1;
-    int32_t none = 0;
-    mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, pc.b, pc.g, first, last, pc.k > 1 ? (int64_t)w : -1,
-                                         chunk_table<NW>(p, pc.b, first, last), none);
+    const int32_t npieces = pre[p.B];
+    struct Run {
+      int32_t b, g, first, last;
+      int64_t slot;
+    };
+    auto run_of = [&](int32_t w) __attribute__((always_inline)) {
+      const Piece pc = piece_of(nbs, pre, p.B, p.Hkv, w);
+      Run r;
+      r.b = pc.b;
+      r.g = pc.g;
+      r.first = blo[pc.b] + pc.first;
+      r.last = r.first + pc.count - 1;
+      r.slot = pc.k > 1 ? (int64_t)w : -1;
+      return r;
+    };
+    if (!p.ws_queue) {
+      // Static: workgroup w owns piece w.
+      const int32_t w = blockIdx.x;
+      if (w >= npieces) return;
+      const Run r = run_of(w);
+      int32_t none = 0, none_c = 0;
+      mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot,
+                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr);
+      return;
+    }
+    // Queue: claims only grow, so a workgroup's pieces come in increasing
+    // order. While piece w streams, the next piece's table entries load and
+    // thread 0 claims the one after it.
+    auto piece_of_claim = [&](int32_t c) __attribute__((always_inline)) {
+      return c < 0 ? -1 : shard + kQueueShards * c;
+    };
+    int32_t w = piece_of_claim(claims[0]);
+    int32_t w1 = piece_of_claim(claims[1]);
+    int32_t tbl0 = 0;
+    // A negative claim can only come from a header that was not zero-filled;
+    // it ends the workgroup rather than naming a piece.
+    if (w >= 0 && w < npieces) {
+      const Run r = run_of(w);
+      tbl0 = settle(chunk_table<NW>(p, r.b, r.first, r.last));
+    }
+    while (w >= 0 && w < npieces) {
+      const Run r = run_of(w);
+      int32_t tbln = 0, claim = 0;
+      if (w1 >= 0 && w1 < npieces) {
+        const Run rn = run_of(w1);
+        tbln = chunk_table<NW>(p, rn.b, rn.first, rn.last);
+      }
+      if (threadIdx.x == 0) claim = atomicAdd(qnext, 1);
+      mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot, tbl0, tbln, claim,
+                                           &claims[0]);
+      w = w1;
+      w1 = piece_of_claim(claims[0]);
+      tbl0 = tbln;
+    }
+    // The last workgroup of a shard out returns its counters to zero for the
+    // next call (every claim on that shard has completed by then).
+    const int32_t members = ((int32_t)gridDim.x - shard + kQueueShards - 1) / kQueueShards;
+    if (threadIdx.x == 0 && atomicAdd(qdone, 1) == members - 1) {
+      atomicExch(qnext, 0);
+      atomicExch(qdone, 0);
+    }
     return;
   }
   if constexpr (MODE == 1) {
@@ -615,7 +683,9 @@ pa_mfma_kernel(const Params p) {
       }
       const bool whole = x == cur.off && cur.end == cur.off + (pre[cur.b + 1] - pre[cur.b]);
       const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
-      mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln);
+      int32_t none_c = 0;
+      mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln, none_c,
+                                           nullptr);
       if (!more) break;
       x = cur.end;
       cur = segment_at(x);

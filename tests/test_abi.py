@@ -119,7 +119,8 @@ def test_int8_entry_rules(lib):
 def test_workspace_is_required_when_split(lib):
     a = _args(num_splits=4, max_seq_len=8192, window=0)
     need = lib.pa_workspace_size(ctypes.byref(a))
-    assert need == 4 * 8 * 4 * 2 * (256 + 2) * 4
+    # 4 KiB header (the piece-queue counters), then 4 splits x 8 units x 2 rows of (o[256], m, l) in fp32.
+    assert need == 4096 + 4 * 8 * 4 * 2 * (256 + 2) * 4
     assert lib.pa_decode(ctypes.byref(a), None) == _lib.PA_ERR_WORKSPACE
 
 
@@ -131,14 +132,22 @@ def test_plan_choices(lib):
     # Global layer: 16 query heads on one KV head go to the matrix cores.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768,
                                           max_blocks_per_seq=2048)), ctypes.byref(info)) == 0
-    # Few long units: each workgroup owns one piece of one unit.
+    # Few long units: each workgroup owns one piece of one unit (no queue).
     assert info.kernel == 1 and info.rows == 16 and info.balanced == 2 and info.waves_per_group == 4
+    assert info.queue == 0 and info.pieces == info.grid
     # Verify step: 4 heads x 5 tokens = 20 rows.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
                                           window=0, max_seq_len=16384, max_blocks_per_seq=1024)),
                        ctypes.byref(info)) == 0
-    # Many units (256 sequences x 8 KV heads): slices of the flattened list.
-    assert info.kernel == 1 and info.rows == 20 and info.balanced == 1
+    # Many units (256 sequences x 8 KV heads, >= 2 per workgroup on a 256-CU part):
+    # pieces handed out through the workspace queue.
+    assert info.kernel == 1 and info.rows == 20 and info.balanced == 2 and info.queue == 1
+    assert info.workspace_bytes >= 4096
+    # About as many units as workgroups (64 sequences x 8 KV heads, int8): the flattened list.
+    assert lib.pa_plan(ctypes.byref(_args(num_seqs=64, num_q_heads=64, num_kv_heads=8, head_dim=128, window=0,
+                                          max_seq_len=4096, max_blocks_per_seq=256, q_dtype=_lib.PA_BF16,
+                                          kv_dtype=_lib.PA_INT8, k_scale=8, v_scale=8)), ctypes.byref(info)) == 0
+    assert info.kernel == 1 and info.rows == 8 and info.balanced == 1 and info.queue == 0
     # A forced split count is honoured (capped by the blocks a sequence can span).
     assert lib.pa_plan(ctypes.byref(_args(num_splits=3)), ctypes.byref(info)) == 0
     assert info.splits == 3
