@@ -74,7 +74,8 @@ typedef struct {
   const void* q;              /* [B][q_len][Hq][D], q_dtype */
   const void* k_pool;         /* [num_blocks][block_size][Hkv][D], kv_dtype */
   const void* v_pool;         /* same shape; may equal k_pool (keys and values shared, read once) */
-  const float* k_scale;       /* int8 cache only: [num_blocks][block_size][Hkv]; else NULL */
+  const float* k_scale;       /* int8 cache only: [num_blocks][Hkv][block_size], one fp32 per (token,
+                                 KV head), a block's 16 scales of one head contiguous; else NULL */
   const float* v_scale;       /* int8 cache only: same shape; else NULL */
   const int32_t* block_table; /* [B][max_blocks_per_seq] physical block ids */
   const int32_t* seq_lens;    /* [B] cached tokens per sequence, this step's q_len tokens included */

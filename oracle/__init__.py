@@ -152,6 +152,9 @@ class Problem:
         kv_code = _dtype_code(self.k_pool)
         if _dtype_code(self.v_pool) != kv_code:
             raise ValueError("k and v pools differ in dtype")
+        for sc in (self.k_scale, self.v_scale):
+            if sc is not None and sc.shape != (nb, Hkv, bs):
+                raise ValueError("scales must be [num_blocks, Hkv, block_size]")
         s = _Problem()
         s.q = self.q.ctypes.data
         s.k_pool = self.k_pool.ctypes.data

@@ -64,7 +64,7 @@ typedef struct {
   const void* q;            /* [B][q_len][Hq][D], q_dtype */
   const void* k_pool;       /* [num_blocks][block_size][Hkv][D], kv_dtype */
   const void* v_pool;       /* same shape and dtype */
-  const float* k_scale;     /* [num_blocks][block_size][Hkv], int8 only */
+  const float* k_scale;     /* [num_blocks][Hkv][block_size], int8 only */
   const float* v_scale;     /* same */
   const int32_t* block_table; /* [B][max_blocks] */
   const int32_t* seq_lens;  /* [B] */
@@ -138,10 +138,13 @@ static size_t key_row(const orc_problem* P, int b, int32_t j, int g) {
 #endif
 }
 
+/* Scale of key j, kv head g of sequence b: one float per (token, head), stored
+ * [block][head][slot] so that a block's scales for one head are contiguous. */
 static double key_scale(const float* s, const orc_problem* P, int b, int32_t j, int g) {
   if (P->kv_dtype != ORC_I8) return 1.0;
-  size_t row = key_row(P, b, j, g) / (size_t)P->D;   /* (blk, slot, g) index */
-  return (double)s[row];
+  int32_t blk = P->block_table[(size_t)b * P->max_blocks + j / P->block_size];
+  int32_t slot = j % P->block_size;
+  return (double)s[((size_t)blk * P->Hkv + g) * P->block_size + slot];
 }
 
 /* One output row: (sequence b, query token t, query head h) -> out[0..D). */

@@ -8,7 +8,7 @@ and allocates the split workspace through PyTorch's caching allocator.
 Layouts (row-major, all tensors on the same GPU):
     q, out       [B, q_len, Hq, D]            float32 or bfloat16
     k_pool, v_pool [num_blocks, 16, Hkv, D]   same dtype as q, or int8
-    k_scale, v_scale [num_blocks, 16, Hkv]    float32 (int8 caches)
+    k_scale, v_scale [num_blocks, Hkv, 16]    float32 (int8 caches)
     block_table  [B, max_blocks_per_seq]      int32
     seq_lens     [B]                          int32, this step's tokens included
 """
@@ -74,7 +74,7 @@ def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, s
     _require(block_table.shape[0] == B and seq_lens.shape[0] == B, "batch mismatch")
     for s in (k_scale, v_scale):
         if s is not None:
-            _require(s.dtype == torch.float32 and tuple(s.shape) == (nb, bs, Hkv), "scales must be float32 [nb, bs, Hkv]")
+            _require(s.dtype == torch.float32 and tuple(s.shape) == (nb, Hkv, bs), "scales must be float32 [nb, Hkv, bs]")
     if debug_visits is not None:
         _require(debug_visits.dtype == torch.int32 and tuple(debug_visits.shape) == (B, Hkv, block_table.shape[1]),
                  "debug_visits must be int32 [B, Hkv, max_blocks]")

@@ -5,7 +5,8 @@
 // unnormalised output. The merge is the online-softmax rule of the Lab 5
 // handout ("Flash Attention") applied across splits:
 //   M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per output row; one thread per dim of the head.
+// One workgroup per unit to merge (or per workgroup boundary of the
+// flattened-list partition), all query rows of it.
 #include "pa_common.h"
 
 namespace pa {
@@ -17,14 +18,28 @@ __host__ __device__ inline int64_t combine_groups(const Params& p) {
   return p.balanced == 1 ? (int64_t)(p.nwg > 1 ? p.nwg - 1 : 0) : (int64_t)p.B * p.Hkv;
 }
 
-constexpr int kCombineChunk = 64;   // partials whose loads are in flight together
+constexpr int kCombineWaves = 4;
 
+// Workgroups per merged unit: 1 when there are enough units to fill the
+// device, else one per group of kCombineWaves query rows.
+__host__ __device__ inline int combine_row_groups(const Params& p) {
+  return combine_groups(p) >= 256 ? 1 : (p.rows + kCombineWaves - 1) / kCombineWaves;
+}
+
+// Workgroup (grp, rg) merges one unit's partials for query rows
+// rg*4 + w, rg*4 + w + 4*RG, ... (w = its wavefront, RG workgroups per unit). For a row, lane s holds split s's
+// (m, l) (64 splits at a time); the row max, the weights 2^(m_s - M) and the
+// weighted sum of l come from wave reductions, and the D dims of the row are
+// spread over the lanes (D/64 consecutive floats each), so every partial row
+// is read with one coalesced load per lane.
 template <typename OutT, int D>
-__global__ void __launch_bounds__(D) pa_combine_kernel(const Params p) {
-  // Workgroup (group, r): output row r of one unit; thread d owns dim d.
-  const int r = blockIdx.x % p.rows;
-  const int32_t grp = blockIdx.x / p.rows;
+__global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Params p) {
+  constexpr int PER = D / 64;   // dims per lane
+  const int rgs = combine_row_groups(p);
+  const int32_t grp = blockIdx.x / rgs;
+  const int rg = blockIdx.x % rgs;
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   int32_t b, g;
   int64_t slot_first;
   int32_t ns;
@@ -35,7 +50,7 @@ __global__ void __launch_bounds__(D) pa_combine_kernel(const Params p) {
     // w0..w1 left its partials in slots w + unit. The block prefix sums are
     // staged in LDS so the search below costs no memory round trips.
     __shared__ int32_t pre[kMaxBalancedSeqs + 1];
-    for (int32_t i = threadIdx.x; i <= p.B; i += D) pre[i] = p.ws_prefix[i];
+    for (int32_t i = threadIdx.x; i <= p.B; i += 64 * kCombineWaves) pre[i] = p.ws_prefix[i];
     __syncthreads();
     const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
     const int64_t x = (int64_t)(grp + 1) * bal.per;
@@ -55,9 +70,9 @@ __global__ void __launch_bounds__(D) pa_combine_kernel(const Params p) {
     const int32_t L = p.seq_lens[b];
     if (!len_ok(L, p)) return;
     if (p.balanced == 2) {
-      // Piece partition: unit (b, g) was cut into k pieces, owned by
-      // workgroups kp[b] + g*k .. + k-1, each of which left its partial in
-      // the slot of its own index; a unit of one piece was written out directly.
+      // Piece partition: unit (b, g) was cut into k pieces, numbered
+      // kp[b] + g*k .. + k-1, each of which left its partial in the slot of
+      // its own number; a unit of one piece was written out directly.
       const int32_t k = (p.ws_prefix[b + 1] - p.ws_prefix[b]) / p.Hkv;
       if (k <= 1) return;
       slot_first = p.ws_prefix[b] + (int64_t)g * k;
@@ -69,48 +84,72 @@ __global__ void __launch_bounds__(D) pa_combine_kernel(const Params p) {
     }
   }
 
-  const size_t slot0 = (size_t)slot_first * p.rows + r;
-  const size_t step = (size_t)p.rows;
-  const float* ml = p.ws_ml + slot0 * 2;
-  const float* acc = p.ws_acc + slot0 * D + threadIdx.x;
-
-  // Chunks of up to 64 partials: every load of a chunk is issued before any
-  // is used. Partial s's (m, l) sits in lane s % 64; the chunk max and the
-  // weights come from wave reductions and v_readlane. Chunks after the first
-  // rescale the running sums (online-softmax rule).
-  float M = -INFINITY, num = 0.f, den = 0.f;
-  for (int32_t c0 = 0; c0 < ns; c0 += kCombineChunk) {
-    const int32_t cnt = min(kCombineChunk, ns - c0);
-    float a[kCombineChunk];
+  for (int r = rg * kCombineWaves + wave; r < p.rows; r += rgs * kCombineWaves) {
+    const size_t slot0 = (size_t)slot_first * p.rows + r;   // partial s of this row: slot0 + s*rows
+    const float* ml = p.ws_ml + slot0 * 2;
+    const float* acc = p.ws_acc + slot0 * D + lane * PER;
+    float o[PER];
 #pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j) a[j] = j < cnt ? acc[(size_t)(c0 + j) * step * D] : 0.f;
-    const float ms = lane < cnt ? ml[(size_t)(c0 + lane) * step * 2] : -INFINITY;
-    const float ls = lane < cnt ? ml[(size_t)(c0 + lane) * step * 2 + 1] : 0.f;
-    float cm = ms;
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+    float M = -INFINITY, den = 0.f;
+    for (int32_t c0 = 0; c0 < ns; c0 += 64) {
+      const int32_t cnt = min(64, ns - c0);
+      const float ms = lane < cnt ? ml[(size_t)(c0 + lane) * p.rows * 2] : -INFINITY;
+      const float ls = lane < cnt ? ml[(size_t)(c0 + lane) * p.rows * 2 + 1] : 0.f;
+      float cm = ms;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor(cm, off));
-    const float Mn = fmaxf(M, cm);
-    const float Ms = Mn == -INFINITY ? 0.f : Mn;
-    const float resc = fast_exp2(M - Ms);   // 0 on the first chunk (M = -inf)
-    num *= resc;
-    den *= resc;
-    M = Mn;
-    const float w = lane < cnt ? fast_exp2(ms - Ms) : 0.f;
-    float dl = w * ls;
+      for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor(cm, off));
+      const float Mn = fmaxf(M, cm);
+      const float Ms = Mn == -INFINITY ? 0.f : Mn;
+      const float resc = fast_exp2(M - Ms);   // 0 on the first chunk (M = -inf)
+      den *= resc;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dl += shfl_xor(dl, off);
-    den += dl;
+      for (int e = 0; e < PER; ++e) o[e] *= resc;
+      M = Mn;
+      const float w = lane < cnt ? fast_exp2(ms - Ms) : 0.f;
+      float dl = w * ls;
 #pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j)
-      num += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j)) * a[j];
-  }
-  const int t = r / p.G;
-  const int h = g * p.G + r % p.G;
-  OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + threadIdx.x;
-  if constexpr (sizeof(OutT) == 4) {
-    *out = num / den;
-  } else {
-    *out = (__bf16)(num / den);
+      for (int off = 32; off >= 1; off >>= 1) dl += shfl_xor(dl, off);
+      den += dl;
+      // Accumulate the chunk's partial rows, NB loads in flight at a time.
+      constexpr int NB = 16;
+      for (int32_t j0 = 0; j0 < cnt; j0 += NB) {
+        float v[NB][PER];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const bool ok = j0 + j < cnt;
+          const float* src = acc + (size_t)(c0 + j0 + j) * p.rows * D;
+          if constexpr (PER == 4) {
+            const float4 t = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
+          } else if constexpr (PER == 2) {
+            const float2 t = ok ? *reinterpret_cast<const float2*>(src) : make_float2(0.f, 0.f);
+            v[j][0] = t.x; v[j][1] = t.y;
+          } else {
+            v[j][0] = ok ? src[0] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int jj = min(j0 + j, 63);
+          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), jj));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o[e] += wj * v[j][e];
+        }
+      }
+    }
+    const float inv = 1.f / den;
+    const int t = r / p.G;
+    const int h = g * p.G + r % p.G;
+    OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if constexpr (sizeof(OutT) == 4) {
+        out[e] = o[e] * inv;
+      } else {
+        out[e] = (__bf16)(o[e] * inv);
+      }
+    }
   }
 }
 
@@ -138,23 +177,23 @@ __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const ch
 }
 
 hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
-  const int64_t rows = combine_groups(p) * p.rows;
-  if (rows == 0) return hipSuccess;
-  if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)rows);
+  const int64_t groups = combine_groups(p) * combine_row_groups(p);
+  if (groups == 0) return hipSuccess;
+  if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)groups), block(64 * kCombineWaves);
   const bool bf16 = q_dtype == 1;
   switch (D) {
     case 64:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 64>), grid, dim3(64), 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 64>), grid, dim3(64), 0, st, p);
+      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 64>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((pa_combine_kernel<float, 64>), grid, block, 0, st, p);
       break;
     case 128:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 128>), grid, dim3(128), 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 128>), grid, dim3(128), 0, st, p);
+      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 128>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((pa_combine_kernel<float, 128>), grid, block, 0, st, p);
       break;
     case 256:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 256>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 256>), grid, dim3(256), 0, st, p);
+      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 256>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((pa_combine_kernel<float, 256>), grid, block, 0, st, p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -246,11 +246,11 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       for (int u = 0; u < NLOAD; ++u) f.v[u] = buffer_load16<CPOL>(vd, lane_off, u * RPI * tok_stride);
     }
     if constexpr (INT8) {
-      // Scales of the block's 16 tokens for this KV head, Hkv floats apart.
-      const size_t s0 = (size_t)phys * kBlock * p.Hkv + g;
-      const int32_t sbytes = valid ? ((kBlock - 1) * p.Hkv + 1) * 4 : 0;
-      f.ks = buffer_load_f32(buffer_rsrc(p.k_scale + s0, sbytes), (lane & 15) * p.Hkv * 4);
-      f.vs = buffer_load_f32(buffer_rsrc(p.v_scale + s0, sbytes), (lane & 15) * p.Hkv * 4);
+      // The block's 16 scales of this KV head: one 64-byte run ([block][head][slot]).
+      const size_t s0 = ((size_t)phys * p.Hkv + g) * kBlock;
+      const int32_t sbytes = valid ? kBlock * 4 : 0;
+      f.ks = buffer_load_f32(buffer_rsrc(p.k_scale + s0, sbytes), (lane & 15) * 4);
+      f.vs = buffer_load_f32(buffer_rsrc(p.v_scale + s0, sbytes), (lane & 15) * 4);
     }
   };
 

@@ -30,8 +30,9 @@ def contiguous_cache(x, b: int):
     k = storage_to_f64(x.k_pool[blocks]).reshape(nblk * x.block_size, x.num_kv_heads, x.head_dim)[:L]
     v = storage_to_f64(x.v_pool[blocks]).reshape(nblk * x.block_size, x.num_kv_heads, x.head_dim)[:L]
     if x.kv_dtype == "int8":
-        ks = x.k_scale[blocks].astype(np.float64).reshape(-1, x.num_kv_heads)[:L]
-        vs = x.v_scale[blocks].astype(np.float64).reshape(-1, x.num_kv_heads)[:L]
+        # scales are [block, head, slot]: bring slots next to blocks, then flatten tokens
+        ks = x.k_scale[blocks].transpose(0, 2, 1).astype(np.float64).reshape(-1, x.num_kv_heads)[:L]
+        vs = x.v_scale[blocks].transpose(0, 2, 1).astype(np.float64).reshape(-1, x.num_kv_heads)[:L]
         k = k * ks[..., None]
         v = v * vs[..., None]
     return k, v

@@ -192,9 +192,9 @@ def test_int8_scales_apply_per_token():
     x = make_inputs([20], q_len=1, num_q_heads=2, num_kv_heads=1, head_dim=64,
                     q_dtype="f32", kv_dtype="int8", seed=21)
     blk, slot = x.block_table[0, 0], 7
-    kf = x.k_pool.astype(np.float32) * x.k_scale[..., None]
-    vf = x.v_pool.astype(np.float32) * x.v_scale[..., None]
-    x.k_scale[blk, slot] *= 2.0
+    kf = x.k_pool.astype(np.float32) * x.k_scale.transpose(0, 2, 1)[..., None]
+    vf = x.v_pool.astype(np.float32) * x.v_scale.transpose(0, 2, 1)[..., None]
+    x.k_scale[blk, :, slot] *= 2.0
     kf[blk, slot] *= 2.0
     got = run(x)
     p = oracle.Problem(x.q, kf.astype(np.float32), vf.astype(np.float32), x.block_table, x.seq_lens,

@@ -5,7 +5,8 @@ Layouts (all row-major, shared by every consumer):
 * ``q``           ``[B, q_len, Hq, D]``      float32, or uint16 holding bf16 bits
 * ``k_pool``      ``[num_blocks, 16, Hkv, D]`` float32 / uint16 (bf16 bits) / int8
 * ``v_pool``      same shape and dtype; may be the very same array as ``k_pool``
-* ``k_scale``     ``[num_blocks, 16, Hkv]``   float32, int8 caches only (one per token per head)
+* ``k_scale``     ``[num_blocks, Hkv, 16]``   float32, int8 caches only (one per token per head; a
+                                              block's 16 scales of one head are contiguous)
 * ``v_scale``     same
 * ``block_table`` ``[B, max_blocks]``         int32, logical block -> physical block
 * ``seq_lens``    ``[B]``                     int32, cached tokens including this step's queries
@@ -170,7 +171,8 @@ def _draw_kv(rng: np.random.Generator, shape, kv_dtype: str):
     if kv_dtype == "bf16":
         return f32_to_bf16_bits(x), None
     if kv_dtype == "int8":
-        return _encode_int8_per_token(x)
+        codes, scale = _encode_int8_per_token(x)          # scale [blocks, 16, Hkv]
+        return codes, np.ascontiguousarray(scale.transpose(0, 2, 1))
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
@@ -178,7 +180,7 @@ def _poison_slots(pool: np.ndarray, scale: Optional[np.ndarray], blocks, slots, 
     """Overwrite pool[blocks, slots] (all heads, all dims) with NaN, or NaN scales for int8."""
     if kv_dtype == "int8":
         pool[blocks, slots] = 127
-        scale[blocks, slots] = np.nan
+        scale[blocks, :, slots] = np.nan
     elif kv_dtype == "bf16":
         pool[blocks, slots] = _BF16_QNAN
     else:
