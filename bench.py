@@ -47,9 +47,21 @@ METRIC = "decode-attention queries/s and achieved KV HBM GB/s (% of MI355X peak)
 # holds only for the kernel sources and the launch plan it was taken with;
 # for anything else the record's traffic is null.
 MEASURED_TRAFFIC = {
-    2: {"kernel_sources": "b00dcd1793c606ef",
-        "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256},
-        "fetch_kib": 132879, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
+    1: {"kernel_sources": "48020fc58e3cf036",
+        "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 4, "balanced": 0, "pieces": 0, "queue": 0},
+        "fetch_kib": 91, "fetch_factor": 2.0, "write_kib": 2, "write_factor": 1.0},
+    2: {"kernel_sources": "48020fc58e3cf036",
+        "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256, "balanced": 0, "pieces": 0, "queue": 0},
+        "fetch_kib": 132865, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
+    3: {"kernel_sources": "35f193dde5d995d4",
+        "plan": {"kernel": 1, "rows": 16, "waves_per_group": 4, "splits": 57, "grid": 512, "balanced": 2, "pieces": 512, "queue": 0},
+        "fetch_kib": 61361, "fetch_factor": 2.0, "write_kib": 7998, "write_factor": 1.0},
+    4: {"kernel_sources": "35f193dde5d995d4",
+        "plan": {"kernel": 1, "rows": 8, "waves_per_group": 4, "splits": 4, "grid": 512, "balanced": 1, "pieces": 0, "queue": 0},
+        "fetch_kib": 190040, "fetch_factor": 2.0, "write_kib": 3992, "write_factor": 1.0},
+    5: {"kernel_sources": "35f193dde5d995d4",
+        "plan": {"kernel": 1, "rows": 20, "waves_per_group": 4, "splits": 16, "grid": 512, "balanced": 2, "pieces": 4096, "queue": 1},
+        "fetch_kib": 839156, "fetch_factor": 2.0, "write_kib": 37182, "write_factor": 1.0},
 }
 KERNEL_SOURCES = {0: ("pa_device.h", "pa_common.h", "pa_valu.hip"), 1: ("pa_device.h", "pa_common.h", "pa_mfma.hip")}
 
