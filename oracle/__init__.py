@@ -57,6 +57,25 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _Write(ctypes.Structure):
+    _fields_ = [
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("slot_ids", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("src_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+    ]
+
+
 def build(force: bool = False, extra_flags: Optional[list] = None, out: Optional[str] = None) -> str:
     """Compile oracle.c into a shared library with gcc (-O2, OpenMP)."""
     target = out or _LIB_PATH
@@ -82,6 +101,8 @@ def _bind(path: str):
                                   ctypes.c_int64]
     lib.oracle_gather.restype = ctypes.c_int
     lib.oracle_default_threads.restype = ctypes.c_int
+    lib.oracle_cache_write.argtypes = [ctypes.POINTER(_Write)]
+    lib.oracle_cache_write.restype = ctypes.c_int
     return lib
 
 
@@ -220,3 +241,37 @@ def gather(p: Problem, which: int, dst_tokens: int, fill: int = 0) -> np.ndarray
 
 def default_threads() -> int:
     return int(_current().oracle_default_threads())
+
+
+def cache_write(k_new: np.ndarray, v_new: np.ndarray, slot_ids: np.ndarray, k_pool: np.ndarray,
+                v_pool: np.ndarray, k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
+                block_size: int = 16) -> None:
+    """Write this step's rows [T, Hkv, D] into the pools in place (int8 pools: quantize per token/head).
+
+    Every array is modified in place and must be C-contiguous of its declared dtype.
+    """
+    lib = _current()
+    arrays = [k_new, v_new, slot_ids, k_pool, v_pool] + [a for a in (k_scale, v_scale) if a is not None]
+    for a in arrays:
+        if not a.flags.c_contiguous:
+            raise ValueError("cache_write needs C-contiguous arrays")
+    if slot_ids.dtype != np.int64 or k_new.shape != v_new.shape or k_new.ndim != 3:
+        raise ValueError("slot_ids must be int64 [T]; k_new, v_new [T, Hkv, D]")
+    T, Hkv, D = k_new.shape
+    nb, bs, hkv2, d2 = k_pool.shape
+    if (bs, hkv2, d2) != (block_size, Hkv, D) or v_pool.shape != k_pool.shape or slot_ids.shape != (T,):
+        raise ValueError("shape mismatch")
+    kv = _dtype_code(k_pool)
+    if kv == ORC_I8:
+        for sc in (k_scale, v_scale):
+            if sc is None or sc.dtype != np.float32 or sc.shape != (nb, Hkv, bs):
+                raise ValueError("int8 pools need float32 scales [num_blocks, Hkv, block_size]")
+    w = _Write()
+    w.k_new, w.v_new, w.slot_ids = k_new.ctypes.data, v_new.ctypes.data, slot_ids.ctypes.data
+    w.k_pool, w.v_pool = k_pool.ctypes.data, v_pool.ctypes.data
+    w.k_scale = k_scale.ctypes.data if k_scale is not None else None
+    w.v_scale = v_scale.ctypes.data if v_scale is not None else None
+    w.src_dtype, w.kv_dtype = _dtype_code(k_new), kv
+    w.T, w.Hkv, w.D, w.block_size, w.num_blocks = T, Hkv, D, bs, nb
+    _check(lib.oracle_cache_write(ctypes.byref(w)))
+

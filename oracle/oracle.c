@@ -308,3 +308,100 @@ int oracle_gather(const orc_problem* P, int which, void* dst, int64_t dst_tokens
   }
   return ORC_OK;
 }
+
+/*
+ * KV append: the rows of this step's new tokens go into the paged pools
+ * (tiniestgpt notes, "PagedAttention": pool[block][slot][head][dim], the
+ * step's tokens addressed by their slot ids; "Quantization", KV cache
+ * quantization: one scale per token per KV head).
+ *   slot_ids[t] = physical_block * block_size + slot; t is skipped if < 0.
+ *   Float caches take the rows unchanged (src dtype == cache dtype).
+ *   An int8 cache takes, per (token, KV head), scale = max_d |x_d| / 127
+ *   (1 for an all-zero row) and codes rint(x_d / scale) clamped to
+ *   [-127, 127], in binary32 with round-half-even -- the quantizer of the
+ *   input recipe, in the precision its integer codes are decided in.
+ *   Scales are stored [num_blocks][Hkv][block_size].
+ */
+typedef struct {
+  const void* k_new;        /* [T][Hkv][D], src dtype */
+  const void* v_new;        /* same */
+  const int64_t* slot_ids;  /* [T] */
+  void* k_pool;             /* [num_blocks][block_size][Hkv][D], kv dtype */
+  void* v_pool;             /* same */
+  float* k_scale;           /* [num_blocks][Hkv][block_size], int8 only */
+  float* v_scale;           /* same */
+  int32_t src_dtype, kv_dtype;
+  int32_t T, Hkv, D, block_size, num_blocks;
+} orc_write;
+
+/* One element of a float source row as binary32 (bf16 widens exactly). */
+static float src_elem(const void* base, int dtype, size_t i) {
+  if (dtype == ORC_F32) return ((const float*)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+static void write_row(const orc_write* W, const void* src, void* pool, float* scales, int64_t t, int g,
+                      int32_t blk, int32_t slot) {
+  const int D = W->D;
+  const size_t in = ((size_t)t * W->Hkv + g) * (size_t)D;
+  const size_t at = (((size_t)blk * W->block_size + slot) * W->Hkv + g) * (size_t)D;
+  if (W->kv_dtype != ORC_I8) {
+    const size_t esz = W->kv_dtype == ORC_F32 ? 4 : 2;
+    memcpy((char*)pool + at * esz, (const char*)src + in * esz, esz * (size_t)D);
+    return;
+  }
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    float a = fabsf(src_elem(src, W->src_dtype, in + d));
+    if (a > amax) amax = a;
+  }
+#if ORC_MUTANT == 9
+  const float scale = amax > 0.0f ? amax / 128.0f : 1.0f;
+#else
+  const float scale = amax > 0.0f ? amax / 127.0f : 1.0f;
+#endif
+  int8_t* codes = (int8_t*)pool + at;
+  for (int d = 0; d < D; ++d) {
+#if ORC_MUTANT == 10
+    float c = truncf(src_elem(src, W->src_dtype, in + d) / scale);
+#else
+    float c = rintf(src_elem(src, W->src_dtype, in + d) / scale);   /* default rounding: to nearest, ties even */
+#endif
+    if (c > 127.0f) c = 127.0f;
+    if (c < -127.0f) c = -127.0f;
+    codes[d] = (int8_t)c;
+  }
+#if ORC_MUTANT == 11
+  scales[((size_t)blk * W->block_size + slot) * W->Hkv + g] = scale;
+#else
+  scales[((size_t)blk * W->Hkv + g) * W->block_size + slot] = scale;
+#endif
+}
+
+int oracle_cache_write(const orc_write* W) {
+  if (!W || !W->k_new || !W->v_new || !W->slot_ids || !W->k_pool || !W->v_pool) return ORC_ERR_ARG;
+  if (W->T < 0 || W->Hkv < 1 || W->D < 1 || W->block_size < 1 || W->num_blocks < 1) return ORC_ERR_ARG;
+  if (W->src_dtype != ORC_F32 && W->src_dtype != ORC_BF16) return ORC_ERR_ARG;
+  if (W->kv_dtype == ORC_I8) {
+    if (!W->k_scale || !W->v_scale) return ORC_ERR_ARG;
+  } else if (W->kv_dtype != W->src_dtype) {
+    return ORC_ERR_ARG;
+  }
+  const int64_t slots = (int64_t)W->num_blocks * W->block_size;
+  for (int64_t t = 0; t < W->T; ++t)
+    if (W->slot_ids[t] >= slots) return ORC_ERR_DATA;
+  for (int64_t t = 0; t < W->T; ++t) {
+    const int64_t s = W->slot_ids[t];
+    if (s < 0) continue;
+    const int32_t blk = (int32_t)(s / W->block_size), slot = (int32_t)(s % W->block_size);
+    for (int g = 0; g < W->Hkv; ++g) {
+      write_row(W, W->k_new, W->k_pool, W->k_scale, t, g, blk, slot);
+      write_row(W, W->v_new, W->v_pool, W->v_scale, t, g, blk, slot);
+    }
+  }
+  return ORC_OK;
+}
+

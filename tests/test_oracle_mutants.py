@@ -4,8 +4,10 @@ Each mutant is oracle.c rebuilt with ``-DORC_MUTANT=n`` (a wrong GQA head
 map, a window one key too wide, verify rows all placed at the last position,
 slot and head swapped in the pool address, the score scale dropped, the
 softmax left unnormalised, the key scale used for values, one dimension left
-out of the dot product). The pins of test_oracle_pins.py run against it; the
-mutant survives only if every pin still passes.
+out of the dot product; in the KV append, an int8 scale of max/128, codes
+truncated instead of rounded, the scale stored [block][slot][head]). The pins
+of test_oracle_pins.py and test_oracle_append.py run against it; the mutant
+survives only if every pin still passes.
 """
 
 from __future__ import annotations
@@ -16,6 +18,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_append as append_pins
 from tests import test_oracle_pins as pins
 
 MUTANTS = {
@@ -27,6 +30,9 @@ MUTANTS = {
     6: "softmax not normalised",
     7: "key scale applied to values",
     8: "first dimension left out of the dot product",
+    9: "append: int8 scale max over 128",
+    10: "append: int8 codes truncated",
+    11: "append: scale stored block-slot-head",
 }
 
 PIN_CALLS = [
@@ -42,6 +48,13 @@ PIN_CALLS = [
     lambda: [pins.test_golden_closed_forms(p) for p in
              sorted(os.path.join(pins.GOLDEN, f) for f in os.listdir(pins.GOLDEN)
                     if f.endswith(".json") and "k_tokens" in open(os.path.join(pins.GOLDEN, f)).read())],
+    lambda: [append_pins.test_float_append_is_a_copy(k) for k in ("f32", "bf16")],
+    append_pins.test_int8_codes_in_range_with_the_peak_at_127,
+    append_pins.test_int8_zero_row_has_unit_scale_and_zero_codes,
+    append_pins.test_int8_exact_multiples_come_back_exactly,
+    append_pins.test_int8_dequantized_row_is_within_half_a_step,
+    append_pins.test_int8_negation_negates_codes,
+    append_pins.test_int8_scale_of_head_g_lands_at_block_head_slot,
 ]
 
 
