@@ -21,6 +21,11 @@ Prints ONE JSON line on stdout (the run's record); diagnostics go to stderr.
               kernel's own dispatch on the launch stream (hipExtLaunchKernel),
               the same start/end timestamps a kernel trace reports
   cpu_baseline = the fp64 oracle on the host's cores, same workload
+  kv_append = the KV append (pa_cache_write) into the same cache, timed
+              apart from the step: once with the step's own new tokens
+              (B x q_len) and once with a prefill-sized chunk of tokens
+              scattered over the pool, each timed by events that the
+              append kernel's own dispatch stamps
 """
 
 from __future__ import annotations
@@ -102,9 +107,50 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0, help="force the context split count (0: library plan)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the KV append timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
     return ap.parse_args()
+
+
+def measure_append(pa, accounting, torch, np, x, k, v, ks, vs, *, reps: int) -> dict:
+    """Time pa_cache_write for the step's own tokens and for a prefill-sized chunk."""
+    dev = k.device
+    src = "f32" if x.kv_dtype == "f32" else "bf16"
+    tdt = torch.float32 if src == "f32" else torch.bfloat16
+    bs = 16
+    step_slots = []
+    for b in range(x.batch):
+        L = int(x.seq_lens[b])
+        for pos in range(L - x.q_len, L):
+            step_slots.append(int(x.block_table[b, pos // bs]) * bs + pos % bs)
+    rng = np.random.default_rng(1234)
+    chunk = min(16384, x.num_blocks * bs)
+    cases = {"step": np.asarray(step_slots, dtype=np.int64),
+             "chunk": rng.permutation(x.num_blocks * bs)[:chunk].astype(np.int64)}
+    out = {}
+    for name, slots in cases.items():
+        T = int(slots.size)
+        kn = torch.randn((T, x.num_kv_heads, x.head_dim), device=dev).to(tdt)
+        vn = kn if x.v_aliases_k else torch.randn_like(kn, dtype=torch.float32).to(tdt)
+        sl = torch.from_numpy(slots).to(dev)
+        for _ in range(3):
+            pa.cache_write(kn, vn, sl, k, v, ks, vs)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:   # materialise the HIP events before the kernel stamps them
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for a, b in evs:
+            pa.cache_write(kn, vn, sl, k, v, ks, vs, timing=(a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        mean = sum(us) / len(us)
+        nbytes = accounting.append_bytes(T, num_kv_heads=x.num_kv_heads, head_dim=x.head_dim, src_dtype=src,
+                                         kv_dtype=x.kv_dtype, v_shares_k=x.v_aliases_k)
+        out[name] = {"tokens": T, "src_dtype": src, "alg_bytes": nbytes, "us_mean": mean,
+                     "us_p50": us[len(us) // 2], "GBps": nbytes / (mean * 1e-6) / 1e9}
+    return out
 
 
 def main() -> int:
@@ -200,6 +246,13 @@ def main() -> int:
         f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS * 100:.1f}% of peak; "
         f"whole step {ms_per_step * 1e3:.2f} us -> {step_gbs:.0f} GB/s, {value:.4g} queries/s")
 
+    app = None
+    if not args.no_append:
+        app = measure_append(pa, accounting, torch, np, x, k0, v0, ks0, vs0, reps=50)
+        for name, r in app.items():
+            log(f"kv append ({name}): {r['tokens']} tokens {r['src_dtype']} -> {x.kv_dtype}: "
+                f"{r['us_mean']:.2f} us -> {r['GBps']:.0f} GB/s")
+
     if args.calibrate_copy:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -254,6 +307,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, plan)},
         "cpu_baseline": cpu,
+        "kv_append": app,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -178,6 +178,48 @@ int pa_verify(const pa_args* args, pa_stream_t stream);
 int pa_debug_gather(const pa_args* args, int32_t which, void* dst, int64_t dst_tokens,
                     pa_stream_t stream);
 
+/*
+ * KV append: write this step's new key and value rows into the paged pools
+ * (tiniestgpt notes, "PagedAttention": the pool is [block][slot][head][dim]
+ * and a step's tokens are addressed by slot ids; "Quantization", KV cache
+ * quantization, per-token granularity: one scale per token per KV head).
+ */
+typedef struct {
+  const void* k_new;          /* [num_tokens][Hkv][D], src_dtype */
+  const void* v_new;          /* same shape and dtype; must equal k_new when v_pool == k_pool */
+  const int64_t* slot_ids;    /* [num_tokens]: physical_block * block_size + slot. A negative id skips
+                                 the token; an id >= num_blocks * block_size is a precondition
+                                 violation and is never written (the token is skipped) */
+  void* k_pool;               /* [num_blocks][block_size][Hkv][D], kv_dtype */
+  void* v_pool;               /* same; may equal k_pool (then the rows are written once) */
+  float* k_scale;             /* int8 cache only: [num_blocks][Hkv][block_size]; else NULL */
+  float* v_scale;             /* int8 cache only: same; else NULL */
+  int32_t num_tokens;         /* T >= 0 (0 enqueues nothing) */
+  int32_t num_kv_heads;       /* Hkv */
+  int32_t head_dim;           /* D: 64, 128 or 256 */
+  int32_t block_size;         /* 16 */
+  int32_t num_blocks;         /* blocks in each pool */
+  int32_t src_dtype;          /* PA_F32 or PA_BF16 */
+  int32_t kv_dtype;           /* PA_INT8, or the same float type as src_dtype */
+  pa_event_t timing_start;    /* NULL, or a timing-enabled event stamped when the append kernel starts */
+  pa_event_t timing_stop;     /* NULL, or one stamped when it completes (the kernel's own dispatch) */
+} pa_write_args;
+
+/*
+ * Write the rows. A float cache receives them unchanged. An int8 cache
+ * receives, per (token, KV head), scale = max_d |x_d| / 127 (1 for an
+ * all-zero row) and codes rint(x_d / scale) clamped to [-127, 127], in IEEE
+ * binary32 with round-half-even, and the scale at k_scale[block][head][slot].
+ * Tokens whose slots repeat within one call race (one of them wins). All
+ * pointers are device pointers owned by the caller; rows and pools 16-byte
+ * aligned, slot ids and scales 8-byte aligned; asynchronous on stream.
+ * Returns PA_OK, PA_ERR_INVALID_ARG (null pointer with num_tokens > 0,
+ * misaligned pointer, dtype mismatch, aliased pools with different rows),
+ * PA_ERR_UNSUPPORTED
+ * (head_dim / block_size / dtype not built) or PA_ERR_HIP.
+ */
+int pa_cache_write(const pa_write_args* args, pa_stream_t stream);
+
 /* Static description of a return code. */
 const char* pa_strerror(int code);
 

@@ -9,6 +9,8 @@ Layouts (row-major, all tensors on the same GPU):
     q, out       [B, q_len, Hq, D]            float32 or bfloat16
     k_pool, v_pool [num_blocks, 16, Hkv, D]   same dtype as q, or int8
     k_scale, v_scale [num_blocks, Hkv, 16]    float32 (int8 caches)
+    k_new, v_new [T, Hkv, D]                  float32 or bfloat16 (cache_write)
+    slot_ids     [T]                          int64, block * 16 + slot (cache_write)
     block_table  [B, max_blocks_per_seq]      int32
     seq_lens     [B]                          int32, this step's tokens included
 """
@@ -21,8 +23,8 @@ from typing import Optional
 from . import _lib
 from ._lib import PaError  # noqa: F401
 
-__all__ = ["decode", "decode_int8", "verify", "debug_gather", "plan", "workspace_size", "PaError",
-           "library_path"]
+__all__ = ["decode", "decode_int8", "verify", "cache_write", "debug_gather", "plan", "workspace_size",
+           "PaError", "library_path"]
 
 
 def library_path() -> str:
@@ -153,6 +155,49 @@ def decode_int8(out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale,
 def verify(out, q, k_pool, v_pool, block_table, seq_lens, **kw):
     """q_len >= 1 query tokens per sequence, causal among themselves."""
     return _run("pa_verify", out, q, k_pool, v_pool, block_table, seq_lens, **kw)
+
+
+def cache_write(k_new, v_new, slot_ids, k_pool, v_pool, k_scale=None, v_scale=None, *, stream=None,
+                timing=None):
+    """Append this step's K/V rows to the pools at ``slot_ids`` (int8 pools: quantize per token and head).
+
+    Negative slot ids skip their token. Pass the same tensor as ``k_pool`` and
+    ``v_pool`` (and as ``k_new`` and ``v_new``) for a cache whose values are
+    its keys. Asynchronous on ``stream``. ``timing``: optional pair of
+    recorded timing events that the kernel's own dispatch stamps.
+    """
+    torch = _torch()
+    tensors = [t for t in (k_new, v_new, slot_ids, k_pool, v_pool, k_scale, v_scale) if t is not None]
+    dev = k_new.device
+    for t in tensors:
+        _require(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+        _require(t.is_contiguous(), "all tensors must be contiguous")
+    _require(k_new.dim() == 3 and v_new.shape == k_new.shape and v_new.dtype == k_new.dtype,
+             "k_new/v_new must be [T, Hkv, D] of one dtype")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype,
+             "k_pool/v_pool must be [num_blocks, block_size, Hkv, D] of one dtype")
+    T, Hkv, D = k_new.shape
+    nb, bs, hkv2, d2 = k_pool.shape
+    _require((hkv2, d2) == (Hkv, D), "k_new and the pools disagree on Hkv or D")
+    _require(slot_ids.dtype == torch.int64 and tuple(slot_ids.shape) == (T,), "slot_ids must be int64 [T]")
+    for sc in (k_scale, v_scale):
+        if sc is not None:
+            _require(sc.dtype == torch.float32 and tuple(sc.shape) == (nb, Hkv, bs),
+                     "scales must be float32 [nb, Hkv, bs]")
+    w = _lib.PaWriteArgs()
+    w.k_new, w.v_new, w.slot_ids = _ptr(k_new), _ptr(v_new), _ptr(slot_ids)
+    w.k_pool, w.v_pool = _ptr(k_pool), _ptr(v_pool)
+    w.k_scale, w.v_scale = _ptr(k_scale) or None, _ptr(v_scale) or None
+    w.num_tokens, w.num_kv_heads, w.head_dim = T, Hkv, D
+    w.block_size, w.num_blocks = bs, nb
+    w.src_dtype = _dtype_code(k_new, allow_int8=False)
+    w.kv_dtype = _dtype_code(k_pool, allow_int8=True)
+    if timing is not None:
+        w.timing_start = getattr(timing[0], "cuda_event", timing[0])
+        w.timing_stop = getattr(timing[1], "cuda_event", timing[1])
+    lib = _lib.load()
+    _lib.check(lib.pa_cache_write(ctypes.byref(w), ctypes.c_void_p(_stream_handle(stream))))
+    return k_pool
 
 
 def plan(q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None, k_scale=None,

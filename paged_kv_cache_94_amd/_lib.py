@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, 1, 2, 3, 4
 
-EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify",
+EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write",
             "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version")
 
 
@@ -63,6 +63,27 @@ class PaPlanInfo(ctypes.Structure):
     ]
 
 
+class PaWriteArgs(ctypes.Structure):
+    _fields_ = [
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("slot_ids", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("src_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("timing_start", ctypes.c_void_p),
+        ("timing_stop", ctypes.c_void_p),
+    ]
+
+
 class PaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{msg} (code {code})")
@@ -92,6 +113,8 @@ def load(path: str = LIB_PATH):
             fn = getattr(lib, name)
             fn.argtypes = [P, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.pa_cache_write.argtypes = [ctypes.POINTER(PaWriteArgs), ctypes.c_void_p]
+        lib.pa_cache_write.restype = ctypes.c_int
         lib.pa_debug_gather.argtypes = [P, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.pa_debug_gather.restype = ctypes.c_int
         lib.pa_strerror.argtypes = [ctypes.c_int]

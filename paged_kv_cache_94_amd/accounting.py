@@ -90,6 +90,18 @@ def step_flops(seq_lens, *, q_len: int, num_q_heads: int, head_dim: int, window:
     return 4 * head_dim * num_q_heads * total
 
 
+def append_bytes(tokens: int, *, num_kv_heads: int, head_dim: int, src_dtype: str, kv_dtype: str,
+                 v_shares_k: bool) -> int:
+    """Algorithmic HBM bytes of one KV append of `tokens` rows per KV head.
+
+    Each (token, head) row is read once in the source dtype and written once
+    in the cache dtype, for K and for V unless V is K; an int8 cache adds
+    one fp32 scale per row; each token's int64 slot id is read once.
+    """
+    per_row = head_dim * (_ELEM[src_dtype] + _ELEM[kv_dtype]) + (4 if kv_dtype == "int8" else 0)
+    return int(tokens * (8 + num_kv_heads * per_row * (1 if v_shares_k else 2)))
+
+
 def for_inputs(x) -> dict:
     """Byte / flop accounting for a PagedInputs-like object."""
     kw = dict(q_len=x.q_len, num_kv_heads=x.num_kv_heads, head_dim=x.head_dim, kv_dtype=x.kv_dtype,

@@ -13,6 +13,7 @@
 
 #include "pa.h"
 #include "pa_common.h"
+#include "pa_write.h"
 
 namespace {
 
@@ -366,6 +367,59 @@ int pa_debug_gather(const pa_args* a, int32_t which, void* dst, int64_t dst_toke
   hipError_t e = pa::launch_gather(p, a->kv_dtype, a->head_dim, which, dst, dst_tokens,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "gather kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
+  g_last_error.clear();
+  if (!a) return fail(PA_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (a->num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (a->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (a->block_size != pa::kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", a->block_size);
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+  if (a->src_dtype != PA_F32 && a->src_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "src_dtype must be PA_F32 or PA_BF16");
+  if (a->kv_dtype == PA_INT8) {
+    if (a->num_tokens > 0 && (!a->k_scale || !a->v_scale))
+      return fail(PA_ERR_INVALID_ARG, "an int8 cache needs k_scale and v_scale");
+  } else if (a->kv_dtype != a->src_dtype) {
+    return fail(PA_ERR_INVALID_ARG, "a floating-point cache must have the rows' dtype");
+  }
+  if (a->num_tokens == 0) return PA_OK;
+  if (!a->k_new || !a->v_new || !a->slot_ids || !a->k_pool || !a->v_pool)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  for (const void* ptr : {a->k_new, a->v_new, (const void*)a->k_pool, (const void*)a->v_pool})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "rows and pools must be 16-byte aligned");
+  for (const void* ptr : {(const void*)a->slot_ids, (const void*)a->k_scale, (const void*)a->v_scale})
+    if (reinterpret_cast<uintptr_t>(ptr) % 8 != 0)
+      return fail(PA_ERR_INVALID_ARG, "slot ids and scales must be 8-byte aligned");
+  const bool alias = a->v_pool == a->k_pool;
+  if (alias && a->v_new != a->k_new)
+    return fail(PA_ERR_INVALID_ARG, "v_pool is k_pool but v_new is not k_new");
+  if ((int64_t)a->num_tokens * a->num_kv_heads > (int64_t)0x7FFFFFFF * 4)
+    return fail(PA_ERR_UNSUPPORTED, "launch too large");
+  pa::WriteParams p{};
+  p.k_new = a->k_new;
+  p.v_new = a->v_new;
+  p.slot_ids = a->slot_ids;
+  p.k_pool = a->k_pool;
+  p.v_pool = a->v_pool;
+  p.k_scale = a->k_scale;
+  p.v_scale = alias ? a->k_scale : a->v_scale;
+  p.T = a->num_tokens;
+  p.Hkv = a->num_kv_heads;
+  p.num_blocks = a->num_blocks;
+  p.write_v = alias ? 0 : 1;
+  bool supported = false;
+  const hipError_t e = pa::launch_cache_write(p, a->src_dtype, a->kv_dtype, a->head_dim,
+                                              reinterpret_cast<hipStream_t>(stream),
+                                              reinterpret_cast<hipEvent_t>(a->timing_start),
+                                              reinterpret_cast<hipEvent_t>(a->timing_stop), &supported);
+  if (!supported) return fail(PA_ERR_UNSUPPORTED, "no append kernel for these dtypes / head_dim");
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -53,12 +53,14 @@ def test_struct_layout_matches_header():
 int main(void) {
   printf("pa_args.size %zu\n", sizeof(pa_args));
   printf("pa_plan_info.size %zu\n", sizeof(pa_plan_info));
+  printf("pa_write_args.size %zu\n", sizeof(pa_write_args));
   %FIELDS%
   return 0;
 }
 '''
     fields = "".join(f"F(pa_args, {f})" for f, _ in _lib.PaArgs._fields_)
     fields += "".join(f"F(pa_plan_info, {f})" for f, _ in _lib.PaPlanInfo._fields_)
+    fields += "".join(f"F(pa_write_args, {f})" for f, _ in _lib.PaWriteArgs._fields_)
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "layout.c")
         open(c, "w").write(src.replace("%FIELDS%", fields))
@@ -72,6 +74,9 @@ int main(void) {
         assert int(got[f"pa_args.{f}"]) == getattr(_lib.PaArgs, f).offset, f
     for f, _ in _lib.PaPlanInfo._fields_:
         assert int(got[f"pa_plan_info.{f}"]) == getattr(_lib.PaPlanInfo, f).offset, f
+    assert int(got["pa_write_args.size"]) == ctypes.sizeof(_lib.PaWriteArgs)
+    for f, _ in _lib.PaWriteArgs._fields_:
+        assert int(got[f"pa_write_args.{f}"]) == getattr(_lib.PaWriteArgs, f).offset, f
 
 
 def _args(**kw):
@@ -151,6 +156,43 @@ def test_plan_choices(lib):
     # A forced split count is honoured (capped by the blocks a sequence can span).
     assert lib.pa_plan(ctypes.byref(_args(num_splits=3)), ctypes.byref(info)) == 0
     assert info.splits == 3
+
+
+def _wargs(**kw):
+    w = _lib.PaWriteArgs()
+    base = dict(k_new=16, v_new=32, slot_ids=8, k_pool=16, v_pool=32, k_scale=8, v_scale=16, num_tokens=4,
+                num_kv_heads=8, head_dim=128, block_size=16, num_blocks=100, src_dtype=_lib.PA_BF16,
+                kv_dtype=_lib.PA_INT8)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(w, k, v)
+    return w
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_tokens=-1), _lib.PA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(block_size=32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(src_dtype=_lib.PA_INT8), _lib.PA_ERR_UNSUPPORTED),
+    (dict(k_scale=0), _lib.PA_ERR_INVALID_ARG),                       # int8 cache without scales
+    (dict(kv_dtype=_lib.PA_F32), _lib.PA_ERR_INVALID_ARG),            # bf16 rows into an fp32 cache
+    (dict(kv_dtype=_lib.PA_BF16, src_dtype=_lib.PA_F32), _lib.PA_ERR_INVALID_ARG),
+    (dict(slot_ids=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(k_pool=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(v_pool=16), _lib.PA_ERR_INVALID_ARG),                       # aliased pools, distinct rows
+    (dict(k_new=24), _lib.PA_ERR_INVALID_ARG),                        # rows not 16-byte aligned
+    (dict(v_scale=20), _lib.PA_ERR_INVALID_ARG),                      # scales not 8-byte aligned
+])
+def test_cache_write_rejects_bad_arguments(lib, kw, code):
+    assert lib.pa_cache_write(ctypes.byref(_wargs(**kw)), None) == code
+    assert lib.pa_last_error()
+
+
+def test_cache_write_zero_tokens_enqueues_nothing(lib):
+    w = _wargs(num_tokens=0, k_new=0, v_new=0, slot_ids=0, k_pool=0, v_pool=0, k_scale=0, v_scale=0)
+    assert lib.pa_cache_write(ctypes.byref(w), None) == 0
 
 
 def test_zero_sequences_enqueue_nothing(lib):

@@ -59,3 +59,13 @@ def test_shared_kv_and_int8_terms():
                     kv_dtype="int8", seed=1)
     b = accounting.for_inputs(y)
     assert b["alg_bytes"] == 100 * 2 * (128 + 4) * 2 + 2 * 8 * 128 * 2 + 4 * 7 + 4
+
+
+def test_append_bytes_by_hand():
+    # 3 tokens, 2 KV heads, D 128: bf16 rows into an int8 cache move 128*(2+1)+4 bytes per row,
+    # for K and V, plus an 8-byte slot id per token.
+    assert accounting.append_bytes(3, num_kv_heads=2, head_dim=128, src_dtype="bf16", kv_dtype="int8",
+                                   v_shares_k=False) == 3 * (8 + 2 * 2 * (128 * 3 + 4))
+    # A float cache with V sharing K: one copy of each row.
+    assert accounting.append_bytes(5, num_kv_heads=1, head_dim=256, src_dtype="bf16", kv_dtype="bf16",
+                                   v_shares_k=True) == 5 * (8 + 256 * 4)
