@@ -21,6 +21,9 @@ Prints ONE JSON line on stdout (the run's record); diagnostics go to stderr.
               kernel's own dispatch on the launch stream (hipExtLaunchKernel),
               the same start/end timestamps a kernel trace reports
   cpu_baseline = the fp64 oracle on the host's cores, same workload
+  block_allocator = host time of the block allocator's work for one step
+              of the same batch (grow every sequence by its q_len new
+              tokens, then export the int32 block table and lengths)
   kv_append = the KV append (pa_cache_write) into the same cache, timed
               apart from the step: once with the step's own new tokens
               (B x q_len) and once with a prefill-sized chunk of tokens
@@ -153,6 +156,31 @@ def measure_append(pa, accounting, torch, np, x, k, v, ks, vs, *, reps: int) -> 
     return out
 
 
+def measure_allocator(np, x, *, steps: int) -> dict:
+    """Host microseconds per step of the block allocator for this batch (binding included)."""
+    from paged_kv_cache_94_amd.allocator import BlockAllocator
+    bs = 16
+    grow = steps * x.q_len
+    need = int(sum(-(-(int(L) + grow) // bs) for L in x.seq_lens))
+    al = BlockAllocator(need + x.batch, bs, prefix_cache=True)
+    rng = np.random.default_rng(7)
+    ids = list(range(x.batch))
+    for b in ids:
+        al.add(b)
+        al.append(b, int(x.seq_lens[b]), rng.integers(0, 32000, int(x.seq_lens[b])).astype(np.int32))
+    mb = int(-(-(int(x.seq_lens.max()) + grow) // bs))
+    counts = [x.q_len] * x.batch
+    toks = rng.integers(0, 32000, (steps, x.batch * x.q_len)).astype(np.int32)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        al.append_batch(ids, counts, toks[i])
+        al.block_table(ids, mb)
+    us = (time.perf_counter() - t0) / steps * 1e6
+    al.close()
+    return {"sequences": x.batch, "tokens_per_step": x.batch * x.q_len, "us_per_step": us,
+            "what": "append_batch + block_table through the Python binding, host only"}
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -246,6 +274,9 @@ def main() -> int:
         f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS * 100:.1f}% of peak; "
         f"whole step {ms_per_step * 1e3:.2f} us -> {step_gbs:.0f} GB/s, {value:.4g} queries/s")
 
+    alloc = measure_allocator(np, x, steps=200)
+    log(f"block allocator: {alloc['us_per_step']:.1f} us of host time per step for {x.batch} sequences")
+
     app = None
     if not args.no_append:
         app = measure_append(pa, accounting, torch, np, x, k0, v0, ks0, vs0, reps=50)
@@ -308,6 +339,7 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, plan)},
         "cpu_baseline": cpu,
         "kv_append": app,
+        "block_allocator": alloc,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -66,7 +66,8 @@ enum {
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, Hq % Hkv != 0, q_len rule broken, non-finite scale */
   PA_ERR_UNSUPPORTED = 2, /* head_dim / block_size / dtype / group combination not built */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_workspace_size() */
-  PA_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing */
+  PA_ERR_HIP = 4,         /* the HIP runtime reported an error while enqueuing */
+  PA_ERR_NO_BLOCKS = 5    /* block allocator (pa_alloc.h): too few free blocks; nothing changed */
 };
 
 typedef struct {

@@ -10,10 +10,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, 1, 2, 3, 4
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write",
-            "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version")
+            "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version",
+            "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_append", "pa_alloc_append_batch",
+            "pa_alloc_release", "pa_alloc_num_free", "pa_alloc_block_table", "pa_alloc_stats",
+            "pa_alloc_free_queue")
 
 
 class PaArgs(ctypes.Structure):
@@ -121,6 +124,23 @@ def load(path: str = LIB_PATH):
         lib.pa_strerror.restype = ctypes.c_char_p
         lib.pa_last_error.restype = ctypes.c_char_p
         lib.pa_version.restype = ctypes.c_int
+        V, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        alloc_sigs = {
+            "pa_alloc_create": ([I32, I32, I32, ctypes.POINTER(V)], ctypes.c_int),
+            "pa_alloc_destroy": ([V], None),
+            "pa_alloc_add": ([V, I64], ctypes.c_int),
+            "pa_alloc_append": ([V, I64, I32, V, V, V], ctypes.c_int),
+            "pa_alloc_append_batch": ([V, I32, V, V, V, V, V, V], ctypes.c_int),
+            "pa_alloc_release": ([V, I64], ctypes.c_int),
+            "pa_alloc_num_free": ([V], I32),
+            "pa_alloc_block_table": ([V, I32, V, I32, V, V], ctypes.c_int),
+            "pa_alloc_stats": ([V, V, V], ctypes.c_int),
+            "pa_alloc_free_queue": ([V, V, I32, V], ctypes.c_int),
+        }
+        for name, (args, res) in alloc_sigs.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
         _lib = lib
         return lib
 

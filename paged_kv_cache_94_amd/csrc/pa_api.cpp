@@ -13,13 +13,15 @@
 
 #include "pa.h"
 #include "pa_common.h"
+#include "pa_error.h"
 #include "pa_write.h"
 
+namespace pa {
+
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -29,6 +31,16 @@ int fail(int code, const char* fmt, ...) {
   g_last_error = buf;
   return code;
 }
+
+void clear_error() { g_last_error.clear(); }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
 
 // Compute units per device, looked up once per device.
 constexpr int kMaxDevices = 64;
@@ -274,7 +286,7 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
 }
 
 int run(const pa_args* a, pa_stream_t stream, Entry entry) {
-  g_last_error.clear();
+  pa::clear_error();
   int rc = validate(a, entry);
   if (rc) return rc;
   Plan P;
@@ -315,7 +327,7 @@ int run(const pa_args* a, pa_stream_t stream, Entry entry) {
 extern "C" {
 
 size_t pa_workspace_size(const pa_args* a) {
-  g_last_error.clear();
+  pa::clear_error();
   if (validate(a, kAny)) return (size_t)-1;
   Plan P;
   if (make_plan(a, &P)) return (size_t)-1;
@@ -323,7 +335,7 @@ size_t pa_workspace_size(const pa_args* a) {
 }
 
 int pa_plan(const pa_args* a, pa_plan_info* info) {
-  g_last_error.clear();
+  pa::clear_error();
   if (!info) return fail(PA_ERR_INVALID_ARG, "info is NULL");
   int rc = validate(a, kAny);
   if (rc) return rc;
@@ -348,7 +360,7 @@ int pa_decode_int8(const pa_args* a, pa_stream_t stream) { return run(a, stream,
 int pa_verify(const pa_args* a, pa_stream_t stream) { return run(a, stream, kVerify); }
 
 int pa_debug_gather(const pa_args* a, int32_t which, void* dst, int64_t dst_tokens, pa_stream_t stream) {
-  g_last_error.clear();
+  pa::clear_error();
   int rc = validate(a, kGather);
   if (rc) return rc;
   if (which != 0 && which != 1) return fail(PA_ERR_INVALID_ARG, "which must be 0 (keys) or 1 (values)");
@@ -371,7 +383,7 @@ int pa_debug_gather(const pa_args* a, int32_t which, void* dst, int64_t dst_toke
 }
 
 int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
-  g_last_error.clear();
+  pa::clear_error();
   if (!a) return fail(PA_ERR_INVALID_ARG, "args is NULL");
   if (a->num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
   if (a->num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
@@ -430,11 +442,12 @@ const char* pa_strerror(int code) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "not enough free cache blocks";
   }
   return "unknown error";
 }
 
-const char* pa_last_error(void) { return g_last_error.c_str(); }
+const char* pa_last_error(void) { return pa::last_error(); }
 
 int pa_version(void) { return 100; }
 

@@ -17,7 +17,8 @@ import pytest
 from paged_kv_cache_94_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +30,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(pa_\w+)\s*\(", text, flags=re.M)))
 
@@ -201,7 +202,7 @@ def test_zero_sequences_enqueue_nothing(lib):
 
 
 def test_strerror(lib):
-    for code in range(5):
+    for code in range(6):
         assert lib.pa_strerror(code)
     assert lib.pa_version() >= 100
 
