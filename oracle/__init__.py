@@ -54,6 +54,8 @@ class _Problem(ctypes.Structure):
         ("max_blocks", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("scale", ctypes.c_double),
+        ("ring_blocks", ctypes.c_int32),
+        ("head_scales", ctypes.c_int32),
     ]
 
 
@@ -73,6 +75,7 @@ class _Write(ctypes.Structure):
         ("D", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32),
+        ("head_scales", ctypes.c_int32),
     ]
 
 
@@ -156,7 +159,7 @@ class Problem:
     """Keeps the numpy arrays alive while the C struct points into them."""
 
     def __init__(self, q, k_pool, v_pool, block_table, seq_lens, *, q_len, window, scale,
-                 k_scale=None, v_scale=None, block_size=16):
+                 k_scale=None, v_scale=None, block_size=16, ring_blocks=0):
         self.q = np.ascontiguousarray(q)
         self.k_pool = np.ascontiguousarray(k_pool)
         self.v_pool = self.k_pool if v_pool is k_pool else np.ascontiguousarray(v_pool)
@@ -173,9 +176,14 @@ class Problem:
         kv_code = _dtype_code(self.k_pool)
         if _dtype_code(self.v_pool) != kv_code:
             raise ValueError("k and v pools differ in dtype")
+        head_scales = 0
         for sc in (self.k_scale, self.v_scale):
-            if sc is not None and sc.shape != (nb, Hkv, bs):
-                raise ValueError("scales must be [num_blocks, Hkv, block_size]")
+            if sc is not None and sc.shape == (Hkv,):
+                head_scales = 1
+            elif sc is not None and sc.shape != (nb, Hkv, bs):
+                raise ValueError("scales must be [num_blocks, Hkv, block_size] (per token) or [Hkv] (per head)")
+        if self.k_scale is not None and self.v_scale is not None and self.k_scale.shape != self.v_scale.shape:
+            raise ValueError("k and v scales must have the same granularity")
         s = _Problem()
         s.q = self.q.ctypes.data
         s.k_pool = self.k_pool.ctypes.data
@@ -191,6 +199,8 @@ class Problem:
         s.max_blocks = self.block_table.shape[1]
         s.window = int(window)
         s.scale = float(scale)
+        s.ring_blocks = int(ring_blocks)
+        s.head_scales = head_scales
         self.struct = s
         self.shape = (B, q_len, Hq, D)
 
@@ -199,7 +209,7 @@ class Problem:
         """Build from any object with the paged-input attribute names."""
         return cls(x.q, x.k_pool, x.v_pool, x.block_table, x.seq_lens, q_len=x.q_len,
                    window=x.window, scale=x.scale, k_scale=x.k_scale, v_scale=x.v_scale,
-                   block_size=x.block_size)
+                   block_size=x.block_size, ring_blocks=getattr(x, "ring_blocks", 0))
 
 
 def _check(rc: int) -> None:
@@ -222,7 +232,11 @@ def attention(p: Problem, rows: Optional[np.ndarray] = None, threads: int = 0) -
 
 
 def visited_blocks(p: Problem) -> np.ndarray:
-    """[B, max_blocks] int32: 1 where the logical block holds a key some query row sees."""
+    """[B, max_blocks] int32: per table entry, the logical blocks it holds with a key some query row sees.
+
+    A linear table gives 1 for such blocks and 0 elsewhere; in a ring the entry
+    holding both the oldest and the newest keys of the window counts 2.
+    """
     lib = _current()
     vis = np.empty((p.shape[0], p.block_table.shape[1]), dtype=np.int32)
     _check(lib.oracle_visited_blocks(ctypes.byref(p.struct), vis.ctypes.data))
@@ -246,9 +260,11 @@ def default_threads() -> int:
 def cache_write(k_new: np.ndarray, v_new: np.ndarray, slot_ids: np.ndarray, k_pool: np.ndarray,
                 v_pool: np.ndarray, k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
                 block_size: int = 16) -> None:
-    """Write this step's rows [T, Hkv, D] into the pools in place (int8 pools: quantize per token/head).
+    """Write this step's rows [T, Hkv, D] into the pools in place (int8 pools: quantize).
 
-    Every array is modified in place and must be C-contiguous of its declared dtype.
+    int8 pools take scales [num_blocks, Hkv, block_size] (per token: computed
+    and written) or [Hkv] (per head: given, read only). Every array is
+    modified in place and must be C-contiguous of its declared dtype.
     """
     lib = _current()
     arrays = [k_new, v_new, slot_ids, k_pool, v_pool] + [a for a in (k_scale, v_scale) if a is not None]
@@ -262,10 +278,14 @@ def cache_write(k_new: np.ndarray, v_new: np.ndarray, slot_ids: np.ndarray, k_po
     if (bs, hkv2, d2) != (block_size, Hkv, D) or v_pool.shape != k_pool.shape or slot_ids.shape != (T,):
         raise ValueError("shape mismatch")
     kv = _dtype_code(k_pool)
+    head_scales = 0
     if kv == ORC_I8:
         for sc in (k_scale, v_scale):
-            if sc is None or sc.dtype != np.float32 or sc.shape != (nb, Hkv, bs):
-                raise ValueError("int8 pools need float32 scales [num_blocks, Hkv, block_size]")
+            if sc is None or sc.dtype != np.float32 or sc.shape not in ((nb, Hkv, bs), (Hkv,)):
+                raise ValueError("int8 pools need float32 scales [num_blocks, Hkv, block_size] or [Hkv]")
+        if k_scale.shape != v_scale.shape:
+            raise ValueError("k and v scales must have the same granularity")
+        head_scales = int(k_scale.shape == (Hkv,))
     w = _Write()
     w.k_new, w.v_new, w.slot_ids = k_new.ctypes.data, v_new.ctypes.data, slot_ids.ctypes.data
     w.k_pool, w.v_pool = k_pool.ctypes.data, v_pool.ctypes.data
@@ -273,5 +293,6 @@ def cache_write(k_new: np.ndarray, v_new: np.ndarray, slot_ids: np.ndarray, k_po
     w.v_scale = v_scale.ctypes.data if v_scale is not None else None
     w.src_dtype, w.kv_dtype = _dtype_code(k_new), kv
     w.T, w.Hkv, w.D, w.block_size, w.num_blocks = T, Hkv, D, bs, nb
+    w.head_scales = head_scales
     _check(lib.oracle_cache_write(ctypes.byref(w)))
 

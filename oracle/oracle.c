@@ -30,7 +30,14 @@
  *    where L (seq_lens[b]) already counts all q_len new tokens.
  *  - int8 cache (tiniestgpt notes, "Quantization" / KV cache quantization):
  *    codes are gathered first and then dequantized, value = code * scale,
- *    with one scale per token per KV head.
+ *    with one scale per token per KV head (per-token granularity) or one
+ *    per KV head for the whole cache (per-head granularity).
+ *  - Ring cache for window layers (Lab 5, "Ring KV Cache"): a sequence owns
+ *    a fixed ring of ring_blocks blocks and position t lives in ring slot
+ *    t mod (ring_blocks * block_size), so logical block i sits in table
+ *    entry i mod ring_blocks; newer tokens overwrite ones that have left
+ *    the window. The ring must hold window + q_len - 1 tokens so that a
+ *    step's own writes spare every key its queries see.
  *
  * The softmax is taken in the textbook two-pass form: the largest score is
  * subtracted before exponentiating, then the weights are normalised by their
@@ -72,6 +79,8 @@ typedef struct {
   int32_t B, q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks;
   int32_t window;
   double scale;
+  int32_t ring_blocks;      /* 0: block_table row is linear; > 0: a ring of this many entries */
+  int32_t head_scales;      /* int8 only: 0 scales per token [num_blocks][Hkv][block_size]; 1 per head [Hkv] */
 } orc_problem;
 
 /* One stored element, widened to double. bf16 is the upper half of a binary32. */
@@ -94,10 +103,18 @@ static int check_problem(const orc_problem* P) {
   if (P->q_dtype != ORC_F32 && P->q_dtype != ORC_BF16) return ORC_ERR_ARG;
   if (P->kv_dtype != ORC_F32 && P->kv_dtype != ORC_BF16 && P->kv_dtype != ORC_I8) return ORC_ERR_ARG;
   if (P->kv_dtype == ORC_I8 && (!P->k_scale || !P->v_scale)) return ORC_ERR_ARG;
+  if (P->head_scales != 0 && P->head_scales != 1) return ORC_ERR_ARG;
+  if (P->ring_blocks < 0) return ORC_ERR_ARG;
+  if (P->ring_blocks > 0) {
+    if (P->window <= 0 || P->ring_blocks > P->max_blocks) return ORC_ERR_ARG;
+    if ((int64_t)P->ring_blocks * P->block_size < (int64_t)P->window + P->q_len - 1) return ORC_ERR_ARG;
+  }
   for (int b = 0; b < P->B; ++b) {
     int32_t L = P->seq_lens[b];
-    if (L < P->q_len || (int64_t)L > (int64_t)P->max_blocks * P->block_size) return ORC_ERR_DATA;
+    if (L < P->q_len) return ORC_ERR_DATA;
+    if (P->ring_blocks == 0 && (int64_t)L > (int64_t)P->max_blocks * P->block_size) return ORC_ERR_DATA;
     int32_t used = (L + P->block_size - 1) / P->block_size;
+    if (P->ring_blocks > 0 && used > P->ring_blocks) used = P->ring_blocks;
     for (int i = 0; i < used; ++i) {
       int32_t blk = P->block_table[(size_t)b * P->max_blocks + i];
       if (blk < 0 || blk >= P->num_blocks) return ORC_ERR_DATA;
@@ -127,9 +144,20 @@ static void query_span(const orc_problem* P, int b, int t, int32_t* first, int32
   *last = p;
 }
 
+/* Table entry that holds key j: logical block j / block_size, or in a ring the
+ * block of ring slot j mod (ring_blocks * block_size). */
+static int32_t table_entry(const orc_problem* P, int32_t j) {
+  if (P->ring_blocks == 0) return j / P->block_size;
+#if ORC_MUTANT == 12
+  return (j % P->window) / P->block_size;
+#else
+  return (j % (P->ring_blocks * P->block_size)) / P->block_size;
+#endif
+}
+
 /* Element index of (key j, kv head g, dim 0) of sequence b, through the block table. */
 static size_t key_row(const orc_problem* P, int b, int32_t j, int g) {
-  int32_t blk = P->block_table[(size_t)b * P->max_blocks + j / P->block_size];
+  int32_t blk = P->block_table[(size_t)b * P->max_blocks + table_entry(P, j)];
   int32_t slot = j % P->block_size;
 #if ORC_MUTANT == 4
   return (((size_t)blk * P->Hkv + g) * P->block_size + slot) * (size_t)P->D;
@@ -139,10 +167,16 @@ static size_t key_row(const orc_problem* P, int b, int32_t j, int g) {
 }
 
 /* Scale of key j, kv head g of sequence b: one float per (token, head), stored
- * [block][head][slot] so that a block's scales for one head are contiguous. */
+ * [block][head][slot] so that a block's scales for one head are contiguous;
+ * or, per-head granularity, one float per head. */
 static double key_scale(const float* s, const orc_problem* P, int b, int32_t j, int g) {
   if (P->kv_dtype != ORC_I8) return 1.0;
-  int32_t blk = P->block_table[(size_t)b * P->max_blocks + j / P->block_size];
+#if ORC_MUTANT == 13
+  if (P->head_scales) return (double)s[0];
+#else
+  if (P->head_scales) return (double)s[g];
+#endif
+  int32_t blk = P->block_table[(size_t)b * P->max_blocks + table_entry(P, j)];
   int32_t slot = j % P->block_size;
   return (double)s[((size_t)blk * P->Hkv + g) * P->block_size + slot];
 }
@@ -263,20 +297,31 @@ int oracle_default_threads(void) {
 
 /*
  * Logical blocks that hold at least one key visible to at least one query
- * row of the sequence: vis[b][i] = 1 for such blocks, 0 otherwise
- * (vis is [B][max_blocks]). Found by listing every visible key.
+ * row of the sequence, counted per table entry: vis[b][e] = the number of
+ * such logical blocks whose keys table entry e holds (vis is
+ * [B][max_blocks]). A linear table gives 0 or 1; in a ring, the entry that
+ * holds both the oldest and the newest keys of the window counts 2. Found by
+ * listing every visible key.
  */
 int oracle_visited_blocks(const orc_problem* P, int32_t* vis) {
   int rc = check_problem(P);
   if (rc != ORC_OK) return rc;
   if (!vis) return ORC_ERR_ARG;
   memset(vis, 0, sizeof(int32_t) * (size_t)P->B * P->max_blocks);
-  for (int b = 0; b < P->B; ++b)
+  for (int b = 0; b < P->B; ++b) {
+    const int32_t L = P->seq_lens[b];
+    const int32_t nlog = (L + P->block_size - 1) / P->block_size;
+    uint8_t* seen = (uint8_t*)calloc((size_t)nlog, 1);
+    if (!seen) return ORC_ERR_NOMEM;
     for (int t = 0; t < P->q_len; ++t) {
       int32_t lo, p;
       query_span(P, b, t, &lo, &p);
-      for (int32_t j = lo; j <= p; ++j) vis[(size_t)b * P->max_blocks + j / P->block_size] = 1;
+      for (int32_t j = lo; j <= p; ++j) seen[j / P->block_size] = 1;
     }
+    for (int32_t i = 0; i < nlog; ++i)
+      if (seen[i]) vis[(size_t)b * P->max_blocks + table_entry(P, i * P->block_size)] += 1;
+    free(seen);
+  }
   return ORC_OK;
 }
 
@@ -321,6 +366,9 @@ int oracle_gather(const orc_problem* P, int which, void* dst, int64_t dst_tokens
  *   [-127, 127], in binary32 with round-half-even -- the quantizer of the
  *   input recipe, in the precision its integer codes are decided in.
  *   Scales are stored [num_blocks][Hkv][block_size].
+ *   Per-head granularity (tiniestgpt notes: per_head, a smaller scale
+ *   table): the scale of head g is given, s[g]; the codes are
+ *   rint(x_d / s[g]) clamped to [-127, 127] and no scale is written.
  */
 typedef struct {
   const void* k_new;        /* [T][Hkv][D], src dtype */
@@ -332,6 +380,7 @@ typedef struct {
   float* v_scale;           /* same */
   int32_t src_dtype, kv_dtype;
   int32_t T, Hkv, D, block_size, num_blocks;
+  int32_t head_scales;      /* int8 only: 1 -> k_scale / v_scale are [Hkv], given, read only */
 } orc_write;
 
 /* One element of a float source row as binary32 (bf16 widens exactly). */
@@ -353,16 +402,25 @@ static void write_row(const orc_write* W, const void* src, void* pool, float* sc
     memcpy((char*)pool + at * esz, (const char*)src + in * esz, esz * (size_t)D);
     return;
   }
-  float amax = 0.0f;
-  for (int d = 0; d < D; ++d) {
-    float a = fabsf(src_elem(src, W->src_dtype, in + d));
-    if (a > amax) amax = a;
-  }
-#if ORC_MUTANT == 9
-  const float scale = amax > 0.0f ? amax / 128.0f : 1.0f;
+  float scale;
+  if (W->head_scales) {
+#if ORC_MUTANT == 14
+    scale = scales[0];
 #else
-  const float scale = amax > 0.0f ? amax / 127.0f : 1.0f;
+    scale = scales[g];
 #endif
+  } else {
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+      float a = fabsf(src_elem(src, W->src_dtype, in + d));
+      if (a > amax) amax = a;
+    }
+#if ORC_MUTANT == 9
+    scale = amax > 0.0f ? amax / 128.0f : 1.0f;
+#else
+    scale = amax > 0.0f ? amax / 127.0f : 1.0f;
+#endif
+  }
   int8_t* codes = (int8_t*)pool + at;
   for (int d = 0; d < D; ++d) {
 #if ORC_MUTANT == 10
@@ -374,6 +432,7 @@ static void write_row(const orc_write* W, const void* src, void* pool, float* sc
     if (c < -127.0f) c = -127.0f;
     codes[d] = (int8_t)c;
   }
+  if (W->head_scales) return;
 #if ORC_MUTANT == 11
   scales[((size_t)blk * W->block_size + slot) * W->Hkv + g] = scale;
 #else
@@ -385,6 +444,7 @@ int oracle_cache_write(const orc_write* W) {
   if (!W || !W->k_new || !W->v_new || !W->slot_ids || !W->k_pool || !W->v_pool) return ORC_ERR_ARG;
   if (W->T < 0 || W->Hkv < 1 || W->D < 1 || W->block_size < 1 || W->num_blocks < 1) return ORC_ERR_ARG;
   if (W->src_dtype != ORC_F32 && W->src_dtype != ORC_BF16) return ORC_ERR_ARG;
+  if (W->head_scales != 0 && (W->head_scales != 1 || W->kv_dtype != ORC_I8)) return ORC_ERR_ARG;
   if (W->kv_dtype == ORC_I8) {
     if (!W->k_scale || !W->v_scale) return ORC_ERR_ARG;
   } else if (W->kv_dtype != W->src_dtype) {

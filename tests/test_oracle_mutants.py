@@ -5,9 +5,11 @@ map, a window one key too wide, verify rows all placed at the last position,
 slot and head swapped in the pool address, the score scale dropped, the
 softmax left unnormalised, the key scale used for values, one dimension left
 out of the dot product; in the KV append, an int8 scale of max/128, codes
-truncated instead of rounded, the scale stored [block][slot][head]). The pins
-of test_oracle_pins.py and test_oracle_append.py run against it; the mutant
-survives only if every pin still passes.
+truncated instead of rounded, the scale stored [block][slot][head]; a ring
+slot taken modulo the window instead of the ring; head 0's per-head scale
+used for every head, in attention and in the append). The pins of
+test_oracle_pins.py, test_oracle_append.py and test_oracle_ring.py run
+against it; the mutant survives only if every pin still passes.
 """
 
 from __future__ import annotations
@@ -20,6 +22,7 @@ import pytest
 import oracle
 from tests import test_oracle_append as append_pins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_ring as ring_pins
 
 MUTANTS = {
     1: "GQA head map h % Hkv",
@@ -33,6 +36,9 @@ MUTANTS = {
     9: "append: int8 scale max over 128",
     10: "append: int8 codes truncated",
     11: "append: scale stored block-slot-head",
+    12: "ring slot taken modulo the window instead of the ring",
+    13: "per-head scale of head 0 for every head",
+    14: "per-head append quantizes with head 0's scale",
 }
 
 PIN_CALLS = [
@@ -55,6 +61,10 @@ PIN_CALLS = [
     append_pins.test_int8_dequantized_row_is_within_half_a_step,
     append_pins.test_int8_negation_negates_codes,
     append_pins.test_int8_scale_of_head_g_lands_at_block_head_slot,
+    lambda: [ring_pins.test_ring_equals_linear(i) for i in range(len(ring_pins.RING_CASES))],
+    lambda: [ring_pins.test_ring_visits_closed_form(i) for i in range(len(ring_pins.RING_CASES))],
+    lambda: [ring_pins.test_per_head_scales_equal_repeated_per_token_scales(w, q) for w, q in ((0, 1), (20, 1))],
+    ring_pins.test_per_head_append_codes,
 ]
 
 

@@ -78,6 +78,14 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def _encode_int8_per_head(x: np.ndarray):
+    """Symmetric int8 codes with one float32 scale per KV head (axis 2) over the whole pool."""
+    amax = np.abs(x).max(axis=(0, 1, 3))
+    scale = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    codes = np.rint(x / scale[None, None, :, None]).clip(-127, 127).astype(np.int8)
+    return codes, scale
+
+
 def _encode_int8_per_token(x: np.ndarray):
     """Symmetric int8 codes with one float32 scale per row of the last axis."""
     amax = np.abs(x).max(axis=-1)
@@ -106,6 +114,7 @@ class PagedInputs:
     block_size: int = BLOCK_SIZE
     name: str = "custom"
     seed: int = 0
+    ring_blocks: int = 0  # > 0: each table row is a ring of this many blocks (window layers)
 
     @property
     def batch(self) -> int:
@@ -164,12 +173,14 @@ def _standard_normal(rng: np.random.Generator, shape) -> np.ndarray:
     return out
 
 
-def _draw_kv(rng: np.random.Generator, shape, kv_dtype: str):
+def _draw_kv(rng: np.random.Generator, shape, kv_dtype: str, head_scales: bool = False):
     x = _standard_normal(rng, shape)
     if kv_dtype == "f32":
         return x, None
     if kv_dtype == "bf16":
         return f32_to_bf16_bits(x), None
+    if kv_dtype == "int8" and head_scales:
+        return _encode_int8_per_head(x)                   # scale [Hkv]
     if kv_dtype == "int8":
         codes, scale = _encode_int8_per_token(x)          # scale [blocks, 16, Hkv]
         return codes, np.ascontiguousarray(scale.transpose(0, 2, 1))
@@ -177,10 +188,14 @@ def _draw_kv(rng: np.random.Generator, shape, kv_dtype: str):
 
 
 def _poison_slots(pool: np.ndarray, scale: Optional[np.ndarray], blocks, slots, kv_dtype: str):
-    """Overwrite pool[blocks, slots] (all heads, all dims) with NaN, or NaN scales for int8."""
+    """Overwrite pool[blocks, slots] (all heads, all dims) with NaN, or NaN scales for int8.
+
+    Per-head int8 scales are shared by every token, so there only the codes
+    are poisoned (to 127, which moves any score that reads them)."""
     if kv_dtype == "int8":
         pool[blocks, slots] = 127
-        scale[blocks, :, slots] = np.nan
+        if scale.ndim == 3:
+            scale[blocks, :, slots] = np.nan
     elif kv_dtype == "bf16":
         pool[blocks, slots] = _BF16_QNAN
     else:
@@ -192,12 +207,17 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
                 scale: Optional[float] = None, seed: int = 0, rng: Optional[np.random.Generator] = None,
                 num_blocks: Optional[int] = None, pool_slack: float = 1.1,
                 max_blocks: Optional[int] = None, alias_v: bool = False, poison: bool = False,
-                name: str = "custom") -> PagedInputs:
+                name: str = "custom", ring: bool = False, head_scales: bool = False) -> PagedInputs:
     """Build one seeded paged-cache problem.
 
     ``seq_lens`` counts cached tokens including this step's ``q_len`` queries.
     Physical blocks are handed to sequences consecutively from one random
     permutation of the pool ids.
+
+    ``ring`` (window layers only): each sequence owns a ring of
+    R = ceil((window + q_len - 1) / 16) blocks and position t lives in ring
+    slot t mod 16R (Lab 5, "Ring KV Cache"); the table has R columns.
+    ``head_scales`` (int8 only): one scale per KV head for the whole pool.
     """
     if rng is None:
         rng = np.random.default_rng(seed)
@@ -209,6 +229,16 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
     B = int(lens.size)
     bs = BLOCK_SIZE
     nblk = (lens + bs - 1) // bs
+    ring_blocks = 0
+    if ring:
+        if window <= 0:
+            raise ValueError("a ring cache needs a window")
+        ring_blocks = -(-(window + q_len - 1) // bs)
+        nblk = np.minimum(nblk, ring_blocks)
+        if max_blocks is None:
+            max_blocks = ring_blocks
+    if head_scales and kv_dtype != "int8":
+        raise ValueError("per-head scales are for int8 caches")
     need = int(nblk.sum())
     if num_blocks is None:
         num_blocks = max(need + 1, int(math.ceil(pool_slack * need)))
@@ -240,11 +270,11 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
     del qf
 
     shape = (num_blocks, bs, num_kv_heads, head_dim)
-    k_pool, k_scale = _draw_kv(rng, shape, kv_dtype)
+    k_pool, k_scale = _draw_kv(rng, shape, kv_dtype, head_scales)
     if alias_v:
         v_pool, v_scale = k_pool, k_scale
     else:
-        v_pool, v_scale = _draw_kv(rng, shape, kv_dtype)
+        v_pool, v_scale = _draw_kv(rng, shape, kv_dtype, head_scales)
 
     if poison:
         pools = [(k_pool, k_scale)] if alias_v else [(k_pool, k_scale), (v_pool, v_scale)]
@@ -254,6 +284,9 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
             table[b, n:] = poison_block
         for pool, sc in pools:
             _poison_slots(pool, sc, unused, slice(None), kv_dtype)
+            if ring_blocks:
+                _poison_ring(pool, sc, table, lens, nblk, ring_blocks, q_len, window, kv_dtype)
+                continue
             for b in range(B):
                 L = int(lens[b])
                 n = int(nblk[b])
@@ -272,7 +305,25 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
                        block_table=table, seq_lens=lens.astype(np.int32), q_len=q_len,
                        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                        window=int(window), scale=float(scale), q_dtype=q_dtype, kv_dtype=kv_dtype,
-                       name=name, seed=seed)
+                       name=name, seed=seed, ring_blocks=ring_blocks)
+
+
+def _poison_ring(pool, sc, table, lens, nblk, R, q_len, window, kv_dtype):
+    """Poison every ring slot that holds no key a query of the step may see.
+
+    Ring slot e*16 + s holds the newest position t <= L-1 with t = e*16 + s
+    (mod 16R); it is visible when t >= L - q_len - window + 1 (and t >= 0)."""
+    bs = BLOCK_SIZE
+    C = R * bs
+    for b in range(table.shape[0]):
+        L = int(lens[b])
+        lo = max(0, L - q_len - window + 1)
+        for e in range(int(nblk[b])):
+            r = e * bs + np.arange(bs)
+            t = (L - 1) - ((L - 1 - r) % C)
+            bad = np.nonzero((t < lo) | (t < 0))[0]
+            if bad.size:
+                _poison_slots(pool, sc, int(table[b, e]), bad, kv_dtype)
 
 
 # The five workloads. Each entry fixes the shape; lengths are drawn from the
@@ -307,11 +358,14 @@ def _draw_lens(spec: str, B: int, rng: np.random.Generator) -> np.ndarray:
     raise ValueError(spec)
 
 
-def make_config(idx: int, *, poison: bool = False, batch: Optional[int] = None) -> PagedInputs:
+def make_config(idx: int, *, poison: bool = False, batch: Optional[int] = None, ring: bool = False,
+                head_scales: bool = False) -> PagedInputs:
     """One of the five named workloads, seeded with its own number.
 
     ``batch`` keeps only the first ``batch`` sequences of the drawn length
     list (a smaller problem with the same length distribution and pool rule).
+    ``ring`` lays a window layer's cache out as rings; ``head_scales`` gives
+    an int8 cache one scale per KV head.
     """
     c = CONFIGS[idx]
     rng = np.random.default_rng(idx)
@@ -319,9 +373,10 @@ def make_config(idx: int, *, poison: bool = False, batch: Optional[int] = None) 
     if batch is not None:
         lens = lens[:batch]
     num_blocks = c.get("num_blocks")
-    max_blocks = (c["max_len"] + BLOCK_SIZE - 1) // BLOCK_SIZE
+    max_blocks = None if ring else (c["max_len"] + BLOCK_SIZE - 1) // BLOCK_SIZE
+    name = c["name"] + ("-ring" if ring else "") + ("-headscale" if head_scales else "")
     return make_inputs(lens, q_len=c["q_len"], num_q_heads=c["Hq"], num_kv_heads=c["Hkv"],
                        head_dim=c["D"], q_dtype=c["q_dtype"], kv_dtype=c["kv_dtype"],
                        window=c["window"], rng=rng, num_blocks=num_blocks,
                        max_blocks=max_blocks, alias_v=c.get("alias_v", False), poison=poison,
-                       name=c["name"], seed=idx)
+                       name=name, seed=idx, ring=ring, head_scales=head_scales)
