@@ -111,6 +111,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the KV append timing")
+    ap.add_argument("--ring", action="store_true",
+                    help="window workloads: lay each sequence's cache out as a ring of window/16 blocks")
+    ap.add_argument("--head-scales", action="store_true", help="int8 workload: one scale per KV head")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
     return ap.parse_args()
@@ -123,10 +126,12 @@ def measure_append(pa, accounting, torch, np, x, k, v, ks, vs, *, reps: int) -> 
     tdt = torch.float32 if src == "f32" else torch.bfloat16
     bs = 16
     step_slots = []
+    R = x.ring_blocks
     for b in range(x.batch):
         L = int(x.seq_lens[b])
         for pos in range(L - x.q_len, L):
-            step_slots.append(int(x.block_table[b, pos // bs]) * bs + pos % bs)
+            entry = (pos // bs) % R if R else pos // bs
+            step_slots.append(int(x.block_table[b, entry]) * bs + pos % bs)
     rng = np.random.default_rng(1234)
     chunk = min(16384, x.num_blocks * bs)
     cases = {"step": np.asarray(step_slots, dtype=np.int64),
@@ -166,9 +171,9 @@ def measure_allocator(np, x, *, steps: int) -> dict:
     rng = np.random.default_rng(7)
     ids = list(range(x.batch))
     for b in ids:
-        al.add(b)
+        al.add(b, x.ring_blocks)
         al.append(b, int(x.seq_lens[b]), rng.integers(0, 32000, int(x.seq_lens[b])).astype(np.int32))
-    mb = int(-(-(int(x.seq_lens.max()) + grow) // bs))
+    mb = x.ring_blocks or int(-(-(int(x.seq_lens.max()) + grow) // bs))
     counts = [x.q_len] * x.batch
     toks = rng.integers(0, 32000, (steps, x.batch * x.q_len)).astype(np.int32)
     t0 = time.perf_counter()
@@ -178,7 +183,8 @@ def measure_allocator(np, x, *, steps: int) -> dict:
     us = (time.perf_counter() - t0) / steps * 1e6
     al.close()
     return {"sequences": x.batch, "tokens_per_step": x.batch * x.q_len, "us_per_step": us,
-            "what": "append_batch + block_table through the Python binding, host only"}
+            "what": "append_batch + block_table through the Python (ctypes) binding, host only; "
+                    "the binding's call overhead dominates"}
 
 
 def main() -> int:
@@ -206,7 +212,7 @@ def main() -> int:
 
     cfg = CONFIGS[args.config]
     t0 = time.time()
-    x = make_config(args.config)
+    x = make_config(args.config, ring=args.ring, head_scales=args.head_scales)
     acct = accounting.for_inputs(x)
     log(f"workload {x.name}: B={x.batch} q_len={x.q_len} Hq={x.num_q_heads} Hkv={x.num_kv_heads} "
         f"D={x.head_dim} window={x.window} kv={x.kv_dtype} pool={x.num_blocks} blocks "
@@ -240,9 +246,10 @@ def main() -> int:
             vs = None if vs0 is None else torch.empty_like(vs0).copy_(vs0)
             table = table0.clone()
         calls.append(pa.Prepared(entry, out, q, k, v, table, lens, window=x.window, scale=x.scale,
-                                 max_seq_len=x.max_seq_len, k_scale=ks, v_scale=vs, num_splits=args.num_splits))
+                                 max_seq_len=x.max_seq_len, k_scale=ks, v_scale=vs, num_splits=args.num_splits,
+                                 ring_blocks=x.ring_blocks))
     plan = pa.plan(q, k0, v0, table0, lens, window=x.window, scale=x.scale, max_seq_len=x.max_seq_len,
-                   k_scale=ks0, v_scale=vs0, num_splits=args.num_splits)
+                   k_scale=ks0, v_scale=vs0, num_splits=args.num_splits, ring_blocks=x.ring_blocks)
     log(f"plan: {plan}; {copies} cache copies rotated")
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -336,7 +343,8 @@ def main() -> int:
             "splits": plan["splits"],
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, plan)},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if (args.ring or args.head_scales) else measured_traffic(args.config, plan)},
         "cpu_baseline": cpu,
         "kv_append": app,
         "block_allocator": alloc,

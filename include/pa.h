@@ -76,9 +76,11 @@ typedef struct {
   const void* k_pool;         /* [num_blocks][block_size][Hkv][D], kv_dtype */
   const void* v_pool;         /* same shape; may equal k_pool (keys and values shared, read once) */
   const float* k_scale;       /* int8 cache only: [num_blocks][Hkv][block_size], one fp32 per (token,
-                                 KV head), a block's 16 scales of one head contiguous; else NULL */
+                                 KV head), a block's 16 scales of one head contiguous; or [Hkv],
+                                 one per KV head, when scale_per_head is 1; else NULL */
   const float* v_scale;       /* int8 cache only: same shape; else NULL */
-  const int32_t* block_table; /* [B][max_blocks_per_seq] physical block ids */
+  const int32_t* block_table; /* [B][max_blocks_per_seq] physical block ids; with ring_blocks > 0 each
+                                 row's first ring_blocks entries form the sequence's ring */
   const int32_t* seq_lens;    /* [B] cached tokens per sequence, this step's q_len tokens included */
   int32_t num_seqs;           /* B >= 0 (B == 0 enqueues nothing) */
   int32_t q_len;              /* query tokens per sequence; query t sits at position seq_len - q_len + t */
@@ -88,7 +90,8 @@ typedef struct {
   int32_t block_size;         /* tokens per cache block: 16 */
   int32_t num_blocks;         /* blocks in each pool */
   int32_t max_blocks_per_seq; /* row length of block_table */
-  int32_t max_seq_len;        /* host-side upper bound on seq_lens[]; sizes the launch, no device sync */
+  int32_t max_seq_len;        /* host-side upper bound on seq_lens[]; sizes the launch, no device sync
+                                 (at most max_blocks_per_seq * block_size unless ring_blocks > 0) */
   int32_t window;             /* <= 0: every earlier key; > 0: the W most recent keys */
   float scale;                /* multiplies q.k before the softmax (1/sqrt(D) for standard attention) */
   int32_t q_dtype;            /* PA_F32 or PA_BF16 (also the output type) */
@@ -109,6 +112,16 @@ typedef struct {
   pa_event_t timing_stop;     /* NULL, or a timing-enabled event: stamped when it completes (before any combine
                                  kernel). Both come from the kernel's own dispatch (hipExtLaunchKernel), so
                                  their interval is the kernel's execution time with no marker overhead. */
+  int32_t ring_blocks;        /* 0: logical block i of a sequence is table entry i. > 0: ring cache for a
+                                 window layer (Lab 5, "Ring KV Cache"): position t lives in ring slot
+                                 t mod (ring_blocks * block_size), so logical block i is entry
+                                 i mod ring_blocks. Needs window > 0, ring_blocks <= max_blocks_per_seq and
+                                 ring_blocks * block_size >= window + q_len - 1 (a step's own keys must
+                                 not overwrite keys its queries see). debug_visits then counts per
+                                 table entry. */
+  int32_t scale_per_head;     /* int8 caches: 0 scales per token (k_scale layout above); 1 one scale
+                                 per KV head for the whole cache, k_scale / v_scale [Hkv] (tiniestgpt
+                                 notes, "Quantization": per_head granularity, a smaller scale table) */
 } pa_args;
 
 /* Plan the library would use for these arguments (informational). */
@@ -204,6 +217,9 @@ typedef struct {
   int32_t kv_dtype;           /* PA_INT8, or the same float type as src_dtype */
   pa_event_t timing_start;    /* NULL, or a timing-enabled event stamped when the append kernel starts */
   pa_event_t timing_stop;     /* NULL, or one stamped when it completes (the kernel's own dispatch) */
+  int32_t scale_per_head;     /* int8 cache: 0 per-token scales, computed and written as above; 1 the
+                                 given per-head scales k_scale / v_scale [Hkv] (read only): codes are
+                                 rint(x / s[head]) clamped to [-127, 127]. Scales must be finite, > 0. */
 } pa_write_args;
 
 /*

@@ -63,6 +63,17 @@ void pa_alloc_destroy(pa_allocator* a);
  * id is live. */
 int pa_alloc_add(pa_allocator* a, int64_t seq_id);
 
+/* Start an empty ring sequence for a window layer (Lab 5, "Ring KV Cache"):
+ * it takes blocks on demand until it holds ring_blocks >= 1 of them, after
+ * which position t lives in slot t mod (ring_blocks * block_size) of its
+ * blocks, overwriting the token ring_blocks * block_size positions earlier.
+ * Its blocks are rewritten, so it never registers or matches a prefix. A
+ * position that a later token of the same append overwrites gets slot id -1,
+ * so pa_cache_write never writes one slot twice in a call. Its block table (ring_blocks entries once full) goes to the attention calls
+ * with pa_args.ring_blocks = ring_blocks. PA_ERR_INVALID_ARG if the id is
+ * live or ring_blocks < 1. */
+int pa_alloc_add_ring(pa_allocator* a, int64_t seq_id, int32_t ring_blocks);
+
 /* Grow sequence seq_id by n >= 0 tokens. tokens: NULL, or the n token ids
  * (needed for prefix caching; a sequence once grown without ids is never
  * registered or matched again). slot_ids: n outputs, the slot of each new

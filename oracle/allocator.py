@@ -33,6 +33,12 @@ Readings where the notes leave a choice open (the library makes the same ones):
 * A call either succeeds whole or changes nothing.
 * Positions whose keys and values are already cached get slot id -1, so the
   KV append skips them.
+* A ring sequence (Lab 5, "Ring KV Cache", for window layers) takes blocks
+  until it holds R of them; position t then lives in its block
+  (t / block_size) mod R, i.e. slot t mod (R * block_size), overwriting the
+  token R * block_size positions earlier. Its blocks are rewritten, so it
+  never registers or matches a prefix. A position that a later token of the
+  same call overwrites gets slot id -1 (one write per slot and call).
 """
 
 from __future__ import annotations
@@ -76,6 +82,7 @@ class _Seq:
         self.tail: List[int] = []  # token ids of the incomplete last block
         self.hashable = True       # every token so far came with its id
         self.matching = True       # every block so far was a prefix hit
+        self.ring = 0              # > 0: a ring of this many blocks
 
 
 class RefAllocator:
@@ -116,10 +123,17 @@ class RefAllocator:
 
     # -- updates -------------------------------------------------------------------------------
 
-    def add(self, sid: int) -> None:
+    def add(self, sid: int, ring_blocks: int = 0) -> None:
         if sid in self.seqs:
             raise AllocError("sequence exists")
-        self.seqs[sid] = _Seq()
+        if ring_blocks < 0:
+            raise AllocError("bad ring size")
+        s = _Seq()
+        if ring_blocks:
+            s.ring = ring_blocks
+            s.hashable = False
+            s.matching = False
+        self.seqs[sid] = s
 
     def append(self, sid: int, n: int, tokens: Optional[Sequence[int]] = None) -> Tuple[List[int], int]:
         """Grow sequence `sid` by n tokens. Returns (slot id per token, -1 if cached; cached count)."""
@@ -145,6 +159,8 @@ class RefAllocator:
                 parent = h
         cached_tokens = len(hits) * bs
         total_blocks = -(-(s.length + n) // bs)
+        if s.ring:
+            total_blocks = min(total_blocks, s.ring)
         fresh = total_blocks - len(s.blocks) - len(hits)
         from_queue = fresh + sum(1 for b, _ in hits if self.ref[b] == 0)
         if from_queue > len(self.free):
@@ -166,16 +182,19 @@ class RefAllocator:
             s.hashable = False
         if n > cached_tokens:
             s.matching = False
+        final = s.length + (n - cached_tokens)
         for i in range(cached_tokens, n):
             pos = s.length
-            if pos % bs == 0:
+            entry = (pos // bs) % s.ring if s.ring else pos // bs
+            if entry == len(s.blocks):
                 b = self.free.pop(0)
                 if self.hash_of[b] is not None:
                     del self.cached[self.hash_of[b]]
                     self.hash_of[b] = None
                 self.ref[b] = 1
                 s.blocks.append(b)
-            slots.append(s.blocks[pos // bs] * bs + pos % bs)
+            overwritten = s.ring and pos < final - s.ring * bs
+            slots.append(-1 if overwritten else s.blocks[entry] * bs + pos % bs)
             s.length += 1
             if s.hashable:
                 s.tail.append(int(tokens[i]))

@@ -8,10 +8,12 @@ and allocates the split workspace through PyTorch's caching allocator.
 Layouts (row-major, all tensors on the same GPU):
     q, out       [B, q_len, Hq, D]            float32 or bfloat16
     k_pool, v_pool [num_blocks, 16, Hkv, D]   same dtype as q, or int8
-    k_scale, v_scale [num_blocks, Hkv, 16]    float32 (int8 caches)
+    k_scale, v_scale [num_blocks, Hkv, 16]    float32 (int8 caches, one scale per token and head)
+                     or [Hkv]                 float32 (int8 caches, one scale per head)
     k_new, v_new [T, Hkv, D]                  float32 or bfloat16 (cache_write)
     slot_ids     [T]                          int64, block * 16 + slot (cache_write)
-    block_table  [B, max_blocks_per_seq]      int32
+    block_table  [B, max_blocks_per_seq]      int32 (ring_blocks > 0: each row's first
+                                              ring_blocks entries are the sequence's ring)
     seq_lens     [B]                          int32, this step's tokens included
 """
 
@@ -57,7 +59,8 @@ def _require(cond: bool, msg: str) -> None:
 
 
 def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, scale: Optional[float],
-                max_seq_len: Optional[int], k_scale, v_scale, num_splits: int, debug_visits) -> _lib.PaArgs:
+                max_seq_len: Optional[int], k_scale, v_scale, num_splits: int, debug_visits,
+                ring_blocks: int = 0) -> _lib.PaArgs:
     torch = _torch()
     tensors = [t for t in (out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, debug_visits)
                if t is not None]
@@ -74,9 +77,14 @@ def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, s
     nb, bs, Hkv, Dk = k_pool.shape
     _require(Dk == D, "head_dim mismatch between q and the cache")
     _require(block_table.shape[0] == B and seq_lens.shape[0] == B, "batch mismatch")
+    per_head = 0
     for s in (k_scale, v_scale):
         if s is not None:
-            _require(s.dtype == torch.float32 and tuple(s.shape) == (nb, Hkv, bs), "scales must be float32 [nb, Hkv, bs]")
+            _require(s.dtype == torch.float32 and tuple(s.shape) in ((nb, Hkv, bs), (Hkv,)),
+                     "scales must be float32 [nb, Hkv, bs] (per token) or [Hkv] (per head)")
+            per_head = int(tuple(s.shape) == (Hkv,))
+    if k_scale is not None and v_scale is not None:
+        _require(k_scale.shape == v_scale.shape, "k_scale and v_scale must have one granularity")
     if debug_visits is not None:
         _require(debug_visits.dtype == torch.int32 and tuple(debug_visits.shape) == (B, Hkv, block_table.shape[1]),
                  "debug_visits must be int32 [B, Hkv, max_blocks]")
@@ -97,6 +105,8 @@ def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, s
     a.kv_dtype = _dtype_code(k_pool, allow_int8=True)
     a.num_splits = int(num_splits)
     a.debug_visits = _ptr(debug_visits) or None
+    a.ring_blocks = int(ring_blocks)
+    a.scale_per_head = per_head
     return a
 
 
@@ -126,11 +136,11 @@ def _attach_workspace(a: _lib.PaArgs, workspace, device) -> object:
 
 def _run(entry: str, out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None,
          k_scale=None, v_scale=None, num_splits=0, workspace=None, debug_visits=None, stream=None,
-         timing=None):
+         timing=None, ring_blocks=0):
     lib = _lib.load()
     a = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
                     max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
-                    debug_visits=debug_visits)
+                    debug_visits=debug_visits, ring_blocks=ring_blocks)
     ws = _attach_workspace(a, workspace, q.device)
     if timing is not None:
         a.timing_start = ctypes.c_void_p(timing[0].cuda_event if hasattr(timing[0], "cuda_event") else timing[0])
@@ -180,10 +190,12 @@ def cache_write(k_new, v_new, slot_ids, k_pool, v_pool, k_scale=None, v_scale=No
     nb, bs, hkv2, d2 = k_pool.shape
     _require((hkv2, d2) == (Hkv, D), "k_new and the pools disagree on Hkv or D")
     _require(slot_ids.dtype == torch.int64 and tuple(slot_ids.shape) == (T,), "slot_ids must be int64 [T]")
+    per_head = 0
     for sc in (k_scale, v_scale):
         if sc is not None:
-            _require(sc.dtype == torch.float32 and tuple(sc.shape) == (nb, Hkv, bs),
-                     "scales must be float32 [nb, Hkv, bs]")
+            _require(sc.dtype == torch.float32 and tuple(sc.shape) in ((nb, Hkv, bs), (Hkv,)),
+                     "scales must be float32 [nb, Hkv, bs] (per token) or [Hkv] (per head)")
+            per_head = int(tuple(sc.shape) == (Hkv,))
     w = _lib.PaWriteArgs()
     w.k_new, w.v_new, w.slot_ids = _ptr(k_new), _ptr(v_new), _ptr(slot_ids)
     w.k_pool, w.v_pool = _ptr(k_pool), _ptr(v_pool)
@@ -192,6 +204,7 @@ def cache_write(k_new, v_new, slot_ids, k_pool, v_pool, k_scale=None, v_scale=No
     w.block_size, w.num_blocks = bs, nb
     w.src_dtype = _dtype_code(k_new, allow_int8=False)
     w.kv_dtype = _dtype_code(k_pool, allow_int8=True)
+    w.scale_per_head = per_head
     if timing is not None:
         w.timing_start = getattr(timing[0], "cuda_event", timing[0])
         w.timing_stop = getattr(timing[1], "cuda_event", timing[1])
@@ -201,12 +214,12 @@ def cache_write(k_new, v_new, slot_ids, k_pool, v_pool, k_scale=None, v_scale=No
 
 
 def plan(q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None, k_scale=None,
-         v_scale=None, num_splits=0) -> dict:
+         v_scale=None, num_splits=0, ring_blocks=0) -> dict:
     """The launch plan libpa would use for these tensors (no launch)."""
     lib = _lib.load()
     a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
                     max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
-                    debug_visits=None)
+                    debug_visits=None, ring_blocks=ring_blocks)
     info = _lib.PaPlanInfo()
     _lib.check(lib.pa_plan(ctypes.byref(a), ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in info._fields_}
@@ -217,13 +230,14 @@ def workspace_size(q, k_pool, v_pool, block_table, seq_lens, **kw) -> int:
 
 
 def debug_gather(which: int, dst, q, k_pool, v_pool, block_table, seq_lens, *, window=0, max_seq_len=None,
-                 stream=None):
+                 stream=None, ring_blocks=0):
     """Raw cache rows the kernels load, in logical key order: dst [B, dst_tokens, Hkv, D]."""
     lib = _lib.load()
     _require(dst.is_cuda and dst.is_contiguous() and dst.dtype == k_pool.dtype and dst.dim() == 4,
              "dst must be a contiguous [B, dst_tokens, Hkv, D] tensor of the cache dtype")
     a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=1.0,
-                    max_seq_len=max_seq_len, k_scale=None, v_scale=None, num_splits=0, debug_visits=None)
+                    max_seq_len=max_seq_len, k_scale=None, v_scale=None, num_splits=0, debug_visits=None,
+                    ring_blocks=ring_blocks)
     rc = lib.pa_debug_gather(ctypes.byref(a), int(which), ctypes.c_void_p(dst.data_ptr()), dst.shape[1],
                              ctypes.c_void_p(_stream_handle(stream)))
     _lib.check(rc)
@@ -241,13 +255,13 @@ class Prepared:
     """
 
     def __init__(self, entry: str, out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None,
-                 max_seq_len=None, k_scale=None, v_scale=None, num_splits=0, workspace=None):
+                 max_seq_len=None, k_scale=None, v_scale=None, num_splits=0, workspace=None, ring_blocks=0):
         self._lib = _lib.load()
         self._fn = getattr(self._lib, {"decode": "pa_decode", "decode_int8": "pa_decode_int8",
                                        "verify": "pa_verify"}[entry])
         self.args = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
                                 max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale,
-                                num_splits=num_splits, debug_visits=None)
+                                num_splits=num_splits, debug_visits=None, ring_blocks=ring_blocks)
         self.workspace = _attach_workspace(self.args, workspace, q.device)
         self._keep = (out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale)
 

@@ -14,7 +14,8 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_
 
 EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write",
             "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version",
-            "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_append", "pa_alloc_append_batch",
+            "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_add_ring", "pa_alloc_append",
+            "pa_alloc_append_batch",
             "pa_alloc_release", "pa_alloc_num_free", "pa_alloc_block_table", "pa_alloc_stats",
             "pa_alloc_free_queue")
 
@@ -48,6 +49,8 @@ class PaArgs(ctypes.Structure):
         ("debug_visits", ctypes.c_void_p),
         ("timing_start", ctypes.c_void_p),
         ("timing_stop", ctypes.c_void_p),
+        ("ring_blocks", ctypes.c_int32),
+        ("scale_per_head", ctypes.c_int32),
     ]
 
 
@@ -84,6 +87,7 @@ class PaWriteArgs(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("timing_start", ctypes.c_void_p),
         ("timing_stop", ctypes.c_void_p),
+        ("scale_per_head", ctypes.c_int32),
     ]
 
 
@@ -129,6 +133,7 @@ def load(path: str = LIB_PATH):
             "pa_alloc_create": ([I32, I32, I32, ctypes.POINTER(V)], ctypes.c_int),
             "pa_alloc_destroy": ([V], None),
             "pa_alloc_add": ([V, I64], ctypes.c_int),
+            "pa_alloc_add_ring": ([V, I64, I32], ctypes.c_int),
             "pa_alloc_append": ([V, I64, I32, V, V, V], ctypes.c_int),
             "pa_alloc_append_batch": ([V, I32, V, V, V, V, V, V], ctypes.c_int),
             "pa_alloc_release": ([V, I64], ctypes.c_int),

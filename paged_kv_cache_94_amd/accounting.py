@@ -56,7 +56,7 @@ _ELEM = {"f32": 4, "bf16": 2, "int8": 1}
 
 
 def step_bytes(seq_lens, *, q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int, q_dtype: str,
-               kv_dtype: str, window: int, v_shares_k: bool) -> int:
+               kv_dtype: str, window: int, v_shares_k: bool, token_scales: bool = True) -> int:
     """Algorithmic HBM bytes of one step (see the module docstring)."""
     L = np.asarray(seq_lens, dtype=np.int64)
     B = int(L.size)
@@ -64,18 +64,19 @@ def step_bytes(seq_lens, *, q_len: int, num_q_heads: int, num_kv_heads: int, hea
     e_kv = _ELEM[kv_dtype]
     e_q = _ELEM[q_dtype]
     kv = T * num_kv_heads * head_dim * e_kv * (1 if v_shares_k else 2)
-    if kv_dtype == "int8":
-        kv += T * num_kv_heads * 4 * (1 if v_shares_k else 2)
+    if kv_dtype == "int8":   # per-token scales; per-head ones are 8 bytes per head in all
+        kv += (T if token_scales else 1) * num_kv_heads * 4 * (1 if v_shares_k else 2)
     qo = 2 * B * q_len * num_q_heads * head_dim * e_q
     meta = 4 * int(touched_blocks(L, q_len, window).sum()) + 4 * B
     return int(kv + qo + meta)
 
 
 def touched_kv_bytes(seq_lens, *, q_len: int, num_kv_heads: int, head_dim: int, kv_dtype: str, window: int,
-                     v_shares_k: bool) -> int:
+                     v_shares_k: bool, token_scales: bool = True) -> int:
     """Cache bytes in the whole blocks a block-skipping kernel reads."""
     nblk = int(touched_blocks(seq_lens, q_len, window).sum())
-    per_tok = num_kv_heads * head_dim * _ELEM[kv_dtype] + (num_kv_heads * 4 if kv_dtype == "int8" else 0)
+    per_tok = num_kv_heads * head_dim * _ELEM[kv_dtype] + (num_kv_heads * 4 if kv_dtype == "int8" and token_scales
+                                                           else 0)
     return nblk * BLOCK * per_tok * (1 if v_shares_k else 2)
 
 
@@ -105,7 +106,8 @@ def append_bytes(tokens: int, *, num_kv_heads: int, head_dim: int, src_dtype: st
 def for_inputs(x) -> dict:
     """Byte / flop accounting for a PagedInputs-like object."""
     kw = dict(q_len=x.q_len, num_kv_heads=x.num_kv_heads, head_dim=x.head_dim, kv_dtype=x.kv_dtype,
-              window=x.window, v_shares_k=x.v_pool is x.k_pool)
+              window=x.window, v_shares_k=x.v_pool is x.k_pool,
+              token_scales=x.k_scale is None or x.k_scale.ndim == 3)
     return {
         "alg_bytes": step_bytes(x.seq_lens, num_q_heads=x.num_q_heads, q_dtype=x.q_dtype, **kw),
         "touched_kv_bytes": touched_kv_bytes(x.seq_lens, **kw),

@@ -43,8 +43,12 @@ class BlockAllocator:
     def __del__(self):
         self.close()
 
-    def add(self, seq_id: int) -> None:
-        _lib.check(self._lib.pa_alloc_add(self._h, int(seq_id)))
+    def add(self, seq_id: int, ring_blocks: int = 0) -> None:
+        """Start a sequence; ring_blocks > 0 makes it a ring of that many blocks (window layers)."""
+        if ring_blocks:
+            _lib.check(self._lib.pa_alloc_add_ring(self._h, int(seq_id), int(ring_blocks)))
+        else:
+            _lib.check(self._lib.pa_alloc_add(self._h, int(seq_id)))
 
     def append(self, seq_id: int, n: int, tokens: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, int]:
         """Grow a sequence by n tokens: (slot ids, -1 where cached; number of cached leading tokens)."""

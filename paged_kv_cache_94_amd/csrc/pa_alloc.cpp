@@ -53,6 +53,7 @@ struct Seq {
   std::vector<int32_t> tail;      // token ids of the incomplete last block
   bool hashable = true;           // every token so far came with its id
   bool matching = true;           // every block so far was a prefix hit
+  int32_t ring = 0;               // > 0: a ring of this many blocks (position t in block (t/bs) mod ring)
 };
 
 }  // namespace
@@ -127,7 +128,8 @@ int pa_allocator::append(int64_t sid, int32_t n, const int32_t* tokens, int64_t*
     }
   }
   const int32_t cached_tokens = (int32_t)hit.size() * bs;
-  const int64_t total_blocks = (s.length + n + bs - 1) / bs;
+  int64_t total_blocks = (s.length + n + bs - 1) / bs;
+  if (s.ring > 0 && total_blocks > s.ring) total_blocks = s.ring;
   const int64_t fresh = total_blocks - (int64_t)s.blocks.size() - (int64_t)hit.size();
   int64_t from_queue = fresh;
   for (const auto& h : hit)
@@ -150,9 +152,12 @@ int pa_allocator::append(int64_t sid, int32_t n, const int32_t* tokens, int64_t*
   }
   if (!tokens && n > 0) s.hashable = false;
   if (n > cached_tokens) s.matching = false;
+  // A ring position that a later token of this call overwrites is not written at all.
+  const int64_t keep_from = s.ring > 0 ? s.length + (n - cached_tokens) - (int64_t)s.ring * bs : INT64_MIN;
   for (int32_t i = cached_tokens; i < n; ++i) {
     const int64_t pos = s.length;
-    if (pos % bs == 0) {
+    const int64_t entry = s.ring > 0 ? (pos / bs) % s.ring : pos / bs;
+    if (entry == (int64_t)s.blocks.size()) {
       const int32_t b = pop_front();
       if (has_hash[b]) {
         cached.erase(hash_of[b]);
@@ -161,7 +166,7 @@ int pa_allocator::append(int64_t sid, int32_t n, const int32_t* tokens, int64_t*
       ref[b] = 1;
       s.blocks.push_back(b);
     }
-    slots[k++] = (int64_t)s.blocks[pos / bs] * bs + pos % bs;
+    slots[k++] = pos < keep_from ? -1 : (int64_t)s.blocks[entry] * bs + pos % bs;
     s.length = pos + 1;
     if (s.hashable) s.tail.push_back(tokens[i]);
     if (s.length % bs == 0) {
@@ -219,6 +224,19 @@ int pa_alloc_add(pa_allocator* a, int64_t seq_id) {
   if (!a) return pa::fail(PA_ERR_INVALID_ARG, "allocator is NULL");
   if (a->seqs.count(seq_id)) return pa::fail(PA_ERR_INVALID_ARG, "sequence %lld is live", (long long)seq_id);
   a->seqs.emplace(seq_id, Seq());
+  return PA_OK;
+}
+
+int pa_alloc_add_ring(pa_allocator* a, int64_t seq_id, int32_t ring_blocks) {
+  pa::clear_error();
+  if (!a) return pa::fail(PA_ERR_INVALID_ARG, "allocator is NULL");
+  if (ring_blocks < 1) return pa::fail(PA_ERR_INVALID_ARG, "ring_blocks must be >= 1 (got %d)", ring_blocks);
+  if (a->seqs.count(seq_id)) return pa::fail(PA_ERR_INVALID_ARG, "sequence %lld is live", (long long)seq_id);
+  Seq s;
+  s.ring = ring_blocks;
+  s.hashable = false;
+  s.matching = false;
+  a->seqs.emplace(seq_id, std::move(s));
   return PA_OK;
 }
 

@@ -110,8 +110,20 @@ int validate(const pa_args* a, Entry entry) {
     return fail(PA_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be >= 1");
   if (a->max_seq_len < a->q_len)
     return fail(PA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= q_len (%d)", a->max_seq_len, a->q_len);
-  if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+  if (a->ring_blocks < 0) return fail(PA_ERR_INVALID_ARG, "ring_blocks must be >= 0");
+  if (a->ring_blocks > 0) {
+    if (a->window <= 0) return fail(PA_ERR_INVALID_ARG, "a ring cache needs a window");
+    if (a->ring_blocks > a->max_blocks_per_seq)
+      return fail(PA_ERR_INVALID_ARG, "ring_blocks (%d) exceeds max_blocks_per_seq (%d)", a->ring_blocks,
+                  a->max_blocks_per_seq);
+    if ((int64_t)a->ring_blocks * a->block_size < (int64_t)a->window + a->q_len - 1)
+      return fail(PA_ERR_INVALID_ARG, "a ring of %d blocks cannot hold window + q_len - 1 = %lld keys",
+                  a->ring_blocks, (long long)a->window + a->q_len - 1);
+  } else if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size) {
     return fail(PA_ERR_INVALID_ARG, "max_seq_len (%d) exceeds max_blocks_per_seq * block_size", a->max_seq_len);
+  }
+  if (a->scale_per_head != 0 && (a->scale_per_head != 1 || a->kv_dtype != PA_INT8))
+    return fail(PA_ERR_INVALID_ARG, "scale_per_head is 0, or 1 for an int8 cache");
   if (a->num_splits < 0) return fail(PA_ERR_INVALID_ARG, "num_splits must be >= 0");
   if (a->num_seqs > 0 && (!a->out || !a->q || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens))
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -282,6 +294,8 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   p.scale_log2 = a->scale * pa::kLog2e;
   p.splits = P.splits;
   p.bps = P.bps;
+  p.ring = a->ring_blocks;
+  p.head_scales = a->scale_per_head;
   return p;
 }
 
@@ -393,6 +407,8 @@ int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
   if (a->src_dtype != PA_F32 && a->src_dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "src_dtype must be PA_F32 or PA_BF16");
+  if (a->scale_per_head != 0 && (a->scale_per_head != 1 || a->kv_dtype != PA_INT8))
+    return fail(PA_ERR_INVALID_ARG, "scale_per_head is 0, or 1 for an int8 cache");
   if (a->kv_dtype == PA_INT8) {
     if (a->num_tokens > 0 && (!a->k_scale || !a->v_scale))
       return fail(PA_ERR_INVALID_ARG, "an int8 cache needs k_scale and v_scale");
@@ -425,6 +441,7 @@ int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
   p.Hkv = a->num_kv_heads;
   p.num_blocks = a->num_blocks;
   p.write_v = alias ? 0 : 1;
+  p.head_scales = a->scale_per_head;
   bool supported = false;
   const hipError_t e = pa::launch_cache_write(p, a->src_dtype, a->kv_dtype, a->head_dim,
                                               reinterpret_cast<hipStream_t>(stream),

@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const ch
   const int64_t n_keys = (int64_t)L - kr.lo0;
   if (w >= n_keys || w >= dst_tokens) return;
   const int32_t j = kr.lo0 + (int32_t)w;
-  const int32_t phys = p.block_table[(size_t)b * p.maxb + j / kBlock];
+  const int32_t phys = p.block_table[(size_t)b * p.maxb + table_entry(p, j / kBlock)];
   const int32_t words = row_bytes / 4;
   for (int32_t g = 0; g < p.Hkv; ++g) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(pool + row_offset_bytes(phys, j % kBlock, g, p.Hkv, row_bytes));

@@ -42,7 +42,15 @@ struct Params {
   int32_t* ws_prefix;   // mode 1: [B+1] block prefix sums; mode 2: [B+1] piece prefix sums (workgroup 0 writes)
   int32_t pieces;       // mode 2: pieces the partition aims for (nwg, or more when they are handed out)
   int32_t* ws_queue;    // mode 2, non-null: hand pieces out through this [2] counter pair (zero between calls)
+  int32_t ring;         // > 0: each table row is a ring of this many entries (logical block i -> i mod ring)
+  int32_t head_scales;  // int8: 1 -> k_scale / v_scale hold one scale per KV head
 };
+
+// Table entry that holds logical block i (Lab 5 handout, "Ring KV Cache": in
+// a ring of R blocks position t lives in slot t mod 16R, i.e. block i mod R).
+__device__ __forceinline__ int32_t table_entry(const Params& p, int32_t i) {
+  return p.ring > 0 ? i % p.ring : i;
+}
 
 // Keys a step touches for one sequence (Lab 5 handout, "Sliding Window
 // Attention": skip whole out-of-window blocks). Query t sits at p0 + t.
@@ -72,7 +80,7 @@ __device__ __forceinline__ KeyRange key_range(int32_t L, int32_t q_len, int32_t 
 // A sequence length the block table can map and that holds the step's queries.
 template <typename P>
 __device__ __forceinline__ bool len_ok(int32_t L, const P& p) {
-  return L >= p.q_len && (int64_t)L <= (int64_t)p.maxb * kBlock;
+  return L >= p.q_len && (p.ring > 0 || (int64_t)L <= (int64_t)p.maxb * kBlock);
 }
 
 // First key visible to query t (window rule) -- keys below it are masked.

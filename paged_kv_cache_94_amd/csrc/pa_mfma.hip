@@ -108,7 +108,7 @@ __device__ __forceinline__ int32_t chunk_table(const Params& p, int32_t b, int32
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int32_t idx = min(cfirst + wave + NW * lane, last);
-  return p.block_table[(size_t)b * p.maxb + idx];
+  return p.block_table[(size_t)b * p.maxb + table_entry(p, idx)];
 }
 
 // Attention of query rows (b, g) over logical blocks [first, last] of sequence
@@ -246,11 +246,13 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       for (int u = 0; u < NLOAD; ++u) f.v[u] = buffer_load16<CPOL>(vd, lane_off, u * RPI * tok_stride);
     }
     if constexpr (INT8) {
-      // The block's 16 scales of this KV head: one 64-byte run ([block][head][slot]).
-      const size_t s0 = ((size_t)phys * p.Hkv + g) * kBlock;
-      const int32_t sbytes = valid ? kBlock * 4 : 0;
-      f.ks = buffer_load_f32(buffer_rsrc(p.k_scale + s0, sbytes), (lane & 15) * 4);
-      f.vs = buffer_load_f32(buffer_rsrc(p.v_scale + s0, sbytes), (lane & 15) * 4);
+      // The block's 16 scales of this KV head: one 64-byte run ([block][head][slot]);
+      // with per-head scales every lane reads the head's one scale.
+      const size_t s0 = p.head_scales ? (size_t)g : ((size_t)phys * p.Hkv + g) * kBlock;
+      const int32_t sbytes = valid ? (p.head_scales ? 4 : kBlock * 4) : 0;
+      const int32_t soff = p.head_scales ? 0 : (lane & 15) * 4;
+      f.ks = buffer_load_f32(buffer_rsrc(p.k_scale + s0, sbytes), soff);
+      f.vs = buffer_load_f32(buffer_rsrc(p.v_scale + s0, sbytes), soff);
     }
   };
 
@@ -404,7 +406,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   while (true) {
     const int32_t tbl_next = chunk_table<NW>(p, b, cfirst + 64 * NW, last);
     // Debug load counts, kept out of the pipelined loop below.
-    if (visits && lane < nmine) atomicAdd(visits + cfirst + wave + NW * lane, 1);
+    if (visits && lane < nmine) atomicAdd(visits + table_entry(p, cfirst + wave + NW * lane), 1);
     if (nmine > 0) {
       for (int32_t k = 0;; k += DEPTH) {
 #pragma unroll

@@ -238,9 +238,9 @@ pa_valu_kernel(const Params p) {
   for (; cfirst <= last; cfirst += 64 * NW) {
     const int32_t clast = min(last, cfirst + 64 * NW - 1);
     nmine = clast >= cfirst + wave ? (clast - cfirst - wave) / NW + 1 : 0;
-    tbl = settle(lane < nmine ? table[cfirst + wave + NW * lane] : 0);
+    tbl = settle(lane < nmine ? table[table_entry(p, cfirst + wave + NW * lane)] : 0);
     // Debug load counts, kept out of the pipelined loop below.
-    if (visits && lane < nmine) atomicAdd(visits + cfirst + wave + NW * lane, 1);
+    if (visits && lane < nmine) atomicAdd(visits + table_entry(p, cfirst + wave + NW * lane), 1);
     if constexpr (PIPE) {
       // Block k+1 is in flight while block k is consumed. The fetches are
       // unconditional (past the end they load zero bytes), so every path into

@@ -12,10 +12,11 @@ struct WriteParams {
   const int64_t* slot_ids;  // [T]: block * 16 + slot; < 0 skips the token
   void* k_pool;             // [num_blocks][16][Hkv][D], cache dtype
   void* v_pool;
-  float* k_scale;           // int8 caches: [num_blocks][Hkv][16]
+  float* k_scale;           // int8 caches: [num_blocks][Hkv][16], or [Hkv] with head_scales
   float* v_scale;
   int32_t T, Hkv, num_blocks;
   int32_t write_v;          // 0 when the V pool is the K pool (written once)
+  int32_t head_scales;      // int8: 1 -> k_scale / v_scale are given per head [Hkv], read only
 };
 
 // start / stop: NULL, or events stamped from the kernel's own dispatch.

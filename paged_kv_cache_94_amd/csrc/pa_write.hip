@@ -45,17 +45,22 @@ __device__ __forceinline__ void widen(const uint4& w, float* x) {
 }
 
 // Quantize one lane's EPL values of a row whose LPR lanes hold it together;
-// returns the packed codes (EPL bytes) and the row's scale.
+// returns the packed codes (EPL bytes) and the row's scale. `given_mode`
+// (uniform over the launch): quantize with `given`, the head's fixed scale,
+// instead of the row's own max / 127.
 template <bool SRC_BF16, int LPR>
-__device__ __forceinline__ float quantize_lane(const uint4& w, uint32_t* packed) {
+__device__ __forceinline__ float quantize_lane(const uint4& w, uint32_t* packed, bool given_mode, float given) {
   constexpr int EPL = SRC_BF16 ? 8 : 4;
   float x[EPL];
   widen<SRC_BF16>(w, x);
-  float amax = 0.f;
+  float scale = given;
+  if (!given_mode) {
+    float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  amax = group_max<LPR>(amax);
-  const float scale = amax > 0.f ? amax / 127.0f : 1.0f;
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = group_max<LPR>(amax);
+    scale = amax > 0.f ? amax / 127.0f : 1.0f;
+  }
 #pragma unroll
   for (int i = 0; i < EPL / 4; ++i) {
     uint32_t word = 0;
@@ -103,9 +108,12 @@ __global__ void __launch_bounds__(256) pa_cache_write_kernel(const WriteParams p
                        : zero;
   if constexpr (KV == 2) {
     const size_t sat = ((size_t)blk * p.Hkv + g) * kBlock + slot;
+    const bool hs = p.head_scales != 0;
+    const float gk = hs && live_row ? p.k_scale[g] : 1.0f;
+    const float gv = hs && live_row ? p.v_scale[g] : 1.0f;
     uint32_t ck[EPL / 4], cv[EPL / 4];
-    const float sk = quantize_lane<SRC_BF16, LPR>(wk, ck);
-    const float sv = quantize_lane<SRC_BF16, LPR>(wv, cv);
+    const float sk = quantize_lane<SRC_BF16, LPR>(wk, ck, hs, gk);
+    const float sv = quantize_lane<SRC_BF16, LPR>(wv, cv, hs, gv);
     if (store) {
       int8_t* dk = reinterpret_cast<int8_t*>(p.k_pool) + at;
       int8_t* dv = reinterpret_cast<int8_t*>(p.v_pool) + at;
@@ -116,7 +124,7 @@ __global__ void __launch_bounds__(256) pa_cache_write_kernel(const WriteParams p
         *reinterpret_cast<uint32_t*>(dk) = ck[0];
         if (p.write_v) *reinterpret_cast<uint32_t*>(dv) = cv[0];
       }
-      if (sub == 0) {
+      if (sub == 0 && !hs) {
         p.k_scale[sat] = sk;
         if (p.write_v) p.v_scale[sat] = sv;
       }

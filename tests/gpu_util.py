@@ -35,6 +35,7 @@ class Dev:
         kw.setdefault("window", x.window)
         kw.setdefault("scale", x.scale)
         kw.setdefault("max_seq_len", x.max_seq_len)
+        kw.setdefault("ring_blocks", getattr(x, "ring_blocks", 0))
         if entry is None:
             entry = "verify" if x.q_len > 1 else ("decode_int8" if x.kv_dtype == "int8" else "decode")
         if entry == "decode_int8":
@@ -51,6 +52,7 @@ class Dev:
         kw.setdefault("window", x.window)
         kw.setdefault("scale", x.scale)
         kw.setdefault("max_seq_len", x.max_seq_len)
+        kw.setdefault("ring_blocks", getattr(x, "ring_blocks", 0))
         return pa.plan(self.q, self.k, self.v, self.table, self.lens, k_scale=self.ks, v_scale=self.vs, **kw)
 
     def run_f64(self, **kw) -> np.ndarray:

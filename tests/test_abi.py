@@ -105,6 +105,12 @@ BAD = [
     (dict(num_splits=-1), _lib.PA_ERR_INVALID_ARG),
     (dict(q_dtype=_lib.PA_F32, kv_dtype=_lib.PA_F32, head_dim=256, num_q_heads=64, num_kv_heads=8),
      _lib.PA_ERR_UNSUPPORTED),
+    (dict(ring_blocks=-1), _lib.PA_ERR_INVALID_ARG),
+    (dict(ring_blocks=64, window=0), _lib.PA_ERR_INVALID_ARG),        # a ring needs a window
+    (dict(ring_blocks=600), _lib.PA_ERR_INVALID_ARG),                 # more than max_blocks_per_seq
+    (dict(ring_blocks=63), _lib.PA_ERR_INVALID_ARG),                  # 1008 slots < window 1024
+    (dict(scale_per_head=1), _lib.PA_ERR_INVALID_ARG),                # per-head scales need int8
+    (dict(scale_per_head=2, kv_dtype=_lib.PA_INT8), _lib.PA_ERR_INVALID_ARG),
 ]
 
 
@@ -185,6 +191,7 @@ def _wargs(**kw):
     (dict(v_pool=16), _lib.PA_ERR_INVALID_ARG),                       # aliased pools, distinct rows
     (dict(k_new=24), _lib.PA_ERR_INVALID_ARG),                        # rows not 16-byte aligned
     (dict(v_scale=20), _lib.PA_ERR_INVALID_ARG),                      # scales not 8-byte aligned
+    (dict(scale_per_head=1, kv_dtype=_lib.PA_BF16), _lib.PA_ERR_INVALID_ARG),
 ])
 def test_cache_write_rejects_bad_arguments(lib, kw, code):
     assert lib.pa_cache_write(ctypes.byref(_wargs(**kw)), None) == code
@@ -194,6 +201,18 @@ def test_cache_write_rejects_bad_arguments(lib, kw, code):
 def test_cache_write_zero_tokens_enqueues_nothing(lib):
     w = _wargs(num_tokens=0, k_new=0, v_new=0, slot_ids=0, k_pool=0, v_pool=0, k_scale=0, v_scale=0)
     assert lib.pa_cache_write(ctypes.byref(w), None) == 0
+
+
+def test_ring_plans_past_the_table_length(lib):
+    # In a ring the sequence may be far longer than its table row: only the window is read.
+    info = _lib.PaPlanInfo()
+    a = _args(ring_blocks=64, max_blocks_per_seq=64, max_seq_len=100000)
+    assert lib.pa_plan(ctypes.byref(a), ctypes.byref(info)) == 0
+    b = _args(max_blocks_per_seq=64, max_seq_len=100000)
+    assert lib.pa_plan(ctypes.byref(b), ctypes.byref(info)) == _lib.PA_ERR_INVALID_ARG
+    c = _args(ring_blocks=65, max_blocks_per_seq=65, num_q_heads=40, num_kv_heads=8, q_len=5,
+              q_dtype=_lib.PA_BF16, head_dim=128, max_seq_len=100000)
+    assert lib.pa_plan(ctypes.byref(c), ctypes.byref(info)) == 0           # 1040 >= 1024 + 4
 
 
 def test_zero_sequences_enqueue_nothing(lib):

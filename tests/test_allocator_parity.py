@@ -4,7 +4,8 @@ Host code only, so these run without a GPU. Both sides take the same seeded
 operation streams (new prompts drawn from shared stems so that prefixes
 repeat, decode steps, batched steps, releases, pool exhaustion) and must
 agree exactly after every operation: slot ids, cached counts, errors, block
-tables, lengths, the free queue in order, and the hit counters.
+tables, lengths, the free queue in order, and the hit counters. Some of the
+sequences are rings (window layers) of 1-4 blocks.
 """
 
 from __future__ import annotations
@@ -40,7 +41,7 @@ def _prompt_tokens(rng, vocab):
     return [int(t) for t in stem[:k]] + [int(t) for t in rng.integers(0, vocab, n - k)]
 
 
-def _run(seed, num_blocks, steps, prefix_cache=True, vocab=3, no_ids_rate=0.05):
+def _run(seed, num_blocks, steps, prefix_cache=True, vocab=3, no_ids_rate=0.05, ring_rate=0.15):
     rng = np.random.default_rng(seed)
     ref = A.RefAllocator(num_blocks, BS, prefix_cache)
     lib = BlockAllocator(num_blocks, BS, prefix_cache)
@@ -51,8 +52,9 @@ def _run(seed, num_blocks, steps, prefix_cache=True, vocab=3, no_ids_rate=0.05):
         if op < 0.2 or not ref.seqs:
             sid = next_id
             next_id += 1
-            ref.add(sid)
-            lib.add(sid)
+            ring = int(rng.integers(1, 5)) if rng.random() < ring_rate else 0
+            ref.add(sid, ring)
+            lib.add(sid, ring)
             calls = [(sid, _prompt_tokens(rng, vocab))]
         elif op < 0.55:
             sid = int(rng.choice(sorted(ref.seqs)))

@@ -49,9 +49,11 @@ def _host(t):
 
 
 class Engine:
-    def __init__(self, kv, num_blocks, rng):
+    def __init__(self, kv, num_blocks, rng, ring_blocks=0, window=0):
         self.kv = kv
         self.rng = rng
+        self.ring = ring_blocks
+        self.window = window
         self.alloc = BlockAllocator(num_blocks, BS, prefix_cache=True)
         self.nb = num_blocks
         if kv == "int8":
@@ -91,7 +93,7 @@ class Engine:
         self._write(prefixes, slots)
 
     def add(self, sid, prompt):
-        self.alloc.add(sid)
+        self.alloc.add(sid, self.ring)
         self.grow([sid], [prompt])
 
     def release(self, sid):
@@ -101,7 +103,7 @@ class Engine:
     def check(self):
         sids = sorted(self.tokens)
         lens = [len(self.tokens[s]) for s in sids]
-        mb = max(-(-n // BS) for n in lens)
+        mb = self.ring if self.ring else max(-(-n // BS) for n in lens)
         table, seq_lens = self.alloc.block_table(sids, mb)
         assert seq_lens.tolist() == lens
         torch.cuda.synchronize()
@@ -110,8 +112,10 @@ class Engine:
                 assert _host(got).tobytes() == exp.tobytes()
         if self.kv == "bf16":   # every sequence sees its own prefix's rows through its table
             for i, s in enumerate(sids):
-                for pos in range(lens[i]):
-                    blk, slot = table[i, pos // BS], pos % BS
+                held = range(max(0, lens[i] - self.ring * BS), lens[i]) if self.ring else range(lens[i])
+                for pos in held:
+                    entry = (pos // BS) % self.ring if self.ring else pos // BS
+                    blk, slot = table[i, entry], pos % BS
                     want = f32_to_bf16_bits(_rows_for(self.tokens[s][:pos + 1]))
                     assert (self.kp[blk, slot] == want[0]).all() and (self.vp[blk, slot] == want[1]).all()
         B = len(sids)
@@ -120,13 +124,14 @@ class Engine:
         dq = to_torch(q)
         out = torch.full_like(dq, float("nan"))
         dt, dl = torch.from_numpy(table).cuda(), torch.from_numpy(seq_lens).cuda()
+        kw = dict(max_seq_len=max(lens), window=self.window, ring_blocks=self.ring)
         if self.kv == "int8":
-            pa.decode_int8(out, dq, self.dk, self.dv, dt, dl, self.dks, self.dvs, max_seq_len=max(lens))
+            pa.decode_int8(out, dq, self.dk, self.dv, dt, dl, self.dks, self.dvs, **kw)
         else:
-            pa.decode(out, dq, self.dk, self.dv, dt, dl, max_seq_len=max(lens))
+            pa.decode(out, dq, self.dk, self.dv, dt, dl, **kw)
         torch.cuda.synchronize()
-        prob = oracle.Problem(q, self.kp, self.vp, table, seq_lens, q_len=1, window=0, scale=D ** -0.5,
-                              k_scale=self.ks, v_scale=self.vs)
+        prob = oracle.Problem(q, self.kp, self.vp, table, seq_lens, q_len=1, window=self.window, scale=D ** -0.5,
+                              k_scale=self.ks, v_scale=self.vs, ring_blocks=self.ring)
         ref = oracle.attention(prob)
         got = out.float().cpu().numpy().astype(np.float64)
         assert not np.isnan(got).any()
@@ -160,3 +165,25 @@ def test_allocator_append_decode_steps(kv):
     q, h = eng.alloc.stats()
     _log(f"{kv}: prefix blocks queried {q}, hit {h}; {eng.hit_tokens} tokens served from cache")
     assert h > 0 and eng.hit_tokens > 0
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_ring_allocator_decode_steps(kv):
+    # A window layer (W = 48) whose sequences live in rings of 3 blocks: prompts longer and shorter
+    # than the ring, then 40 decode steps, so every ring wraps several times.
+    rng = np.random.default_rng(77 if kv == "bf16" else 78)
+    eng = Engine(kv, num_blocks=24, rng=rng, ring_blocks=3, window=48)
+    for sid, n in enumerate([5, 30, 47, 48, 49, 120]):
+        eng.add(sid, [int(t) for t in rng.integers(0, 99, n)])
+    assert eng.alloc.num_free() == 24 - (1 + 2 + 3 + 3 + 3 + 3)
+    for step in range(40):
+        if step == 20:
+            eng.release(2)
+            eng.add(100, [int(t) for t in rng.integers(0, 99, 70)])
+        sids = sorted(eng.tokens)
+        eng.grow(sids, [[int(rng.integers(0, 99))] for _ in sids])
+        err = eng.check()
+        if step % 10 == 0:
+            _log(f"ring {kv} step {step}: free={eng.alloc.num_free()} max|err|={err:.2e}")
+        assert err <= TOL[kv]
+    assert eng.alloc.num_free() == 24 - 6 * 3

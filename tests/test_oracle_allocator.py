@@ -259,3 +259,22 @@ def test_each_mutant_fails_a_pin(mutant):
     finally:
         A.MUTANT = 0
     assert failed, f"mutant {mutant} ({MUTANT_NAMES[mutant]}) passed every pin"
+
+
+def test_ring_sequence_wraps_at_its_block_count():
+    al = A.RefAllocator(10, BS)
+    al.add(1, ring_blocks=3)
+    slots, _ = al.append(1, 100, list(range(100)))
+    blocks = al.blocks(1)
+    assert len(blocks) == 3 and al.num_free() == 7                # never more than its ring
+    for t in range(100):                                          # slot t mod 48; -1 if overwritten later
+        want = blocks[(t // BS) % 3] * BS + t % BS if t >= 100 - 48 else -1
+        assert slots[t] == want
+    assert len(set(slots[-48:])) == 48                            # one write per slot and call
+    assert not al.cached and al.queried == 0                       # rings never touch the prefix cache
+    more, _ = al.append(1, 5, [1] * 5)
+    assert more == [blocks[(t // BS) % 3] * BS + t % BS for t in range(100, 105)]
+    table, lens = al.block_table([1], 3)
+    assert table == [blocks] and lens == [105]
+    al.release(1)
+    assert al.num_free() == 10

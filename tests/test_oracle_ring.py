@@ -14,6 +14,8 @@ head scale must produce clamp(rint(x / s)).
 
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -23,8 +25,8 @@ from workloads import make_inputs
 BS = 16
 
 
-def _ringify(x, rng):
-    """The same problem with each sequence's cache in a ring of R blocks (built here, not by the oracle)."""
+def ring_inputs(x, rng):
+    """The same inputs with each sequence's cache in a ring of R blocks (built here, not by the oracle)."""
     R = -(-(x.window + x.q_len - 1) // BS)
     C = R * BS
     B = x.batch
@@ -57,8 +59,12 @@ def _ringify(x, rng):
                 vs[dst, :, slot] = x.v_scale[src_blk, :, src_slot]
         used = min(R, -(-L // BS))
         table[b, used:] = poison_blk
-    return oracle.Problem(x.q, kp, vp, table, x.seq_lens, q_len=x.q_len, window=x.window, scale=x.scale,
-                          k_scale=ks, v_scale=vs, ring_blocks=R), R
+    return dataclasses.replace(x, k_pool=kp, v_pool=vp, k_scale=ks, v_scale=vs, block_table=table, ring_blocks=R)
+
+
+def _ringify(x, rng):
+    y = ring_inputs(x, rng)
+    return oracle.Problem.from_inputs(y), y.ring_blocks
 
 
 # (lens, q_len, Hq, Hkv, D, window, q_dtype, kv_dtype)
