@@ -56,6 +56,7 @@ class _Problem(ctypes.Structure):
         ("scale", ctypes.c_double),
         ("ring_blocks", ctypes.c_int32),
         ("head_scales", ctypes.c_int32),
+        ("q_start", ctypes.c_void_p),
     ]
 
 
@@ -159,7 +160,15 @@ class Problem:
     """Keeps the numpy arrays alive while the C struct points into them."""
 
     def __init__(self, q, k_pool, v_pool, block_table, seq_lens, *, q_len, window, scale,
-                 k_scale=None, v_scale=None, block_size=16, ring_blocks=0):
+                 k_scale=None, v_scale=None, block_size=16, ring_blocks=0, q_start=None):
+        """q_start: None (q is [B, q_len, Hq, D]) or [B+1] offsets of packed queries (q is [total, Hq, D])."""
+        self.q_start = None if q_start is None else np.ascontiguousarray(q_start, dtype=np.int32)
+        q = np.asarray(q)
+        if self.q_start is not None:
+            if q.ndim != 3 or q.shape[0] != int(self.q_start[-1]):
+                raise ValueError("packed queries must be [q_start[-1], Hq, D]")
+            q = q.reshape(q.shape[0], 1, q.shape[1], q.shape[2])
+            q_len = 1
         self.q = np.ascontiguousarray(q)
         self.k_pool = np.ascontiguousarray(k_pool)
         self.v_pool = self.k_pool if v_pool is k_pool else np.ascontiguousarray(v_pool)
@@ -201,15 +210,23 @@ class Problem:
         s.scale = float(scale)
         s.ring_blocks = int(ring_blocks)
         s.head_scales = head_scales
+        if self.q_start is not None:
+            if self.q_start.shape != (self.seq_lens.size + 1,):
+                raise ValueError("q_start must be [B+1]")
+            s.q_start = self.q_start.ctypes.data
+            s.B = self.seq_lens.size
+            self.shape = (int(self.q_start[-1]), Hq, D)
+        else:
+            self.shape = (B, q_len, Hq, D)
         self.struct = s
-        self.shape = (B, q_len, Hq, D)
 
     @classmethod
     def from_inputs(cls, x) -> "Problem":
         """Build from any object with the paged-input attribute names."""
         return cls(x.q, x.k_pool, x.v_pool, x.block_table, x.seq_lens, q_len=x.q_len,
                    window=x.window, scale=x.scale, k_scale=x.k_scale, v_scale=x.v_scale,
-                   block_size=x.block_size, ring_blocks=getattr(x, "ring_blocks", 0))
+                   block_size=x.block_size, ring_blocks=getattr(x, "ring_blocks", 0),
+                   q_start=getattr(x, "q_start", None))
 
 
 def _check(rc: int) -> None:
@@ -218,11 +235,11 @@ def _check(rc: int) -> None:
 
 
 def attention(p: Problem, rows: Optional[np.ndarray] = None, threads: int = 0) -> np.ndarray:
-    """fp64 attention. All rows -> [B,q_len,Hq,D]; listed rows -> [n_rows, D]."""
+    """fp64 attention. All rows -> [B,q_len,Hq,D] ([total,Hq,D] packed); listed rows -> [n_rows, D]."""
     lib = _current()
-    B, ql, Hq, D = p.shape
+    D = p.shape[-1]
     if rows is None:
-        out = np.empty((B, ql, Hq, D), dtype=np.float64)
+        out = np.empty(p.shape, dtype=np.float64)
         _check(lib.oracle_attention(ctypes.byref(p.struct), None, 0, out.ctypes.data, threads))
     else:
         r = np.ascontiguousarray(rows, dtype=np.int64)
@@ -238,7 +255,7 @@ def visited_blocks(p: Problem) -> np.ndarray:
     holding both the oldest and the newest keys of the window counts 2.
     """
     lib = _current()
-    vis = np.empty((p.shape[0], p.block_table.shape[1]), dtype=np.int32)
+    vis = np.empty((p.seq_lens.size, p.block_table.shape[1]), dtype=np.int32)
     _check(lib.oracle_visited_blocks(ctypes.byref(p.struct), vis.ctypes.data))
     return vis
 
@@ -246,7 +263,7 @@ def visited_blocks(p: Problem) -> np.ndarray:
 def gather(p: Problem, which: int, dst_tokens: int, fill: int = 0) -> np.ndarray:
     """Raw K (which=0) or V (which=1) rows of the visible key range, [B, dst_tokens, Hkv, D]."""
     lib = _current()
-    B = p.shape[0]
+    B = p.seq_lens.size
     _, _, Hkv, D = p.k_pool.shape
     dst = np.full((B, dst_tokens, Hkv, D), fill, dtype=p.k_pool.dtype)
     _check(lib.oracle_gather(ctypes.byref(p.struct), which, dst.ctypes.data, dst_tokens))

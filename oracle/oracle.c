@@ -28,6 +28,11 @@
  *  - Causal multi-token step (tiniestgpt notes, "Speculative decoding"): a
  *    verify step feeds q_len tokens; query t sits at position L - q_len + t,
  *    where L (seq_lens[b]) already counts all q_len new tokens.
+ *  - Prefill over a paged cache (Lab 5, "Flash Attention": causal
+ *    attention for q_len > 1 with history already in the cache): with
+ *    q_start set, sequence b brings q_start[b+1] - q_start[b] query tokens
+ *    of its own, packed one sequence after another, and query t of b sits at
+ *    L - (q_start[b+1] - q_start[b]) + t.
  *  - int8 cache (tiniestgpt notes, "Quantization" / KV cache quantization):
  *    codes are gathered first and then dequantized, value = code * scale,
  *    with one scale per token per KV head (per-token granularity) or one
@@ -81,7 +86,23 @@ typedef struct {
   double scale;
   int32_t ring_blocks;      /* 0: block_table row is linear; > 0: a ring of this many entries */
   int32_t head_scales;      /* int8 only: 0 scales per token [num_blocks][Hkv][block_size]; 1 per head [Hkv] */
+  const int32_t* q_start;   /* NULL: every sequence has q_len queries, q is [B][q_len][Hq][D]. Else [B+1]
+                               offsets: q (and out) are [q_start[B]][Hq][D], q_len is unused */
 } orc_problem;
+
+/* Query tokens of sequence b. */
+static int32_t seq_queries(const orc_problem* P, int b) {
+  return P->q_start ? P->q_start[b + 1] - P->q_start[b] : P->q_len;
+}
+
+/* Largest query count of any sequence (the ring must hold window + that - 1). */
+static int32_t max_queries(const orc_problem* P) {
+  int32_t m = P->q_start ? 0 : P->q_len;
+  if (P->q_start)
+    for (int b = 0; b < P->B; ++b)
+      if (seq_queries(P, b) > m) m = seq_queries(P, b);
+  return m;
+}
 
 /* One stored element, widened to double. bf16 is the upper half of a binary32. */
 static double elem(const void* base, int dtype, size_t i) {
@@ -97,7 +118,13 @@ static double elem(const void* base, int dtype, size_t i) {
 
 static int check_problem(const orc_problem* P) {
   if (!P || !P->q || !P->k_pool || !P->v_pool || !P->block_table || !P->seq_lens) return ORC_ERR_ARG;
-  if (P->B < 0 || P->q_len < 1 || P->Hq < 1 || P->Hkv < 1 || P->D < 1) return ORC_ERR_ARG;
+  if (P->B < 0 || P->Hq < 1 || P->Hkv < 1 || P->D < 1) return ORC_ERR_ARG;
+  if (!P->q_start && P->q_len < 1) return ORC_ERR_ARG;
+  if (P->q_start) {
+    if (P->q_start[0] != 0) return ORC_ERR_ARG;
+    for (int b = 0; b < P->B; ++b)
+      if (seq_queries(P, b) < 0) return ORC_ERR_ARG;
+  }
   if (P->block_size < 1 || P->num_blocks < 1 || P->max_blocks < 1) return ORC_ERR_ARG;
   if (P->Hq % P->Hkv != 0) return ORC_ERR_ARG;
   if (P->q_dtype != ORC_F32 && P->q_dtype != ORC_BF16) return ORC_ERR_ARG;
@@ -107,11 +134,11 @@ static int check_problem(const orc_problem* P) {
   if (P->ring_blocks < 0) return ORC_ERR_ARG;
   if (P->ring_blocks > 0) {
     if (P->window <= 0 || P->ring_blocks > P->max_blocks) return ORC_ERR_ARG;
-    if ((int64_t)P->ring_blocks * P->block_size < (int64_t)P->window + P->q_len - 1) return ORC_ERR_ARG;
+    if ((int64_t)P->ring_blocks * P->block_size < (int64_t)P->window + max_queries(P) - 1) return ORC_ERR_ARG;
   }
   for (int b = 0; b < P->B; ++b) {
     int32_t L = P->seq_lens[b];
-    if (L < P->q_len) return ORC_ERR_DATA;
+    if (L < seq_queries(P, b) || L < 1) return ORC_ERR_DATA;
     if (P->ring_blocks == 0 && (int64_t)L > (int64_t)P->max_blocks * P->block_size) return ORC_ERR_DATA;
     int32_t used = (L + P->block_size - 1) / P->block_size;
     if (P->ring_blocks > 0 && used > P->ring_blocks) used = P->ring_blocks;
@@ -129,7 +156,7 @@ static void query_span(const orc_problem* P, int b, int t, int32_t* first, int32
 #if ORC_MUTANT == 3
   int32_t p = L - 1; (void)t;
 #else
-  int32_t p = L - P->q_len + t;
+  int32_t p = L - seq_queries(P, b) + t;
 #endif
   int32_t lo = 0;
   if (P->window > 0) {
@@ -191,7 +218,8 @@ static int attend_row(const orc_problem* P, int b, int t, int h, double* out, do
 #endif
   int32_t lo, p;
   query_span(P, b, t, &lo, &p);
-  const size_t qrow = (((size_t)b * P->q_len + t) * P->Hq + h) * (size_t)D;
+  const size_t qtok = P->q_start ? (size_t)P->q_start[b] + t : (size_t)b * P->q_len + t;
+  const size_t qrow = (qtok * P->Hq + h) * (size_t)D;
   const int32_t n = p - lo + 1;
 
   for (int32_t j = lo; j <= p; ++j) {
@@ -238,16 +266,17 @@ static int attend_row(const orc_problem* P, int b, int t, int h, double* out, do
 
 /*
  * Attention output in fp64.
- *   rows == NULL: every row, out is [B][q_len][Hq][D].
- *   rows != NULL: only the listed rows, row index r = (b*q_len + t)*Hq + h,
- *                 out is [n_rows][D].
+ *   rows == NULL: every row, out is [B][q_len][Hq][D] ([q_start[B]][Hq][D] with q_start).
+ *   rows != NULL: only the listed rows, row index r = (b*q_len + t)*Hq + h
+ *                 ((q_start[b] + t)*Hq + h with q_start), out is [n_rows][D].
  * nthreads <= 0 uses the OpenMP default. Returns an ORC_* code.
  */
 int oracle_attention(const orc_problem* P, const int64_t* rows, int64_t n_rows, double* out, int nthreads) {
   int rc = check_problem(P);
   if (rc != ORC_OK) return rc;
   if (!out) return ORC_ERR_ARG;
-  const int64_t total = (int64_t)P->B * P->q_len * P->Hq;
+  const int64_t tokens = P->q_start ? (int64_t)P->q_start[P->B] : (int64_t)P->B * P->q_len;
+  const int64_t total = tokens * P->Hq;
   const int64_t n = rows ? n_rows : total;
   if (rows) {
     for (int64_t i = 0; i < n_rows; ++i)
@@ -276,8 +305,15 @@ int oracle_attention(const orc_problem* P, const int64_t* rows, int64_t n_rows, 
         int64_t r = rows ? rows[i] : i;
         int h = (int)(r % P->Hq);
         int64_t bt = r / P->Hq;
-        int t = (int)(bt % P->q_len);
-        int b = (int)(bt / P->q_len);
+        int b, t;
+        if (P->q_start) {   /* the sequence whose query range holds token bt */
+          b = 0;
+          while (P->q_start[b + 1] <= bt) ++b;
+          t = (int)(bt - P->q_start[b]);
+        } else {
+          t = (int)(bt % P->q_len);
+          b = (int)(bt / P->q_len);
+        }
         attend_row(P, b, t, h, out + (size_t)i * P->D, scores);
       }
       free(scores);
@@ -313,7 +349,7 @@ int oracle_visited_blocks(const orc_problem* P, int32_t* vis) {
     const int32_t nlog = (L + P->block_size - 1) / P->block_size;
     uint8_t* seen = (uint8_t*)calloc((size_t)nlog, 1);
     if (!seen) return ORC_ERR_NOMEM;
-    for (int t = 0; t < P->q_len; ++t) {
+    for (int t = 0; t < seq_queries(P, b); ++t) {
       int32_t lo, p;
       query_span(P, b, t, &lo, &p);
       for (int32_t j = lo; j <= p; ++j) seen[j / P->block_size] = 1;
@@ -341,8 +377,9 @@ int oracle_gather(const orc_problem* P, int which, void* dst, int64_t dst_tokens
   const size_t row_bytes = esz * (size_t)P->D;
   for (int b = 0; b < P->B; ++b) {
     int32_t lo0, p0, lo_last, p_last;
+    if (seq_queries(P, b) < 1) continue;
     query_span(P, b, 0, &lo0, &p0);
-    query_span(P, b, P->q_len - 1, &lo_last, &p_last);
+    query_span(P, b, seq_queries(P, b) - 1, &lo_last, &p_last);
     if ((int64_t)(p_last - lo0 + 1) > dst_tokens) return ORC_ERR_ARG;
     for (int32_t j = lo0; j <= p_last; ++j)
       for (int g = 0; g < P->Hkv; ++g) {

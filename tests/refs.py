@@ -69,3 +69,27 @@ def dense_sdpa(x) -> np.ndarray:
                                            enable_gqa=x.num_q_heads != x.num_kv_heads)
         out[b] = o[0].permute(1, 0, 2).numpy()
     return out
+
+
+def dense_sdpa_packed(x) -> np.ndarray:
+    """[total, Hq, D] float64 for packed (prefill) queries, sequence by sequence, as dense_sdpa."""
+    q_all = storage_to_f64(x.q)
+    out = np.empty(q_all.shape, dtype=np.float64)
+    for b in range(x.batch):
+        a, e = int(x.q_start[b]), int(x.q_start[b + 1])
+        if e == a:
+            continue
+        k, v = contiguous_cache(x, b)
+        L = k.shape[0]
+        mask_np = band_mask(L, e - a, x.window)
+        unseen = ~mask_np.any(axis=0)
+        k[unseen] = 0.0
+        v[unseen] = 0.0
+        q = torch.from_numpy(q_all[a:e]).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k).permute(1, 0, 2)[None].contiguous()
+        vt = torch.from_numpy(v).permute(1, 0, 2)[None].contiguous()
+        mask = torch.from_numpy(mask_np)[None, None]
+        o = F.scaled_dot_product_attention(q, kt, vt, attn_mask=mask, scale=x.scale,
+                                           enable_gqa=x.num_q_heads != x.num_kv_heads)
+        out[a:e] = o[0].permute(1, 0, 2).numpy()
+    return out

@@ -22,6 +22,7 @@ import pytest
 import oracle
 from tests import test_oracle_append as append_pins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_prefill as prefill_pins
 from tests import test_oracle_ring as ring_pins
 
 MUTANTS = {
@@ -65,6 +66,7 @@ PIN_CALLS = [
     lambda: [ring_pins.test_ring_visits_closed_form(i) for i in range(len(ring_pins.RING_CASES))],
     lambda: [ring_pins.test_per_head_scales_equal_repeated_per_token_scales(w, q) for w, q in ((0, 1), (20, 1))],
     ring_pins.test_per_head_append_codes,
+    lambda: [prefill_pins.test_prefill_matches_torch_sdpa(i) for i in range(len(prefill_pins.CASES))],
 ]
 
 

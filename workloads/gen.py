@@ -115,6 +115,7 @@ class PagedInputs:
     name: str = "custom"
     seed: int = 0
     ring_blocks: int = 0  # > 0: each table row is a ring of this many blocks (window layers)
+    q_start: Optional[np.ndarray] = None  # prefill: [B+1] offsets of packed queries q [total, Hq, D]
 
     @property
     def batch(self) -> int:
@@ -207,7 +208,8 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
                 scale: Optional[float] = None, seed: int = 0, rng: Optional[np.random.Generator] = None,
                 num_blocks: Optional[int] = None, pool_slack: float = 1.1,
                 max_blocks: Optional[int] = None, alias_v: bool = False, poison: bool = False,
-                name: str = "custom", ring: bool = False, head_scales: bool = False) -> PagedInputs:
+                name: str = "custom", ring: bool = False, head_scales: bool = False,
+                q_lens: Optional[Sequence[int]] = None) -> PagedInputs:
     """Build one seeded paged-cache problem.
 
     ``seq_lens`` counts cached tokens including this step's ``q_len`` queries.
@@ -218,14 +220,23 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
     R = ceil((window + q_len - 1) / 16) blocks and position t lives in ring
     slot t mod 16R (Lab 5, "Ring KV Cache"); the table has R columns.
     ``head_scales`` (int8 only): one scale per KV head for the whole pool.
+    ``q_lens`` (prefill): per-sequence query counts; queries are packed one
+    sequence after another, q is [sum(q_lens), Hq, D] with offsets q_start,
+    and query t of sequence b sits at seq_lens[b] - q_lens[b] + t. ``q_len``
+    is then ignored and set to max(q_lens).
     """
     if rng is None:
         rng = np.random.default_rng(seed)
     lens = np.asarray(seq_lens, dtype=np.int64)
     if lens.ndim != 1:
         raise ValueError("seq_lens must be 1-D")
-    if np.any(lens < q_len):
-        raise ValueError("every sequence must hold at least q_len tokens")
+    qls = np.full(lens.size, q_len, dtype=np.int64) if q_lens is None else np.asarray(q_lens, dtype=np.int64)
+    if q_lens is not None:
+        if qls.shape != lens.shape or np.any(qls < 0):
+            raise ValueError("q_lens must be [B], >= 0")
+        q_len = int(qls.max()) if qls.size else 1
+    if np.any(lens < qls) or np.any(lens < 1):
+        raise ValueError("every sequence must hold at least its query tokens (and one token)")
     B = int(lens.size)
     bs = BLOCK_SIZE
     nblk = (lens + bs - 1) // bs
@@ -260,7 +271,12 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
         table[b, :n] = perm[off:off + n]
         off += n
 
-    qf = _standard_normal(rng, (B, q_len, num_q_heads, head_dim))
+    q_start = None
+    if q_lens is not None:
+        q_start = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+        qf = _standard_normal(rng, (int(q_start[-1]), num_q_heads, head_dim))
+    else:
+        qf = _standard_normal(rng, (B, q_len, num_q_heads, head_dim))
     if q_dtype == "f32":
         q = qf
     elif q_dtype == "bf16":
@@ -285,7 +301,7 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
         for pool, sc in pools:
             _poison_slots(pool, sc, unused, slice(None), kv_dtype)
             if ring_blocks:
-                _poison_ring(pool, sc, table, lens, nblk, ring_blocks, q_len, window, kv_dtype)
+                _poison_ring(pool, sc, table, lens, nblk, ring_blocks, qls, window, kv_dtype)
                 continue
             for b in range(B):
                 L = int(lens[b])
@@ -294,7 +310,7 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
                 if tail < bs:
                     _poison_slots(pool, sc, table[b, n - 1], slice(tail, bs), kv_dtype)
                 if window > 0:
-                    first_key = max(0, L - q_len - window + 1)
+                    first_key = max(0, L - int(qls[b]) - window + 1)
                     full = first_key // bs
                     if full:
                         _poison_slots(pool, sc, table[b, :full], slice(None), kv_dtype)
@@ -305,10 +321,10 @@ def make_inputs(seq_lens: Sequence[int], *, q_len: int, num_q_heads: int, num_kv
                        block_table=table, seq_lens=lens.astype(np.int32), q_len=q_len,
                        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                        window=int(window), scale=float(scale), q_dtype=q_dtype, kv_dtype=kv_dtype,
-                       name=name, seed=seed, ring_blocks=ring_blocks)
+                       name=name, seed=seed, ring_blocks=ring_blocks, q_start=q_start)
 
 
-def _poison_ring(pool, sc, table, lens, nblk, R, q_len, window, kv_dtype):
+def _poison_ring(pool, sc, table, lens, nblk, R, qls, window, kv_dtype):
     """Poison every ring slot that holds no key a query of the step may see.
 
     Ring slot e*16 + s holds the newest position t <= L-1 with t = e*16 + s
@@ -317,7 +333,7 @@ def _poison_ring(pool, sc, table, lens, nblk, R, q_len, window, kv_dtype):
     C = R * bs
     for b in range(table.shape[0]):
         L = int(lens[b])
-        lo = max(0, L - q_len - window + 1)
+        lo = max(0, L - int(qls[b]) - window + 1)
         for e in range(int(nblk[b])):
             r = e * bs + np.arange(bs)
             t = (L - 1) - ((L - 1 - r) % C)
