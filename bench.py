@@ -114,6 +114,8 @@ def parse():
     ap.add_argument("--ring", action="store_true",
                     help="window workloads: lay each sequence's cache out as a ring of window/16 blocks")
     ap.add_argument("--head-scales", action="store_true", help="int8 workload: one scale per KV head")
+    ap.add_argument("--prefill", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="time a paged prefill workload instead of a decode step (1 local layer, 2 global, 3 int8)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
     return ap.parse_args()
@@ -187,6 +189,110 @@ def measure_allocator(np, x, *, steps: int) -> dict:
                     "the binding's call overhead dominates"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published
+
+
+def main_prefill(args) -> int:
+    """One step = one pa_prefill call over the workload's packed chunks (inputs resident in HBM)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_94_amd as pa
+    from paged_kv_cache_94_amd import accounting
+    from workloads import PREFILL_CONFIGS, make_prefill_config
+
+    if not os.path.exists(pa.library_path()):
+        from paged_kv_cache_94_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = PREFILL_CONFIGS[args.prefill]
+    x = make_prefill_config(args.prefill)
+    acct = accounting.for_inputs(x)
+    log(f"workload {x.name}: B={x.batch} chunk {cfg['chunk']} history {cfg['hist']} Hq={x.num_q_heads} "
+        f"Hkv={x.num_kv_heads} D={x.head_dim} window={x.window} kv={x.kv_dtype}; "
+        f"{acct['flops'] / 1e12:.3f} TFLOP per step")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, qs, lens, table = to_dev(x.q), to_dev(x.q_start), to_dev(x.seq_lens), to_dev(x.block_table)
+    k = to_dev(x.k_pool)
+    v = k if x.v_aliases_k else to_dev(x.v_pool)
+    ks = None if x.k_scale is None else to_dev(x.k_scale)
+    vs = None if x.v_scale is None else to_dev(x.v_scale)
+    out = torch.empty_like(q)
+    kw = dict(max_q_len=int(np.diff(x.q_start).max()), window=x.window, scale=x.scale, max_seq_len=x.max_seq_len,
+              k_scale=ks, v_scale=vs)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        pa.prefill(out, q, qs, k, v, table, lens, **kw)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        pa.prefill(out, q, qs, k, v, table, lens, timing=ev[i], **kw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    tflops = acct["flops"] / kern_s / 1e12
+    ms_per_step = elapsed / args.steps * 1e3
+    value = acct["queries"] * args.steps / elapsed
+    log(f"prefill kernel: mean {kern_s * 1e6:.1f} us -> {tflops:.1f} TFLOP/s = "
+        f"{tflops / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of bf16 MFMA peak; step {ms_per_step * 1e3:.1f} us, "
+        f"{value:.4g} query tokens/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle   # the CPU baseline leg is the only part of the benchmark that uses the oracle
+        prob = oracle.Problem.from_inputs(x)
+        threads = oracle.default_threads()
+        rng = np.random.default_rng(0)
+        total_rows = acct["queries"] * x.num_q_heads
+        n, spent, done = 256, 0.0, 0
+        while spent < args.cpu_seconds and done < total_rows:
+            rows = rng.integers(0, total_rows, n).astype(np.int64)
+            c0 = time.perf_counter()
+            oracle.attention(prob, rows=rows, threads=threads)
+            spent += time.perf_counter() - c0
+            done += n
+        cpu = {"value": done / x.num_q_heads / spent, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{done} (query token, head) rows drawn uniformly from the workload, fp64, "
+                         f"{spent:.1f} s; value = rows/s / Hq"}
+        log(f"cpu baseline: {cpu['value']:.4g} query tokens/s on {threads} threads")
+
+    rec = {
+        "metric": "paged prefill query tokens/s and matrix-core TFLOP/s (% of MI355X bf16 peak)",
+        "value": value,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if x.kv_dtype == "bf16" else "int8 cache, bf16 q",
+        "data": "synthetic",
+        "config": {"workload": f"{x.name}: B={x.batch}, chunk={cfg['chunk']}, history {cfg['hist']}, "
+                               f"Hq={x.num_q_heads}, Hkv={x.num_kv_heads}, D={x.head_dim}, window={x.window} "
+                               f"(seed {100 + args.prefill})",
+                   "flops_per_step": acct["flops"], "kernel_us": kern_s * 1e6},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,6 +301,9 @@ def main() -> int:
               "decode attention shards by sequence or KV head with no exchange, so a multi-GPU figure "
               "would be N independent copies of this one.", file=sys.stderr)
         return 2
+
+    if args.prefill:
+        return main_prefill(args)
 
     import numpy as np
     import torch

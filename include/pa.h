@@ -237,6 +237,56 @@ typedef struct {
  */
 int pa_cache_write(const pa_write_args* args, pa_stream_t stream);
 
+/*
+ * Paged prefill: a chunk of query tokens per sequence, causal among
+ * themselves, over the sequence's history already in the cache (Lab 5,
+ * "Flash Attention": q_len > 1 with cached history, global and window
+ * layers, GQA without repeating K/V, key blocks outside a query tile's
+ * causal and window range never loaded). The chunk's own keys and values
+ * must be in the cache first (pa_cache_write). Sequence b brings
+ * q_start[b+1] - q_start[b] >= 0 query tokens, packed one sequence after
+ * another; its query t sits at position seq_lens[b] - (q_start[b+1] -
+ * q_start[b]) + t and sees keys j with j <= position (and position - j <
+ * window when window > 0).
+ */
+typedef struct {
+  void* out;                  /* [total_q][Hq][D] bf16 */
+  const void* q;              /* [total_q][Hq][D] bf16 */
+  const int32_t* q_start;     /* [num_seqs + 1] device int32, q_start[0] = 0, non-decreasing,
+                                 q_start[num_seqs] = total_q */
+  const void* k_pool;         /* [num_blocks][block_size][Hkv][D], bf16 or int8 */
+  const void* v_pool;         /* same; may equal k_pool */
+  const float* k_scale;       /* int8 only: as in pa_args (per token, or per head with scale_per_head) */
+  const float* v_scale;
+  const int32_t* block_table; /* [B][max_blocks_per_seq]; ring rows with ring_blocks > 0 */
+  const int32_t* seq_lens;    /* [B] cached tokens, this chunk's included; >= the chunk's length */
+  int32_t num_seqs;           /* B >= 0 */
+  int32_t total_q;            /* q_start[B] (host copy; sizes nothing on the device) */
+  int32_t max_q_len;          /* host upper bound on any sequence's query count; sizes the grid */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv; Hq / Hkv <= 128 (64 at head_dim 256) */
+  int32_t head_dim;           /* 64, 128 or 256 */
+  int32_t block_size;         /* 16 */
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_seq_len;        /* host upper bound on seq_lens[] */
+  int32_t window;             /* <= 0: every earlier key; > 0: the W most recent keys */
+  float scale;                /* multiplies q.k */
+  int32_t q_dtype;            /* PA_BF16 */
+  int32_t kv_dtype;           /* PA_BF16 or PA_INT8 */
+  int32_t ring_blocks;        /* as in pa_args; the ring must hold window + max_q_len - 1 keys */
+  int32_t scale_per_head;     /* as in pa_args */
+  pa_event_t timing_start;    /* NULL, or an event stamped when the prefill kernel starts */
+  pa_event_t timing_stop;     /* NULL, or one stamped when it completes */
+} pa_prefill_args;
+
+/* Enqueue the prefill attention on stream. Returns PA_OK, PA_ERR_INVALID_ARG
+ * (NULL pointer, bad sizes, a ring too small for the chunk, misaligned
+ * pointers: q, out and the pools must be 16-byte aligned), PA_ERR_UNSUPPORTED
+ * (fp32, head_dim, block_size, or a query group too large) or PA_ERR_HIP.
+ * Sequences whose q_start range is empty write nothing. */
+int pa_prefill(const pa_prefill_args* args, pa_stream_t stream);
+
 /* Static description of a return code. */
 const char* pa_strerror(int code);
 

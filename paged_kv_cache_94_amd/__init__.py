@@ -12,6 +12,7 @@ Layouts (row-major, all tensors on the same GPU):
                      or [Hkv]                 float32 (int8 caches, one scale per head)
     k_new, v_new [T, Hkv, D]                  float32 or bfloat16 (cache_write)
     slot_ids     [T]                          int64, block * 16 + slot (cache_write)
+    q, out       [total, Hq, D] with q_start [B+1] int32 (prefill: packed per-sequence queries)
     block_table  [B, max_blocks_per_seq]      int32 (ring_blocks > 0: each row's first
                                               ring_blocks entries are the sequence's ring)
     seq_lens     [B]                          int32, this step's tokens included
@@ -25,8 +26,8 @@ from typing import Optional
 from . import _lib
 from ._lib import PaError  # noqa: F401
 
-__all__ = ["decode", "decode_int8", "verify", "cache_write", "debug_gather", "plan", "workspace_size",
-           "PaError", "library_path"]
+__all__ = ["decode", "decode_int8", "verify", "prefill", "cache_write", "debug_gather", "plan",
+           "workspace_size", "PaError", "library_path"]
 
 
 def library_path() -> str:
@@ -211,6 +212,62 @@ def cache_write(k_new, v_new, slot_ids, k_pool, v_pool, k_scale=None, v_scale=No
     lib = _lib.load()
     _lib.check(lib.pa_cache_write(ctypes.byref(w), ctypes.c_void_p(_stream_handle(stream))))
     return k_pool
+
+
+def prefill(out, q, q_start, k_pool, v_pool, block_table, seq_lens, *, max_q_len: int, window=0, scale=None,
+            max_seq_len: Optional[int] = None, k_scale=None, v_scale=None, ring_blocks=0, stream=None,
+            timing=None):
+    """Causal attention of packed query chunks over their sequences' paged caches. Writes and returns ``out``.
+
+    Sequence b's queries are rows q_start[b] .. q_start[b+1]-1 of q; the chunk's own
+    keys and values must already be in the cache. ``max_q_len`` (a host integer, no
+    device read) bounds every sequence's query count and sizes the launch.
+    """
+    torch = _torch()
+    tensors = [t for t in (out, q, q_start, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale) if t is not None]
+    dev = q.device
+    for t in tensors:
+        _require(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+        _require(t.is_contiguous(), "all tensors must be contiguous")
+    _require(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype, "q/out must be [total, Hq, D]")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype,
+             "k_pool/v_pool must be [num_blocks, block_size, Hkv, D] of one dtype")
+    _require(q_start.dtype == torch.int32 and q_start.dim() == 1, "q_start must be int32 [B+1]")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table must be int32 [B, max_blocks]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens must be int32 [B]")
+    total, Hq, D = q.shape
+    nb, bs, Hkv, Dk = k_pool.shape
+    B = seq_lens.shape[0]
+    _require(Dk == D and q_start.shape[0] == B + 1 and block_table.shape[0] == B, "shape mismatch")
+    per_head = 0
+    for sc in (k_scale, v_scale):
+        if sc is not None:
+            _require(sc.dtype == torch.float32 and tuple(sc.shape) in ((nb, Hkv, bs), (Hkv,)),
+                     "scales must be float32 [nb, Hkv, bs] (per token) or [Hkv] (per head)")
+            per_head = int(tuple(sc.shape) == (Hkv,))
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 1   # host sync; pass it to avoid one
+    a = _lib.PaPrefillArgs()
+    a.out, a.q, a.q_start = _ptr(out), _ptr(q), _ptr(q_start)
+    a.k_pool, a.v_pool = _ptr(k_pool), _ptr(v_pool)
+    a.k_scale, a.v_scale = _ptr(k_scale) or None, _ptr(v_scale) or None
+    a.block_table, a.seq_lens = _ptr(block_table), _ptr(seq_lens)
+    a.num_seqs, a.total_q, a.max_q_len = B, total, int(max_q_len)
+    a.num_q_heads, a.num_kv_heads, a.head_dim = Hq, Hkv, D
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = bs, nb, block_table.shape[1]
+    a.max_seq_len = int(max_seq_len)
+    a.window = int(window)
+    a.scale = float(D ** -0.5 if scale is None else scale)
+    a.q_dtype = _dtype_code(q, allow_int8=False)
+    a.kv_dtype = _dtype_code(k_pool, allow_int8=True)
+    a.ring_blocks = int(ring_blocks)
+    a.scale_per_head = per_head
+    if timing is not None:
+        a.timing_start = getattr(timing[0], "cuda_event", timing[0])
+        a.timing_stop = getattr(timing[1], "cuda_event", timing[1])
+    lib = _lib.load()
+    _lib.check(lib.pa_prefill(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+    return out
 
 
 def plan(q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None, k_scale=None,

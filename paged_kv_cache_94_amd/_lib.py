@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 0, 1, 2, 3, 4, 5
 
-EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write",
+EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write", "pa_prefill",
             "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version",
             "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_add_ring", "pa_alloc_append",
             "pa_alloc_append_batch",
@@ -91,6 +91,38 @@ class PaWriteArgs(ctypes.Structure):
     ]
 
 
+class PaPrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("out", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("q_start", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("ring_blocks", ctypes.c_int32),
+        ("scale_per_head", ctypes.c_int32),
+        ("timing_start", ctypes.c_void_p),
+        ("timing_stop", ctypes.c_void_p),
+    ]
+
+
 class PaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{msg} (code {code})")
@@ -120,6 +152,8 @@ def load(path: str = LIB_PATH):
             fn = getattr(lib, name)
             fn.argtypes = [P, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        lib.pa_prefill.argtypes = [ctypes.POINTER(PaPrefillArgs), ctypes.c_void_p]
+        lib.pa_prefill.restype = ctypes.c_int
         lib.pa_cache_write.argtypes = [ctypes.POINTER(PaWriteArgs), ctypes.c_void_p]
         lib.pa_cache_write.restype = ctypes.c_int
         lib.pa_debug_gather.argtypes = [P, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]

@@ -103,8 +103,30 @@ def append_bytes(tokens: int, *, num_kv_heads: int, head_dim: int, src_dtype: st
     return int(tokens * (8 + num_kv_heads * per_row * (1 if v_shares_k else 2)))
 
 
+def prefill_flops(seq_lens, q_lens, *, num_q_heads: int, head_dim: int, window: int) -> int:
+    """4 * D per (query row, visible key) for packed chunks: query t of a chunk of n
+    sits at L - n + t and sees min(p + 1, W) keys (p + 1 without a window)."""
+    total = 0
+    for L, n in zip(np.asarray(seq_lens, dtype=np.int64), np.asarray(q_lens, dtype=np.int64)):
+        p = np.arange(L - n, L)
+        vis = p + 1 if window <= 0 else np.minimum(p + 1, window)
+        total += int(vis.sum())
+    return 4 * head_dim * num_q_heads * total
+
+
 def for_inputs(x) -> dict:
     """Byte / flop accounting for a PagedInputs-like object."""
+    if getattr(x, "q_start", None) is not None:   # packed prefill chunks
+        q_lens = np.diff(x.q_start)
+        e = _ELEM[x.kv_dtype] * (1 if x.v_pool is x.k_pool else 2)
+        keys = sum(int(min(L, x.window + n - 1)) if x.window > 0 else int(L) for L, n in zip(x.seq_lens, q_lens))
+        kv = keys * x.num_kv_heads * x.head_dim * e
+        return {
+            "alg_bytes": int(kv + 2 * x.q.size * 2),
+            "flops": prefill_flops(x.seq_lens, q_lens, num_q_heads=x.num_q_heads, head_dim=x.head_dim,
+                                   window=x.window),
+            "queries": int(x.q_start[-1]),
+        }
     kw = dict(q_len=x.q_len, num_kv_heads=x.num_kv_heads, head_dim=x.head_dim, kv_dtype=x.kv_dtype,
               window=x.window, v_shares_k=x.v_pool is x.k_pool,
               token_scales=x.k_scale is None or x.k_scale.ndim == 3)

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_valu.hip", "pa_mfma.hip", "pa_aux.hip", "pa_write.hip"]
+SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_valu.hip", "pa_mfma.hip", "pa_aux.hip", "pa_write.hip", "pa_prefill.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -14,6 +14,7 @@
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_error.h"
+#include "pa_prefill.h"
 #include "pa_write.h"
 
 namespace pa {
@@ -449,6 +450,80 @@ int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
                                               reinterpret_cast<hipEvent_t>(a->timing_stop), &supported);
   if (!supported) return fail(PA_ERR_UNSUPPORTED, "no append kernel for these dtypes / head_dim");
   if (e != hipSuccess) return fail(PA_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_prefill(const pa_prefill_args* a, pa_stream_t stream) {
+  pa::clear_error();
+  if (!a) return fail(PA_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 0 || a->total_q < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs and total_q must be >= 0");
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->block_size != pa::kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", a->block_size);
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256 (got %d)", a->head_dim);
+  if (a->q_dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill takes bf16 queries");
+  if (a->kv_dtype != PA_BF16 && a->kv_dtype != PA_INT8)
+    return fail(PA_ERR_UNSUPPORTED, "prefill takes a bf16 or int8 cache");
+  const int G = a->num_q_heads / a->num_kv_heads;
+  const int rows = pa::prefill_rows(a->head_dim);
+  if (G > rows) return fail(PA_ERR_UNSUPPORTED, "query group of %d heads exceeds %d rows", G, rows);
+  if (!std::isfinite(a->scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (a->num_blocks < 1 || a->max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks and max_blocks_per_seq must be >= 1");
+  if (a->scale_per_head != 0 && (a->scale_per_head != 1 || a->kv_dtype != PA_INT8))
+    return fail(PA_ERR_INVALID_ARG, "scale_per_head is 0, or 1 for an int8 cache");
+  if (a->kv_dtype == PA_INT8 && (!a->k_scale || !a->v_scale))
+    return fail(PA_ERR_INVALID_ARG, "an int8 cache needs k_scale and v_scale");
+  if (a->num_seqs == 0 || a->total_q == 0) return PA_OK;
+  if (a->max_q_len < 1) return fail(PA_ERR_INVALID_ARG, "max_q_len must be >= 1");
+  if (a->max_seq_len < a->max_q_len)
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= max_q_len (%d)", a->max_seq_len, a->max_q_len);
+  if (a->ring_blocks < 0) return fail(PA_ERR_INVALID_ARG, "ring_blocks must be >= 0");
+  if (a->ring_blocks > 0) {
+    if (a->window <= 0) return fail(PA_ERR_INVALID_ARG, "a ring cache needs a window");
+    if (a->ring_blocks > a->max_blocks_per_seq)
+      return fail(PA_ERR_INVALID_ARG, "ring_blocks exceeds max_blocks_per_seq");
+    if ((int64_t)a->ring_blocks * a->block_size < (int64_t)a->window + a->max_q_len - 1)
+      return fail(PA_ERR_INVALID_ARG, "a ring of %d blocks cannot hold window + max_q_len - 1 keys", a->ring_blocks);
+  } else if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size) {
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len (%d) exceeds max_blocks_per_seq * block_size", a->max_seq_len);
+  }
+  if (!a->out || !a->q || !a->q_start || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  for (const void* ptr : {(const void*)a->out, a->q, a->k_pool, a->v_pool})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "q, out and the pools must be 16-byte aligned");
+  pa::PrefillParams p{};
+  p.out = a->out;
+  p.q = a->q;
+  p.q_start = a->q_start;
+  p.k_pool = a->k_pool;
+  p.v_pool = a->v_pool;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.B = a->num_seqs;
+  p.Hq = a->num_q_heads;
+  p.Hkv = a->num_kv_heads;
+  p.G = G;
+  p.maxb = a->max_blocks_per_seq;
+  p.window = a->window;
+  p.ring = a->ring_blocks;
+  p.head_scales = a->scale_per_head;
+  p.scale_log2 = a->scale * pa::kLog2e;
+  p.qt = rows / G;
+  p.ntiles = (a->max_q_len + p.qt - 1) / p.qt;
+  const int64_t grid = (int64_t)p.ntiles * a->num_seqs * a->num_kv_heads;
+  if (grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
+  bool supported = false;
+  const hipError_t e = pa::launch_prefill(p, a->kv_dtype, a->head_dim, grid, reinterpret_cast<hipStream_t>(stream),
+                                          reinterpret_cast<hipEvent_t>(a->timing_start),
+                                          reinterpret_cast<hipEvent_t>(a->timing_stop), &supported);
+  if (!supported) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this head_dim / dtype");
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -43,32 +43,6 @@
 
 namespace pa {
 
-namespace {
-
-__device__ __forceinline__ uint32_t i8pair_to_bf16(uint32_t w, int byte0) {
-  const float a = (float)(int32_t)(int8_t)(w >> (8 * byte0));
-  const float b = (float)(int32_t)(int8_t)(w >> (8 * byte0 + 8));
-  return pack_bf16(a, b);
-}
-
-// 16 int8 codes widened to 16 bf16 values (exact for |code| <= 127), in order.
-__device__ __forceinline__ void i8x16_to_bf16(const uint4& w, uint4& lo, uint4& hi) {
-  lo = make_uint4(i8pair_to_bf16(w.x, 0), i8pair_to_bf16(w.x, 2), i8pair_to_bf16(w.y, 0), i8pair_to_bf16(w.y, 2));
-  hi = make_uint4(i8pair_to_bf16(w.z, 0), i8pair_to_bf16(w.z, 2), i8pair_to_bf16(w.w, 0), i8pair_to_bf16(w.w, 2));
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// ds_read_b64_tr_b16 at LDS address p (see the layout note above).
-__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(const_cast<lds_char*>((const lds_char*)p)));
-  return __builtin_bit_cast(uint2, v);
-}
-
-}  // namespace
-
 template <int D, int MT, int NW, bool ALIAS>
 struct MfmaLds {
   static constexpr int ROWS = 16 * MT;

@@ -1,0 +1,350 @@
+// pa_prefill.hip -- paged prefill attention on the matrix cores: a chunk of
+// query tokens per sequence, causal among themselves, over the sequence's
+// history already in the paged cache (Lab 5 handout, "Flash Attention": a
+// query block walks only the key blocks the causal rule lets it see, and a
+// window layer also skips the blocks before its window, instead of scoring
+// everything and masking; GQA without repeating K/V heads; an incomplete last
+// tile masked). The softmax is the online form with fp32 state m, l and the
+// accumulator, and O = o / l at the end (same section).
+//
+// Work: one workgroup of four wavefronts per (query tile, sequence, KV head).
+// Its rows are (query token, query head) pairs of that KV head's group --
+// 128 rows (64 at head_dim 256), each wavefront 16 or 32 of them -- so one
+// K/V tile staged in LDS serves every row. Tiles of late query tokens, which
+// see the most keys, are dispatched first.
+//
+// Per step of 32 keys (two cache blocks): every thread loads 16-byte pieces
+// of the K and V rows along the cached rows and writes them to LDS as bf16
+// (int8 codes widen exactly); the next step's loads are in flight while the
+// current step is computed from the other LDS buffer. The MFMA operand
+// layouts are those of the decode kernel: S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (Q^T in registers), the softmax lane-local per row
+// with a 4-lane max, and O^T += V^T [P_hi; P_lo] with V^T read transposed by
+// ds_read_b64_tr_b16. Keys outside the tile's range are staged as zeros and
+// every score outside a row's [first visible key, own position] is removed
+// by select.
+#include <hip/hip_ext.h>
+
+#include "pa_device.h"
+#include "pa_prefill.h"
+
+namespace pa {
+
+template <bool INT8, int D>
+struct PrefillShape {
+  static constexpr int NW = 4;
+  static constexpr int MT = prefill_rows(D) / (NW * 16);   // 16-row tiles per wavefront
+  static constexpr int C = D / 32;                         // contraction chunks of S^T
+  static constexpr int TJ = D / 16;                        // 16-dim output tiles
+  static constexpr int KB = 32;                            // keys per step
+  static constexpr int EB = INT8 ? 1 : 2;
+  static constexpr int ROW_BYTES = D * EB;
+  static constexpr int LPR = ROW_BYTES / 16;               // 16-byte pieces per cached row
+  static constexpr int NP = 2 * KB * LPR / (NW * 64);      // K and V pieces per thread per step
+  static constexpr int RS = D * 2 + 32;                    // LDS row stride: bf16 row + 32-byte skew
+  static constexpr int TILE = KB * RS;
+  static constexpr int STAGE = 2 * TILE + 2 * KB * 4;      // K tile, V tile, K and V scales
+  static constexpr int BYTES = 2 * STAGE;                  // double buffered
+  static_assert(NP >= 1 && (2 * KB * LPR) % (NW * 64) == 0, "piece split");
+};
+
+template <bool INT8, int D>
+__global__ void __launch_bounds__(256) pa_prefill_kernel(const PrefillParams p) {
+  using S = PrefillShape<INT8, D>;
+  constexpr int MT = S::MT, C = S::C, TJ = S::TJ, KB = S::KB, LPR = S::LPR, NP = S::NP, RS = S::RS;
+  constexpr int ROW_BYTES = S::ROW_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
+
+  // The workgroup's tile: late query tiles first.
+  const int32_t units = p.B * p.Hkv;
+  const int32_t tile = p.ntiles - 1 - (int32_t)(blockIdx.x / units);
+  const int32_t u = (int32_t)(blockIdx.x % units);
+  const int32_t b = u / p.Hkv;
+  const int32_t g = u - b * p.Hkv;
+  const int32_t qs = p.q_start[b];
+  const int32_t qn = p.q_start[b + 1] - qs;
+  const int32_t t0 = tile * p.qt;
+  if (t0 >= qn) return;
+  const int32_t L = p.seq_lens[b];
+  if (L < qn || (p.ring == 0 && (int64_t)L > (int64_t)p.maxb * kBlock)) return;   // broken precondition
+  const int32_t tcount = min(p.qt, qn - t0);
+  const int32_t pos_first = L - qn + t0;                    // position of the tile's first query
+  const int32_t khi = pos_first + tcount - 1;               // last key any row sees (its own position)
+  const int32_t klo = p.window > 0 ? max(0, pos_first - p.window + 1) : 0;
+  const int32_t blk_lo = klo / kBlock;
+  const int32_t nsteps = (khi / kBlock - blk_lo) / 2 + 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int q4 = lane >> 4;
+
+  // Rows of this lane: tile mt holds rows (wave*MT + mt)*16 + n; row r is
+  // query token r / G of the tile and head g*G + r % G.
+  bf16x8 qt[MT][C];
+  int32_t row_lo[MT], row_hi[MT], row_tok[MT], row_head[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = (wave * MT + mt) * 16 + n;
+    const int32_t tt = r / p.G;
+    const bool live = tt < tcount;
+    const int32_t pos = pos_first + tt;
+    row_tok[mt] = live ? tt : -1;
+    row_head[mt] = g * p.G + (r - tt * p.G);
+    row_lo[mt] = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+    row_hi[mt] = live ? pos : -1;
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       ((size_t)(qs + t0 + (live ? tt : 0)) * p.Hq + row_head[mt]) * (size_t)D * 2;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (live) v = load16(qrow + (32 * c + 8 * q4) * 2);
+      qt[mt][c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  float ksh = 1.f, vsh = 1.f;   // per-head int8 scales
+  if constexpr (INT8) {
+    if (p.head_scales) {
+      ksh = p.k_scale[g];
+      vsh = p.v_scale[g];
+    }
+  }
+
+  f32x4 o[MT][TJ];
+  float m[MT], l[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    m[mt] = -INFINITY;
+    l[mt] = 0.f;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) o[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // This thread's pieces of a step: piece pi = tid + 256*k is K (pi < 32*LPR)
+  // or V, cached row (pi % (32*LPR)) / LPR of the step, 16-byte chunk pi % LPR.
+  // A wavefront's 64 pieces of one k lie in one half (one cache block) of one
+  // of K and V, so its buffer descriptor is wave-uniform.
+  const int32_t tok_stride = p.Hkv * ROW_BYTES;
+  const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
+  const int32_t* table = p.block_table + (size_t)b * p.maxb;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
+  const bool token_scales = INT8 && !p.head_scales;
+
+  uint4 ld[NP];
+  float lsc = 0.f;
+  // Issue the loads of step s (the block pair blk_lo + 2s, +1; a block past
+  // the range loads zero bytes).
+  auto issue = [&](int32_t s) __attribute__((always_inline)) {
+    const int32_t i0 = blk_lo + 2 * s;
+    const bool has1 = (i0 + 1) * kBlock <= khi;
+    const int32_t ph0 = table[table_entry(p, i0)];
+    const int32_t ph1 = has1 ? table[table_entry(p, i0 + 1)] : 0;
+    const size_t t0b = (size_t)ph0 * kBlock * (size_t)tok_stride;
+    const size_t t1b = (size_t)ph1 * kBlock * (size_t)tok_stride;
+    const auto k0 = buffer_rsrc(kpool + t0b, tile_bytes);
+    const auto k1 = buffer_rsrc(kpool + t1b, has1 ? tile_bytes : 0);
+    const auto v0 = buffer_rsrc(vpool + t0b, tile_bytes);
+    const auto v1 = buffer_rsrc(vpool + t1b, has1 ? tile_bytes : 0);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int base = 64 * wave + 256 * k;                 // wave-uniform
+      const bool isv = base >= KB * LPR;
+      const bool hi_half = (base % (KB * LPR)) / LPR >= kBlock;
+      const int rem = (base % (KB * LPR)) + lane;
+      const int voff = ((rem / LPR) % kBlock) * tok_stride + 16 * (rem % LPR);
+      const auto d = isv ? (hi_half ? v1 : v0) : (hi_half ? k1 : k0);
+      ld[k] = buffer_load16<0>(d, voff);
+    }
+    // Scales: lanes 0..31 of wavefront 0 (K) and 1 (V), one key each. A key of
+    // a missing second block reads block 0's scale, which the masks ignore.
+    if (token_scales && wave < 2 && lane < KB) {
+      const float* sc = wave == 0 ? p.k_scale : p.v_scale;
+      const int32_t ph = lane < kBlock ? ph0 : ph1;
+      lsc = sc[((size_t)ph * p.Hkv + g) * kBlock + (lane % kBlock)];
+    }
+  };
+  // Write step s's loaded pieces into LDS buffer `buf` as bf16; keys outside
+  // [klo, khi] are written as zeros.
+  auto stage = [&](int32_t s, char* buf) __attribute__((always_inline)) {
+    const int32_t key0 = (blk_lo + 2 * s) * kBlock;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int pi = tid + 256 * k;
+      const bool isv = pi >= KB * LPR;
+      const int rem = pi % (KB * LPR);
+      const int row = rem / LPR;
+      const int chunk = rem % LPR;
+      const int32_t key = key0 + row;
+      const bool ok = key >= klo && key <= khi;
+      uint4 w = ld[k];
+      w.x = ok ? w.x : 0u;
+      w.y = ok ? w.y : 0u;
+      w.z = ok ? w.z : 0u;
+      w.w = ok ? w.w : 0u;
+      char* dst = buf + (isv ? S::TILE : 0) + row * RS;
+      if constexpr (INT8) {
+        uint4 lo, hi;
+        i8x16_to_bf16(w, lo, hi);
+        *reinterpret_cast<uint4*>(dst + 32 * chunk) = lo;
+        *reinterpret_cast<uint4*>(dst + 32 * chunk + 16) = hi;
+      } else {
+        *reinterpret_cast<uint4*>(dst + 16 * chunk) = w;
+      }
+    }
+    if (token_scales && wave < 2 && lane < KB) reinterpret_cast<float*>(buf + 2 * S::TILE)[wave * KB + lane] = lsc;
+  };
+
+  // Step s from LDS buffer `buf`.
+  auto compute = [&](int32_t s, const char* buf) __attribute__((always_inline)) {
+    const int32_t key0 = (blk_lo + 2 * s) * kBlock;
+    const char* kst = buf;
+    const char* vst = buf + S::TILE;
+    const float* sst = reinterpret_cast<const float*>(buf + 2 * S::TILE);
+    // S^T for both 16-key halves: lane l gets query row n, keys 16*half + 4*q4 .. +3.
+    f32x4 sacc[MT][2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const char* kread = kst + (16 * half + n) * RS + 16 * q4;
+      bf16x8 kop[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kread + 64 * c));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c], qt[mt][c], acc, 0, 0, 0);
+        sacc[mt][half] = acc;
+      }
+    }
+    float ksc[8], vsc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ksc[e] = ksh;
+      vsc[e] = vsh;
+    }
+    if (token_scales) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float4 a = *reinterpret_cast<const float4*>(sst + 16 * half + 4 * q4);
+        const float4 v = *reinterpret_cast<const float4*>(sst + KB + 16 * half + 4 * q4);
+        ksc[4 * half + 0] = a.x; ksc[4 * half + 1] = a.y; ksc[4 * half + 2] = a.z; ksc[4 * half + 3] = a.w;
+        vsc[4 * half + 0] = v.x; vsc[4 * half + 1] = v.y; vsc[4 * half + 2] = v.z; vsc[4 * half + 3] = v.w;
+      }
+    }
+    // Online softmax per row over the step's 32 keys; P leaves as hi/lo bf16 parts.
+    bf16x8 pbv[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float sc[8];
+      bool ok[8];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int32_t j = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
+        ok[e] = j >= row_lo[mt] && j <= row_hi[mt];
+        float x = sacc[mt][e >> 2][e & 3] * p.scale_log2;
+        if constexpr (INT8) x *= ksc[e];
+        sc[e] = ok[e] ? x : -INFINITY;
+        mb = fmaxf(mb, sc[e]);
+      }
+      mb = quads16_max(mb);
+      const float mn = fmaxf(m[mt], mb);
+      const bool grow = mn > m[mt];
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float a = grow ? fast_exp2(m[mt] - mn) : 1.f;
+        l[mt] *= a;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) o[mt][j] *= a;
+        m[mt] = mn;
+      }
+      const float msafe = m[mt] == -INFINITY ? 0.f : m[mt];
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pe[e] = fast_exp2(sc[e] - msafe);
+        l[mt] += pe[e];
+        if constexpr (INT8) pe[e] = ok[e] ? pe[e] * vsc[e] : 0.f;
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = pe[4 * half + e];
+          lo[e] = hi[e] - __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)hi[e]) << 16);
+        }
+        pbv[mt][half] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]),
+                                                              pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])));
+      }
+    }
+    // O^T += V^T [P_hi; P_lo] for each half, V^T read transposed from LDS.
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const char* vread = vst + (16 * half + 4 * q4 + (n >> 2)) * RS + 8 * (n & 3);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const uint2 a = lds_read_tr16(vread + 32 * j);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, a.x, a.y));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv[mt][half], o[mt][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // Double-buffered key loop: step s+1's loads are in flight while step s is
+  // computed; one barrier per step (buffer s&1 is rewritten two steps later,
+  // after every wavefront has passed the barrier that follows its last read).
+  issue(0);
+  for (int32_t s = 0; s < nsteps; ++s) {
+    char* buf = smem + (s & 1) * S::STAGE;
+    stage(s, buf);
+    if (s + 1 < nsteps) issue(s + 1);
+    __syncthreads();
+    compute(s, buf);
+  }
+
+  // Row sums (the four lanes of a row each hold a quarter of the keys), then O / l.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) l[mt] = quads16_sum(l[mt]);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (row_tok[mt] < 0) continue;
+    const float inv = 1.f / l[mt];
+    __bf16* out = reinterpret_cast<__bf16*>(p.out) + ((size_t)(qs + t0 + row_tok[mt]) * p.Hq + row_head[mt]) * D + 4 * q4;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const f32x4 v = o[mt][j];
+      *reinterpret_cast<uint2*>(out + 16 * j) =
+          make_uint2(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv));
+    }
+  }
+}
+
+namespace {
+template <bool INT8>
+hipError_t by_dim(const PrefillParams& p, int D, int64_t grid, hipStream_t st, hipEvent_t t0, hipEvent_t t1,
+                  bool* ok) {
+  *ok = true;
+  const dim3 g((unsigned)grid), blk(256);
+  switch (D) {
+    case 64: hipExtLaunchKernelGGL((pa_prefill_kernel<INT8, 64>), g, blk, 0, st, t0, t1, 0, p); break;
+    case 128: hipExtLaunchKernelGGL((pa_prefill_kernel<INT8, 128>), g, blk, 0, st, t0, t1, 0, p); break;
+    case 256: hipExtLaunchKernelGGL((pa_prefill_kernel<INT8, 256>), g, blk, 0, st, t0, t1, 0, p); break;
+    default: *ok = false; return hipSuccess;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int kv_dtype, int D, int64_t grid, hipStream_t st,
+                          hipEvent_t start, hipEvent_t stop, bool* supported) {
+  *supported = false;
+  if (kv_dtype == 2) return by_dim<true>(p, D, grid, st, start, stop, supported);
+  if (kv_dtype == 1) return by_dim<false>(p, D, grid, st, start, stop, supported);
+  return hipSuccess;
+}
+
+}  // namespace pa

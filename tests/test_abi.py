@@ -55,6 +55,7 @@ int main(void) {
   printf("pa_args.size %zu\n", sizeof(pa_args));
   printf("pa_plan_info.size %zu\n", sizeof(pa_plan_info));
   printf("pa_write_args.size %zu\n", sizeof(pa_write_args));
+  printf("pa_prefill_args.size %zu\n", sizeof(pa_prefill_args));
   %FIELDS%
   return 0;
 }
@@ -62,6 +63,7 @@ int main(void) {
     fields = "".join(f"F(pa_args, {f})" for f, _ in _lib.PaArgs._fields_)
     fields += "".join(f"F(pa_plan_info, {f})" for f, _ in _lib.PaPlanInfo._fields_)
     fields += "".join(f"F(pa_write_args, {f})" for f, _ in _lib.PaWriteArgs._fields_)
+    fields += "".join(f"F(pa_prefill_args, {f})" for f, _ in _lib.PaPrefillArgs._fields_)
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "layout.c")
         open(c, "w").write(src.replace("%FIELDS%", fields))
@@ -76,6 +78,9 @@ int main(void) {
     for f, _ in _lib.PaPlanInfo._fields_:
         assert int(got[f"pa_plan_info.{f}"]) == getattr(_lib.PaPlanInfo, f).offset, f
     assert int(got["pa_write_args.size"]) == ctypes.sizeof(_lib.PaWriteArgs)
+    assert int(got["pa_prefill_args.size"]) == ctypes.sizeof(_lib.PaPrefillArgs)
+    for f, _ in _lib.PaPrefillArgs._fields_:
+        assert int(got[f"pa_prefill_args.{f}"]) == getattr(_lib.PaPrefillArgs, f).offset, f
     for f, _ in _lib.PaWriteArgs._fields_:
         assert int(got[f"pa_write_args.{f}"]) == getattr(_lib.PaWriteArgs, f).offset, f
 
@@ -196,6 +201,43 @@ def _wargs(**kw):
 def test_cache_write_rejects_bad_arguments(lib, kw, code):
     assert lib.pa_cache_write(ctypes.byref(_wargs(**kw)), None) == code
     assert lib.pa_last_error()
+
+
+def _pargs(**kw):
+    a = _lib.PaPrefillArgs()
+    base = dict(out=16, q=16, q_start=8, k_pool=16, v_pool=32, block_table=8, seq_lens=8, num_seqs=4, total_q=512,
+                max_q_len=256, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=1000,
+                max_blocks_per_seq=512, max_seq_len=8192, window=0, scale=0.088, q_dtype=_lib.PA_BF16,
+                kv_dtype=_lib.PA_BF16)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=12), _lib.PA_ERR_INVALID_ARG),
+    (dict(q_dtype=_lib.PA_F32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=_lib.PA_F32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=256, num_kv_heads=1, head_dim=256), _lib.PA_ERR_UNSUPPORTED),   # group > 64 rows
+    (dict(kv_dtype=_lib.PA_INT8), _lib.PA_ERR_INVALID_ARG),                       # scales missing
+    (dict(max_q_len=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(max_seq_len=100), _lib.PA_ERR_INVALID_ARG),                             # < max_q_len
+    (dict(max_seq_len=9000), _lib.PA_ERR_INVALID_ARG),                            # > table capacity
+    (dict(window=64, ring_blocks=8, max_blocks_per_seq=8), _lib.PA_ERR_INVALID_ARG),   # 128 < 64 + 255
+    (dict(q_start=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(q=8), _lib.PA_ERR_INVALID_ARG),                                         # misaligned
+    (dict(scale=float("inf")), _lib.PA_ERR_INVALID_ARG),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, code):
+    assert lib.pa_prefill(ctypes.byref(_pargs(**kw)), None) == code
+    assert lib.pa_last_error()
+
+
+def test_prefill_empty_enqueues_nothing(lib):
+    assert lib.pa_prefill(ctypes.byref(_pargs(total_q=0, out=0, q=0)), None) == 0
+    assert lib.pa_prefill(ctypes.byref(_pargs(num_seqs=0)), None) == 0
 
 
 def test_cache_write_zero_tokens_enqueues_nothing(lib):

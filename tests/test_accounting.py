@@ -69,3 +69,15 @@ def test_append_bytes_by_hand():
     # A float cache with V sharing K: one copy of each row.
     assert accounting.append_bytes(5, num_kv_heads=1, head_dim=256, src_dtype="bf16", kv_dtype="bf16",
                                    v_shares_k=True) == 5 * (8 + 256 * 4)
+
+
+def test_prefill_flops_by_enumeration():
+    # Count (query row, visible key) pairs one by one for a small packed batch.
+    lens, q_lens, hq, d = [10, 40, 7], [3, 40, 0], 4, 64
+    for window in (0, 5):
+        pairs = 0
+        for L, n in zip(lens, q_lens):
+            for t in range(n):
+                p = L - n + t
+                pairs += sum(1 for j in range(L) if j <= p and (window <= 0 or p - j < window))
+        assert accounting.prefill_flops(lens, q_lens, num_q_heads=hq, head_dim=d, window=window) == 4 * d * hq * pairs

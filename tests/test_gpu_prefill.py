@@ -1,0 +1,127 @@
+"""GPU parity of the paged prefill kernel (pa_prefill) against the oracle, through the C ABI.
+
+Packed per-sequence query chunks with cached history (Lab 5, "Flash
+Attention"): empty and one-token chunks, chunks spanning many query tiles
+with ragged last tiles, histories of zero and of thousands of tokens,
+windows and rings, GQA groups 1-16, head_dim 64/128/256, bf16 and int8
+caches (per-token and per-head scales), poisoned unseen slots. Bar: max |err|
+<= 1e-2 against the fp64 oracle (bf16 output).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_94_amd as pa
+from tests.gpu_util import TOL, Dev, max_err, to_torch
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# (history lens, q_lens, Hq, Hkv, D, window, kv_dtype, extra)
+CASES = [
+    ([0, 10, 33], [37, 5, 16], 4, 2, 64, 0, "bf16", {}),
+    ([0, 0, 100], [1, 64, 70], 8, 1, 128, 0, "bf16", {}),
+    ([5, 200, 17], [90, 33, 0], 8, 2, 64, 40, "bf16", {}),
+    ([64, 3], [48, 129], 16, 2, 128, 0, "int8", {}),
+    ([300], [100], 6, 3, 64, 16, "bf16", {}),
+    ([0, 500], [300, 257], 16, 8, 256, 100, "bf16", {}),
+    ([1000], [600], 16, 1, 256, 0, "bf16", {}),
+    ([40, 7, 0], [1, 1, 1], 64, 8, 128, 0, "int8", {"head_scales": True}),
+    ([200, 70], [40, 70], 8, 2, 128, 64, "bf16", {"ring": True}),
+    ([2048, 0], [1024, 2048], 32, 8, 128, 0, "bf16", {}),
+    ([33, 900], [77, 300], 8, 8, 128, 0, "int8", {"head_scales": True}),
+    ([0, 4000], [513, 96], 16, 2, 256, 1024, "bf16", {"ring": True}),
+]
+
+
+def _ids(c):
+    return "h%s_q%s_g%d-%d_d%d_w%d_%s%s" % ("-".join(map(str, c[0][:3])), "-".join(map(str, c[1][:3])), c[2], c[3],
+                                            c[4], c[5], c[6], "".join(sorted(c[7])))
+
+
+def _inputs(c, seed):
+    hist, ql, hq, hkv, d, w, kd, extra = c
+    lens = [h + q for h, q in zip(hist, ql)]
+    return make_inputs(lens, q_len=1, q_lens=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, q_dtype="bf16",
+                       kv_dtype=kd, window=w, seed=seed, poison=True, **extra)
+
+
+def run_prefill(x, timing=None):
+    dev = Dev(x)
+    qs = to_torch(x.q_start)
+    out = torch.full_like(dev.q, float("nan"))
+    pa.prefill(out, dev.q, qs, dev.k, dev.v, dev.table, dev.lens, max_q_len=x.q_len, window=x.window,
+               scale=x.scale, max_seq_len=x.max_seq_len, k_scale=dev.ks, v_scale=dev.vs, ring_blocks=x.ring_blocks,
+               timing=timing)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("c", CASES, ids=_ids)
+def test_prefill_matches_oracle(c):
+    x = _inputs(c, 900 + CASES.index(c))
+    _log(f"prefill {_ids(c)}: total {x.q.shape[0]} queries, ring {x.ring_blocks}")
+    got = run_prefill(x).float().cpu().numpy().astype(np.float64)
+    ref = oracle.attention(oracle.Problem.from_inputs(x))
+    assert got.shape == ref.shape
+    assert not np.isnan(got).any()
+    err = max_err(got, ref)
+    _log(f"  max|err| = {err:.3e}")
+    assert err <= TOL[c[6]]
+
+
+def test_prefill_one_token_chunks_match_decode():
+    # A chunk of one token per sequence is a decode step: both kernels against each other and the oracle.
+    c = ([100, 7, 3000, 16], [1, 1, 1, 1], 16, 2, 128, 0, "bf16", {})
+    x = _inputs(c, 5)
+    got = run_prefill(x).float().cpu().numpy().astype(np.float64)
+    y = make_inputs(x.seq_lens, q_len=1, num_q_heads=16, num_kv_heads=2, head_dim=128, q_dtype="bf16",
+                    kv_dtype="bf16", seed=5, poison=True)
+    y.q[:] = x.q.reshape(y.q.shape)
+    y.k_pool[:] = x.k_pool
+    y.v_pool[:] = x.v_pool
+    y.block_table[:] = x.block_table
+    dec = Dev(y).run_f64()
+    assert max_err(got, dec.reshape(got.shape)) <= 2 * TOL["bf16"]
+    assert max_err(got, oracle.attention(oracle.Problem.from_inputs(x))) <= TOL["bf16"]
+
+
+def test_prefill_empty_sequences_write_nothing():
+    c = ([5, 9, 3], [0, 20, 0], 8, 2, 64, 0, "bf16", {})
+    x = _inputs(c, 6)
+    out = run_prefill(x)
+    assert not torch.isnan(out).any() and out.shape[0] == 20
+    err = max_err(out.float().cpu().numpy().astype(np.float64), oracle.attention(oracle.Problem.from_inputs(x)))
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_prefill_full_size_workloads(idx):
+    # The benchmark's prefill workloads at full size: a seeded sample of rows, plus every head of each
+    # sequence's first and last query, against the oracle row by row.
+    from workloads import make_prefill_config
+    x = make_prefill_config(idx, poison=True)
+    _log(f"{x.name}: {x.q.shape[0]} queries, lens {list(x.seq_lens)}")
+    got = run_prefill(x).float().cpu().numpy().astype(np.float64).reshape(-1, x.head_dim)
+    hq = x.num_q_heads
+    rng = np.random.default_rng(idx)
+    rows = set(rng.integers(0, got.shape[0], 1500).tolist())
+    for b in range(x.batch):
+        for tok in (int(x.q_start[b]), int(x.q_start[b + 1]) - 1):
+            rows.update(range(tok * hq, tok * hq + hq))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref = oracle.attention(oracle.Problem.from_inputs(x), rows=rows)
+    sub = got[rows]
+    assert not np.isnan(sub).any()
+    err = max_err(sub, ref)
+    _log(f"{x.name}: max|err| over {rows.size} rows = {err:.3e}")
+    assert err <= TOL[x.kv_dtype]

@@ -7,9 +7,11 @@ attention arithmetic and imports neither the HIP library nor the oracle.
 
 from .gen import (  # noqa: F401
     CONFIGS,
+    PREFILL_CONFIGS,
     PagedInputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_config,
     make_inputs,
+    make_prefill_config,
 )

@@ -358,6 +358,31 @@ CONFIGS = {
 }
 
 
+# Prefill chunks (Lab 5, "Flash Attention": prefill with q_len > 1 over cached
+# history, global and window layers). Each sequence brings `chunk` query
+# tokens after a history drawn from `hist`; shapes are those of the decode
+# workloads' layers.
+PREFILL_CONFIGS = {
+    1: dict(name="gemma4-12b-local-prefill", B=4, chunk=2048, hist="uniform:0,6144", Hq=16, Hkv=8, D=256,
+            window=1024, kv_dtype="bf16"),
+    2: dict(name="gemma4-12b-global-prefill", B=2, chunk=4096, hist="uniform:0,4096", Hq=16, Hkv=1, D=256,
+            window=0, kv_dtype="bf16", alias_v=True),
+    3: dict(name="gqa70b-int8kv-prefill", B=4, chunk=2048, hist="uniform:0,2048", Hq=64, Hkv=8, D=128,
+            window=0, kv_dtype="int8"),
+}
+
+
+def make_prefill_config(idx: int, *, poison: bool = False) -> PagedInputs:
+    """One of the prefill workloads, seeded with 100 + its number."""
+    c = PREFILL_CONFIGS[idx]
+    rng = np.random.default_rng(100 + idx)
+    hist = _draw_lens(c["hist"], c["B"], rng)
+    q_lens = np.full(c["B"], c["chunk"], dtype=np.int64)
+    return make_inputs(hist + q_lens, q_len=1, q_lens=q_lens, num_q_heads=c["Hq"], num_kv_heads=c["Hkv"],
+                       head_dim=c["D"], q_dtype="bf16", kv_dtype=c["kv_dtype"], window=c["window"], rng=rng,
+                       alias_v=c.get("alias_v", False), poison=poison, name=c["name"], seed=100 + idx)
+
+
 def _draw_lens(spec: str, B: int, rng: np.random.Generator) -> np.ndarray:
     kind, arg = spec.split(":", 1)
     if kind == "fixed":
