@@ -355,6 +355,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Online softmax with a lazily moved reference max: a row's reference moves
+// only when a new score exceeds it by more than this many log2 units, so the
+// accumulator is rescaled rarely; exp2 of (score - reference) stays below
+// 2^kRescaleSlack.
+constexpr float kRescaleSlack = 8.f;
+
 // Copy a freshly loaded value into a register written by a VALU move (a DPP
 // identity permutation). The wait for the load happens once, here; later
 // reads of the copy inside a software-pipelined loop then never make the

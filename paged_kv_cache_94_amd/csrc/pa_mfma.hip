@@ -305,9 +305,12 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
         mb = fmaxf(mb, sc[e]);
       }
       mb = quads16_max(mb);
-      const float mn = fmaxf(m[tile], mb);
-      const bool grow = mn > m[tile];
+      // Lazy rescale: the row's reference max moves only when the block max
+      // passes it by more than kRescaleSlack (log2 units); weights stay below
+      // 2^kRescaleSlack and o / l is unchanged by the choice of reference.
+      const bool grow = mb > m[tile] + kRescaleSlack;   // true for the first visible keys (m = -inf)
       if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mb : m[tile];
         const float a = grow ? fast_exp2(m[tile] - mn) : 1.f;
         l[tile] *= a;
 #pragma unroll

@@ -22,7 +22,13 @@
 // with a 4-lane max, and O^T += V^T [P_hi; P_lo] with V^T read transposed by
 // ds_read_b64_tr_b16. Keys outside the tile's range are staged as zeros and
 // every score outside a row's [first visible key, own position] is removed
-// by select.
+// by select; steps whose keys every row of the tile sees skip the masks.
+//
+// The running max is moved lazily: a row's reference max only changes when
+// its block max exceeds it by more than kRescaleSlack (log2 units), so the
+// accumulator is rescaled a handful of times per row instead of at nearly
+// every step. The softmax is unchanged -- any reference value gives the same
+// o / l -- and the weights stay below 2^kRescaleSlack, far from overflow.
 #include <hip/hip_ext.h>
 
 #include "pa_device.h"
@@ -49,7 +55,8 @@ struct PrefillShape {
 };
 
 template <bool INT8, int D>
-__global__ void __launch_bounds__(256) pa_prefill_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+pa_prefill_kernel(const PrefillParams p) {
   using S = PrefillShape<INT8, D>;
   constexpr int MT = S::MT, C = S::C, TJ = S::TJ, KB = S::KB, LPR = S::LPR, NP = S::NP, RS = S::RS;
   constexpr int ROW_BYTES = S::ROW_BYTES;
@@ -73,6 +80,10 @@ __global__ void __launch_bounds__(256) pa_prefill_kernel(const PrefillParams p) 
   const int32_t klo = p.window > 0 ? max(0, pos_first - p.window + 1) : 0;
   const int32_t blk_lo = klo / kBlock;
   const int32_t nsteps = (khi / kBlock - blk_lo) / 2 + 1;
+  // Keys every row of a full tile sees: [lo_all, pos_first] (the last row's
+  // window start to the first row's position).
+  const bool full_tile = tcount == p.qt && p.qt * p.G == S::NW * MT * 16;
+  const int32_t lo_all = p.window > 0 ? max(0, khi - p.window + 1) : 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,6 +210,7 @@ __global__ void __launch_bounds__(256) pa_prefill_kernel(const PrefillParams p) 
   // Step s from LDS buffer `buf`.
   auto compute = [&](int32_t s, const char* buf) __attribute__((always_inline)) {
     const int32_t key0 = (blk_lo + 2 * s) * kBlock;
+    const bool interior = full_tile && key0 >= lo_all && key0 + KB - 1 <= pos_first;   // wave-uniform
     const char* kst = buf;
     const char* vst = buf + S::TILE;
     const float* sst = reinterpret_cast<const float*>(buf + 2 * S::TILE);
@@ -243,16 +255,16 @@ __global__ void __launch_bounds__(256) pa_prefill_kernel(const PrefillParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int32_t j = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
-        ok[e] = j >= row_lo[mt] && j <= row_hi[mt];
+        ok[e] = interior || (j >= row_lo[mt] && j <= row_hi[mt]);
         float x = sacc[mt][e >> 2][e & 3] * p.scale_log2;
         if constexpr (INT8) x *= ksc[e];
         sc[e] = ok[e] ? x : -INFINITY;
         mb = fmaxf(mb, sc[e]);
       }
       mb = quads16_max(mb);
-      const float mn = fmaxf(m[mt], mb);
-      const bool grow = mn > m[mt];
+      const bool grow = mb > m[mt] + kRescaleSlack;   // true for the first visible keys (m = -inf)
       if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mb : m[mt];
         const float a = grow ? fast_exp2(m[mt] - mn) : 1.f;
         l[mt] *= a;
 #pragma unroll
