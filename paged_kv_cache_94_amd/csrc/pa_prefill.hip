@@ -47,12 +47,49 @@ struct PrefillShape {
   static constexpr int ROW_BYTES = D * EB;
   static constexpr int LPR = ROW_BYTES / 16;               // 16-byte pieces per cached row
   static constexpr int NP = 2 * KB * LPR / (NW * 64);      // K and V pieces per thread per step
-  static constexpr int RS = D * 2 + 32;                    // LDS row stride: bf16 row + 32-byte skew
+  // bf16 caches load straight into LDS (no staging registers), rows 2D bytes
+  // apart with 16-byte chunks XOR-swizzled by row; int8 caches are staged
+  // through registers (widened to bf16), rows padded to 2D + 32 bytes.
+  static constexpr bool DIRECT = !INT8;
+  static constexpr int RS = DIRECT ? D * 2 : D * 2 + 32;  // LDS row stride
   static constexpr int TILE = KB * RS;
-  static constexpr int STAGE = 2 * TILE + 2 * KB * 4;      // K tile, V tile, K and V scales
-  static constexpr int BYTES = 2 * STAGE;                  // double buffered
+  static constexpr int STAGE = 2 * TILE + (INT8 ? 2 * KB * 4 : 0);   // K tile, V tile, int8 scales
+  static constexpr int NSTAGE = DIRECT && 3 * STAGE <= 72 * 1024 ? 3 : 2;
+  static constexpr int BYTES = NSTAGE * STAGE;
+  // Direct loads: one load instruction fills 1 KiB of LDS (64 lanes x 16 bytes),
+  // RPI rows of CPR 16-byte chunks; IPW instructions per wavefront per tile.
+  static constexpr int RPI = 1024 / (D * 2);
+  static constexpr int CPR = D * 2 / 16;
+  static constexpr int IPW = KB / RPI / NW;
   static_assert(NP >= 1 && (2 * KB * LPR) % (NW * 64) == 0, "piece split");
+  static_assert(!DIRECT || (IPW >= 1 && kBlock % RPI == 0), "direct-load split");
 };
+
+// Swizzle of the 16-byte chunks of LDS row `row` (direct-load layout): chunk c
+// of the cached row is stored at chunk c ^ swz(row). Sixteen consecutive rows
+// get distinct swizzles within one 256-byte bank sweep, so the K-operand reads
+// (16 rows, one chunk) and the transposed V reads hit distinct banks.
+template <int D>
+__device__ __forceinline__ int lds_swz(int row) {
+  return D >= 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// s_waitcnt immediate waiting until at most n vector-memory operations are outstanding.
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) & 3) << 14 | (7 << 4) | (15 << 8);
+}
+
+// 16 bytes per lane from buffer `rsrc` at byte `voff` straight into LDS:
+// lane i's bytes land at LDS address lds_base + 16 * i. Issued as assembly so
+// that the compiler does not wait for these loads before every LDS access
+// (it cannot tell which of them an LDS read depends on); the kernel waits for
+// them itself (vmcnt, then a barrier) before reading the buffer they fill.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, int32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "m0");
+}
 
 template <bool INT8, int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -142,6 +179,60 @@ pa_prefill_kernel(const PrefillParams p) {
   const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
   const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
   const bool token_scales = INT8 && !p.head_scales;
+  const bool alias = p.v_pool == p.k_pool;   // V is K: its tile is loaded once and read as both
+
+  // ---- direct-load path (bf16 caches) ----------------------------------------------------------
+  // Step s's loads: the block pair blk_lo + 2s, +1 (a block past the range, or
+  // a step past the last, loads through a zero-byte descriptor, so every step
+  // issues the same number of loads and the waits below can count them).
+  constexpr int NL = S::IPW * 2;   // load instructions per wavefront per step (K and V)
+  // Block ids come 64 at a time, one per lane (logical blocks tbl_base ..
+  // tbl_base + 63), and are picked per step with readlane: the only wait for
+  // a table read happens when a new group of 64 is needed (every 32 steps).
+  const int32_t blk_last = khi / kBlock;
+  int32_t tbl_base = blk_lo;
+  int32_t tbl = settle(table[table_entry(p, min(blk_lo + lane, blk_last))]);
+  auto issue_direct = [&](int32_t s, char* buf) __attribute__((always_inline)) {
+    const bool live = s < nsteps;
+    const int32_t i0 = min(blk_lo + 2 * s, blk_last);
+    const bool has1 = live && (i0 + 1) * kBlock <= khi;
+    if (i0 + 1 >= tbl_base + 64) {           // wave-uniform: next group of block ids
+      tbl_base = i0;
+      tbl = settle(table[table_entry(p, min(tbl_base + lane, blk_last))]);   // the wait stays in this branch
+    }
+    const int32_t ph0 = __builtin_amdgcn_readlane(tbl, i0 - tbl_base);
+    const int32_t ph1 = __builtin_amdgcn_readlane(tbl, (has1 ? i0 + 1 : i0) - tbl_base);
+    const size_t t0b = (size_t)ph0 * kBlock * (size_t)tok_stride;
+    const size_t t1b = (size_t)ph1 * kBlock * (size_t)tok_stride;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {            // K tile, then V tile
+      const char* pool = t == 0 || alias ? kpool : vpool;
+      const bool skip = t == 1 && alias;     // V shares K's tile
+      const auto d0 = buffer_rsrc(pool + t0b, live && !skip ? tile_bytes : 0);
+      const auto d1 = buffer_rsrc(pool + t1b, has1 && !skip ? tile_bytes : 0);
+#pragma unroll
+      for (int k = 0; k < S::IPW; ++k) {
+        const int seg = wave + S::NW * k;    // 1 KiB segment of the tile (wave-uniform)
+        const int row = seg * S::RPI + lane / S::CPR;
+        const int chunk = (lane % S::CPR) ^ lds_swz<D>(row);
+        const int voff = (row % kBlock) * tok_stride + 16 * chunk;
+        char* dst = buf + t * S::TILE + seg * 1024;
+        load_lds16(row < kBlock ? d0 : d1, voff,
+                   (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst));
+      }
+    }
+  };
+  // Zero the rows of step s's tiles whose keys lie outside [klo, khi] (edge steps only).
+  auto zero_edges = [&](int32_t s, char* buf) __attribute__((always_inline)) {
+    const int32_t key0 = (blk_lo + 2 * s) * kBlock;
+    for (int pi = tid; pi < 2 * KB * S::CPR; pi += S::NW * 64) {
+      const int t = pi / (KB * S::CPR);
+      const int row = (pi / S::CPR) % KB;
+      const int32_t key = key0 + row;
+      if (key < klo || key > khi)
+        *reinterpret_cast<uint4*>(buf + t * S::TILE + row * RS + 16 * (pi % S::CPR)) = make_uint4(0, 0, 0, 0);
+    }
+  };
 
   uint4 ld[NP];
   float lsc = 0.f;
@@ -212,16 +303,20 @@ pa_prefill_kernel(const PrefillParams p) {
     const int32_t key0 = (blk_lo + 2 * s) * kBlock;
     const bool interior = full_tile && key0 >= lo_all && key0 + KB - 1 <= pos_first;   // wave-uniform
     const char* kst = buf;
-    const char* vst = buf + S::TILE;
+    const char* vst = S::DIRECT && alias ? buf : buf + S::TILE;
     const float* sst = reinterpret_cast<const float*>(buf + 2 * S::TILE);
     // S^T for both 16-key halves: lane l gets query row n, keys 16*half + 4*q4 .. +3.
     f32x4 sacc[MT][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const char* kread = kst + (16 * half + n) * RS + 16 * q4;
+      const int krow = 16 * half + n;
       bf16x8 kop[C];
 #pragma unroll
-      for (int c = 0; c < C; ++c) kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kread + 64 * c));
+      for (int c = 0; c < C; ++c) {
+        // dims 32c + 8*q4 .. +7: 16-byte chunk 4c + q4 of the row
+        const int chunk = S::DIRECT ? ((4 * c + q4) ^ lds_swz<D>(krow)) : 4 * c + q4;
+        kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kst + krow * RS + 16 * chunk));
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -294,10 +389,13 @@ pa_prefill_kernel(const PrefillParams p) {
     // O^T += V^T [P_hi; P_lo] for each half, V^T read transposed from LDS.
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const char* vread = vst + (16 * half + 4 * q4 + (n >> 2)) * RS + 8 * (n & 3);
+      const int vrow = 16 * half + 4 * q4 + (n >> 2);
+      const char* vread = vst + vrow * RS + 8 * (n & 1);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const uint2 a = lds_read_tr16(vread + 32 * j);
+        // dims 16j + 4*(n&3) .. +3: 16-byte chunk 2j + ((n&3) >> 1), half (n & 1)
+        const int chunk = 2 * j + ((n & 3) >> 1);
+        const uint2 a = lds_read_tr16(vread + 16 * (S::DIRECT ? (chunk ^ lds_swz<D>(vrow)) : chunk));
         const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, a.x, a.y));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -309,13 +407,36 @@ pa_prefill_kernel(const PrefillParams p) {
   // Double-buffered key loop: step s+1's loads are in flight while step s is
   // computed; one barrier per step (buffer s&1 is rewritten two steps later,
   // after every wavefront has passed the barrier that follows its last read).
-  issue(0);
-  for (int32_t s = 0; s < nsteps; ++s) {
-    char* buf = smem + (s & 1) * S::STAGE;
-    stage(s, buf);
-    if (s + 1 < nsteps) issue(s + 1);
-    __syncthreads();
-    compute(s, buf);
+  if constexpr (S::DIRECT) {
+    // NSTAGE LDS buffers; loads run NSTAGE - 1 steps ahead. At step s the
+    // wavefront waits for its own loads of step s, the barrier makes every
+    // wavefront's loads visible, and only then is buffer (s + NSTAGE - 1)
+    // refilled: its last reader, step s - 1, is behind the barrier.
+    constexpr int NS = S::NSTAGE;
+#pragma unroll
+    for (int k = 0; k + 1 < NS; ++k) issue_direct(k, smem + k * S::STAGE);
+    for (int32_t s = 0; s < nsteps; ++s) {
+      char* buf = smem + (s % NS) * S::STAGE;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * NL));
+      __syncthreads();
+      const int32_t key0 = (blk_lo + 2 * s) * kBlock;
+      if (key0 < klo || key0 + KB - 1 > khi) {   // edge step: clear rows of keys no row may see
+        zero_edges(s, buf);
+        __syncthreads();
+      }
+      issue_direct(s + NS - 1, smem + ((s + NS - 1) % NS) * S::STAGE);
+      compute(s, buf);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // loads past the last step (zero bytes) drain
+  } else {
+    issue(0);
+    for (int32_t s = 0; s < nsteps; ++s) {
+      char* buf = smem + (s & 1) * S::STAGE;
+      stage(s, buf);
+      if (s + 1 < nsteps) issue(s + 1);
+      __syncthreads();
+      compute(s, buf);
+    }
   }
 
   // Row sums (the four lanes of a row each hold a quarter of the keys), then O / l.
