@@ -62,7 +62,7 @@ struct PrefillShape {
   static constexpr int CPR = D * 2 / 16;
   static constexpr int IPW = KB / RPI / NW;
   static_assert(NP >= 1 && (2 * KB * LPR) % (NW * 64) == 0, "piece split");
-  static_assert(!DIRECT || (IPW >= 1 && kBlock % RPI == 0), "direct-load split");
+  static_assert(!DIRECT || (IPW >= 1 && IPW * RPI == 8 && NW == 4), "direct-load split: 8 rows per wavefront");
 };
 
 // Swizzle of the 16-byte chunks of LDS row `row` (direct-load layout): chunk c
@@ -200,25 +200,24 @@ pa_prefill_kernel(const PrefillParams p) {
       tbl_base = i0;
       tbl = settle(table[table_entry(p, min(tbl_base + lane, blk_last))]);   // the wait stays in this branch
     }
-    const int32_t ph0 = __builtin_amdgcn_readlane(tbl, i0 - tbl_base);
-    const int32_t ph1 = __builtin_amdgcn_readlane(tbl, (has1 ? i0 + 1 : i0) - tbl_base);
-    const size_t t0b = (size_t)ph0 * kBlock * (size_t)tok_stride;
-    const size_t t1b = (size_t)ph1 * kBlock * (size_t)tok_stride;
+    // Wavefront w fills rows 8w .. 8w+7 of each tile (segments w*IPW ..), all
+    // in cache block w / 2 of the step: one descriptor per tile per step.
+    const bool mine1 = wave >= 2;
+    const int32_t ph = __builtin_amdgcn_readlane(tbl, (mine1 && has1 ? i0 + 1 : i0) - tbl_base);
+    const bool ok = mine1 ? has1 : live;
+    const size_t tb = (size_t)ph * kBlock * (size_t)tok_stride;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(buf) + wave * S::IPW * 1024;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {            // K tile, then V tile
       const char* pool = t == 0 || alias ? kpool : vpool;
       const bool skip = t == 1 && alias;     // V shares K's tile
-      const auto d0 = buffer_rsrc(pool + t0b, live && !skip ? tile_bytes : 0);
-      const auto d1 = buffer_rsrc(pool + t1b, has1 && !skip ? tile_bytes : 0);
+      const auto d = buffer_rsrc(pool + tb, ok && !skip ? tile_bytes : 0);
 #pragma unroll
       for (int k = 0; k < S::IPW; ++k) {
-        const int seg = wave + S::NW * k;    // 1 KiB segment of the tile (wave-uniform)
-        const int row = seg * S::RPI + lane / S::CPR;
+        const int row = (wave * S::IPW + k) * S::RPI + lane / S::CPR;   // row of the step's 32
         const int chunk = (lane % S::CPR) ^ lds_swz<D>(row);
         const int voff = (row % kBlock) * tok_stride + 16 * chunk;
-        char* dst = buf + t * S::TILE + seg * 1024;
-        load_lds16(row < kBlock ? d0 : d1, voff,
-                   (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst));
+        load_lds16(d, voff, lds0 + t * S::TILE + k * 1024);
       }
     }
   };
