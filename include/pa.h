@@ -192,6 +192,25 @@ int pa_verify(const pa_args* args, pa_stream_t stream);
 int pa_debug_gather(const pa_args* args, int32_t which, void* dst, int64_t dst_tokens,
                     pa_stream_t stream);
 
+/* Status bits written by pa_validate. */
+enum {
+  PA_BAD_LEN_SHORT = 1, /* seq_len < q_len */
+  PA_BAD_LEN_LONG = 2,  /* seq_len > max_seq_len, or (linear table) > max_blocks_per_seq * block_size */
+  PA_BAD_BLOCK = 4      /* a table entry the step would read is outside [0, num_blocks) */
+};
+
+/*
+ * Check on the device the preconditions the attention kernels trust (the
+ * sequence lengths and the block-table entries a step reads; tiniestgpt
+ * notes, "PagedAttention": block_table[seq][i] names a block of the pool).
+ * d_status: device int32 [num_seqs + 1]. Entry 1 + b receives the PA_BAD_*
+ * bits of sequence b (0 when it is fine); entry 0 receives the OR of all
+ * of them and must be zero before the call. Only table entries inside each
+ * row are read, whatever the lengths say. Same argument rules as pa_verify
+ * (q and out must be non-NULL but are not read). Asynchronous on stream.
+ */
+int pa_validate(const pa_args* args, int32_t* d_status, pa_stream_t stream);
+
 /*
  * KV append: write this step's new key and value rows into the paged pools
  * (tiniestgpt notes, "PagedAttention": the pool is [block][slot][head][dim]

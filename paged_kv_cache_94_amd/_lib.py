@@ -13,7 +13,7 @@ PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write", "pa_prefill",
-            "pa_debug_gather", "pa_strerror", "pa_last_error", "pa_version",
+            "pa_debug_gather", "pa_validate", "pa_strerror", "pa_last_error", "pa_version",
             "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_add_ring", "pa_alloc_append",
             "pa_alloc_append_batch",
             "pa_alloc_release", "pa_alloc_num_free", "pa_alloc_block_table", "pa_alloc_stats",
@@ -158,6 +158,8 @@ def load(path: str = LIB_PATH):
         lib.pa_cache_write.restype = ctypes.c_int
         lib.pa_debug_gather.argtypes = [P, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.pa_debug_gather.restype = ctypes.c_int
+        lib.pa_validate.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
+        lib.pa_validate.restype = ctypes.c_int
         lib.pa_strerror.argtypes = [ctypes.c_int]
         lib.pa_strerror.restype = ctypes.c_char_p
         lib.pa_last_error.restype = ctypes.c_char_p

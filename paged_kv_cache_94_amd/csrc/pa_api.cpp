@@ -397,6 +397,23 @@ int pa_debug_gather(const pa_args* a, int32_t which, void* dst, int64_t dst_toke
   return PA_OK;
 }
 
+int pa_validate(const pa_args* a, int32_t* d_status, pa_stream_t stream) {
+  pa::clear_error();
+  int rc = validate(a, kGather);   // the attention pointers are not used here
+  if (rc) return rc;
+  if (!d_status) return fail(PA_ERR_INVALID_ARG, "d_status is NULL");
+  if (a->num_seqs > 0x7FFFFFFF - 1) return fail(PA_ERR_UNSUPPORTED, "too many sequences");
+  if (a->num_seqs == 0) return PA_OK;
+  Plan P;
+  rc = make_plan(a, &P);
+  if (rc) return rc;
+  const pa::Params p = make_params(a, P);
+  const hipError_t e = pa::launch_validate(p, a->num_blocks, a->max_seq_len, d_status,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "validate kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
   pa::clear_error();
   if (!a) return fail(PA_ERR_INVALID_ARG, "args is NULL");

@@ -201,6 +201,46 @@ hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Precondition check: one workgroup per sequence. Lengths: q_len <= L <=
+// max_seq_len (and, linear tables, L <= maxb * 16). Table: every entry the
+// step reads (logical blocks [blk_lo, blk_hi] through table_entry) lies in
+// [0, num_blocks). Bits as in pa.h: 1 short, 2 long, 4 bad block.
+__global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_t num_blocks, int32_t max_seq_len,
+                                                          int32_t* status) {
+  __shared__ int32_t bits;
+  const int32_t b = blockIdx.x;
+  if (threadIdx.x == 0) bits = 0;
+  __syncthreads();
+  const int32_t L = p.seq_lens[b];
+  int32_t mine = 0;
+  if (threadIdx.x == 0) {
+    if (L < p.q_len) mine |= 1;
+    if (L > max_seq_len || (p.ring == 0 && (int64_t)L > (int64_t)p.maxb * kBlock)) mine |= 2;
+  }
+  if (L >= 1) {
+    const KeyRange kr = key_range(L, min(p.q_len, L), p.window);
+    // Entries read for blocks blk_lo .. blk_hi; a length the table cannot hold is clamped to the row.
+    const int32_t hi = p.ring > 0 ? kr.blk_hi : min(kr.blk_hi, p.maxb - 1);
+    for (int32_t i = kr.blk_lo + (int32_t)threadIdx.x; i <= hi; i += blockDim.x) {
+      const int32_t e = p.block_table[(size_t)b * p.maxb + table_entry(p, i)];
+      if (e < 0 || e >= num_blocks) mine |= 4;
+    }
+  }
+  if (mine) atomicOr(&bits, mine);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    status[1 + b] = bits;
+    if (bits) atomicOr(status, bits);
+  }
+}
+
+hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_len, int32_t* status,
+                           hipStream_t st) {
+  if (p.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(pa_validate_kernel, dim3((unsigned)p.B), dim3(256), 0, st, p, num_blocks, max_seq_len, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const Params& p, int kv_dtype, int D, int which, void* dst, int64_t dst_tokens,
                          hipStream_t st) {
   const int32_t eb = kv_dtype == 0 ? 4 : (kv_dtype == 1 ? 2 : 1);
