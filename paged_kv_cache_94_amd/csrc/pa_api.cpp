@@ -166,9 +166,10 @@ int make_plan(const pa_args* a, Plan* pl) {
 
   // Tuning knobs for experiments: waves per workgroup (4 or 8), blocks per wave.
   int bpw_force = 0;
+  bool nw_forced = false;
   if (const char* e = getenv("PA_WAVES")) {
     const int v = atoi(e);
-    if (v == 4 || v == 8 || (P.kernel == 1 && v == 2)) P.nw = v;
+    if (v == 4 || v == 8 || (P.kernel == 1 && v == 2)) P.nw = v, nw_forced = true;
   }
   if (const char* e = getenv("PA_BLOCKS_PER_WAVE")) bpw_force = atoi(e);
 
@@ -212,6 +213,11 @@ int make_plan(const pa_args* a, Plan* pl) {
   bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= pa::balanced_seq_limit(P.nw);
   if (const char* e = getenv("PA_BALANCED")) balanced = balanced && atoi(e) != 0;
   if (balanced) {
+    // Few units (at most one per two CUs) are cut into one piece per
+    // workgroup: one 8-wave workgroup per CU streams them as fast as two of
+    // 4 waves (C3: 29.4 vs 29.2 us) and leaves half the partials to merge
+    // (step 34.9 vs 37.0 us).
+    if (!nw_forced && P.kernel == 1 && 2 * units <= (int64_t)cu_count()) P.nw = 8;
     P.nwg = cu_count() * (8 / P.nw);
     if (const char* e = getenv("PA_OVERSUB")) { const int v = atoi(e); if (v >= 1 && v <= 64) P.nwg *= v; }
     // Measured on MI355X: one piece per workgroup is best for few units

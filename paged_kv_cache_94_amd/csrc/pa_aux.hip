@@ -20,18 +20,24 @@ __host__ __device__ inline int64_t combine_groups(const Params& p) {
 
 constexpr int kCombineWaves = 4;
 
-// Workgroups per merged unit: 1 when there are enough units to fill the
-// device, else one per group of kCombineWaves query rows.
+// Workgroups per merged unit: one per group of kCombineWaves query rows, so
+// that every wavefront merges one row (rows merged one after another by a
+// wavefront chain their memory round trips), unless that would launch
+// thousands of workgroups (2048 units x 5 row groups measured 3 us slower
+// than one workgroup per unit).
 __host__ __device__ inline int combine_row_groups(const Params& p) {
-  return combine_groups(p) >= 256 ? 1 : (p.rows + kCombineWaves - 1) / kCombineWaves;
+  return combine_groups(p) >= 1024 ? 1 : (p.rows + kCombineWaves - 1) / kCombineWaves;
 }
 
 // Workgroup (grp, rg) merges one unit's partials for query rows
-// rg*4 + w, rg*4 + w + 4*RG, ... (w = its wavefront, RG workgroups per unit). For a row, lane s holds split s's
-// (m, l) (64 splits at a time); the row max, the weights 2^(m_s - M) and the
-// weighted sum of l come from wave reductions, and the D dims of the row are
-// spread over the lanes (D/64 consecutive floats each), so every partial row
-// is read with one coalesced load per lane.
+// rg*4 + w, rg*4 + w + 4*RG, ... (w = its wavefront, RG workgroups per
+// unit). For a row, lane s holds split s's (m, l) (64 splits
+// at a time); the row max, the weights 2^(m_s - M) and the weighted sum of l
+// come from wave reductions, and the D dims of the row are spread over the
+// lanes (D/64 consecutive floats each), so every partial row is read with
+// one coalesced load per lane. The first partial rows of a chunk are
+// requested together with its (m, l), so a row costs one memory round trip
+// after its unit's bounds are known.
 template <typename OutT, int D>
 __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Params p) {
   constexpr int PER = D / 64;   // dims per lane
@@ -68,16 +74,21 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
     b = grp / p.Hkv;
     g = grp % p.Hkv;
     const int32_t L = p.seq_lens[b];
-    if (!len_ok(L, p)) return;
     if (p.balanced == 2) {
       // Piece partition: unit (b, g) was cut into k pieces, numbered
       // kp[b] + g*k .. + k-1, each of which left its partial in the slot of
-      // its own number; a unit of one piece was written out directly.
-      const int32_t k = (p.ws_prefix[b + 1] - p.ws_prefix[b]) / p.Hkv;
+      // its own number; a unit of one piece was written out directly. The
+      // prefix entries are requested with the length (both are in bounds
+      // whatever the length holds).
+      const int32_t kp0 = p.ws_prefix[b];
+      const int32_t kp1 = p.ws_prefix[b + 1];
+      if (!len_ok(L, p)) return;
+      const int32_t k = (kp1 - kp0) / p.Hkv;
       if (k <= 1) return;
-      slot_first = p.ws_prefix[b] + (int64_t)g * k;
+      slot_first = kp0 + (int64_t)g * k;
       ns = k;
     } else {
+      if (!len_ok(L, p)) return;
       const KeyRange kr = key_range(L, p.q_len, p.window);
       slot_first = (int64_t)grp * p.splits;
       ns = min(live_splits(kr, p.bps), p.splits);
@@ -92,10 +103,30 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
     float M = -INFINITY, den = 0.f;
+    // Partial rows j0 .. j0+NB-1 of the chunk starting at c0 (cnt of them), NB loads in flight.
+    constexpr int NB = 16;
+    float v[NB][PER];
+    auto load_rows = [&](int32_t c0, int32_t j0, int32_t cnt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const bool ok = j0 + j < cnt;
+        const float* src = acc + (size_t)(c0 + j0 + j) * p.rows * D;
+        if constexpr (PER == 4) {
+          const float4 t = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+          v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
+        } else if constexpr (PER == 2) {
+          const float2 t = ok ? *reinterpret_cast<const float2*>(src) : make_float2(0.f, 0.f);
+          v[j][0] = t.x; v[j][1] = t.y;
+        } else {
+          v[j][0] = ok ? src[0] : 0.f;
+        }
+      }
+    };
     for (int32_t c0 = 0; c0 < ns; c0 += 64) {
       const int32_t cnt = min(64, ns - c0);
       const float ms = lane < cnt ? ml[(size_t)(c0 + lane) * p.rows * 2] : -INFINITY;
       const float ls = lane < cnt ? ml[(size_t)(c0 + lane) * p.rows * 2 + 1] : 0.f;
+      load_rows(c0, 0, cnt);
       float cm = ms;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor(cm, off));
@@ -111,24 +142,9 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) dl += shfl_xor(dl, off);
       den += dl;
-      // Accumulate the chunk's partial rows, NB loads in flight at a time.
-      constexpr int NB = 16;
+      // Accumulate the chunk's partial rows (the first NB are already requested).
       for (int32_t j0 = 0; j0 < cnt; j0 += NB) {
-        float v[NB][PER];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const bool ok = j0 + j < cnt;
-          const float* src = acc + (size_t)(c0 + j0 + j) * p.rows * D;
-          if constexpr (PER == 4) {
-            const float4 t = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
-            v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
-          } else if constexpr (PER == 2) {
-            const float2 t = ok ? *reinterpret_cast<const float2*>(src) : make_float2(0.f, 0.f);
-            v[j][0] = t.x; v[j][1] = t.y;
-          } else {
-            v[j][0] = ok ? src[0] : 0.f;
-          }
-        }
+        if (j0 > 0) load_rows(c0, j0, cnt);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int jj = min(j0 + j, 63);

@@ -149,8 +149,8 @@ def test_plan_choices(lib):
     # Global layer: 16 query heads on one KV head go to the matrix cores.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768,
                                           max_blocks_per_seq=2048)), ctypes.byref(info)) == 0
-    # Few long units: each workgroup owns one piece of one unit (no queue).
-    assert info.kernel == 1 and info.rows == 16 and info.balanced == 2 and info.waves_per_group == 4
+    # Few long units: each workgroup owns one piece of one unit (no queue), one 8-wave workgroup per CU.
+    assert info.kernel == 1 and info.rows == 16 and info.balanced == 2 and info.waves_per_group == 8
     assert info.queue == 0 and info.pieces == info.grid
     # Verify step: 4 heads x 5 tokens = 20 rows.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
@@ -165,6 +165,7 @@ def test_plan_choices(lib):
                                           max_seq_len=4096, max_blocks_per_seq=256, q_dtype=_lib.PA_BF16,
                                           kv_dtype=_lib.PA_INT8, k_scale=8, v_scale=8)), ctypes.byref(info)) == 0
     assert info.kernel == 1 and info.rows == 8 and info.balanced == 1 and info.queue == 0
+    assert info.waves_per_group == 4
     # A forced split count is honoured (capped by the blocks a sequence can span).
     assert lib.pa_plan(ctypes.byref(_args(num_splits=3)), ctypes.byref(info)) == 0
     assert info.splits == 3
