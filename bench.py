@@ -20,8 +20,10 @@ Prints ONE JSON line on stdout (the run's record); diagnostics go to stderr.
               kernel; on every 8th timed step (--event-every) the library
               stamps a pair of HIP events from that kernel's own dispatch on
               the launch stream (hipExtLaunchKernel), the same start/end
-              timestamps a kernel trace reports. Stamping every step would
-              cost each step ~4.5 us of GPU time.
+              timestamps a kernel trace reports. The events are created
+              without the system-scope fence (hipEventDisableSystemFence),
+              whose cache writeback and invalidation would cost every stamped
+              step GPU time and slow the kernel after it.
   cpu_baseline = the fp64 oracle on the host's cores, same workload
   block_allocator = host time of the block allocator's work for one step
               of the same batch (grow every sequence by its q_len new
@@ -57,21 +59,21 @@ METRIC = "decode-attention queries/s and achieved KV HBM GB/s (% of MI355X peak)
 # holds only for the kernel sources and the launch plan it was taken with;
 # for anything else the record's traffic is null.
 MEASURED_TRAFFIC = {
-    1: {"kernel_sources": "13b74f85ad92bd1e",
+    1: {"kernel_sources": "8e3ced7a55775b45",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 4, "balanced": 0, "pieces": 0, "queue": 0},
         "fetch_kib": 93, "fetch_factor": 2.0, "write_kib": 2, "write_factor": 1.0},
-    2: {"kernel_sources": "13b74f85ad92bd1e",
+    2: {"kernel_sources": "8e3ced7a55775b45",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256, "balanced": 0, "pieces": 0, "queue": 0},
         "fetch_kib": 132875, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
-    3: {"kernel_sources": "d0b6db116c6c27bd",
-        "plan": {"kernel": 1, "rows": 16, "waves_per_group": 4, "splits": 57, "grid": 512, "balanced": 2, "pieces": 512, "queue": 0},
-        "fetch_kib": 61361, "fetch_factor": 2.0, "write_kib": 7998, "write_factor": 1.0},
-    4: {"kernel_sources": "d0b6db116c6c27bd",
+    3: {"kernel_sources": "ce983f808d7e7940",
+        "plan": {"kernel": 1, "rows": 16, "waves_per_group": 8, "splits": 57, "grid": 256, "balanced": 2, "pieces": 256, "queue": 0},
+        "fetch_kib": 61350, "fetch_factor": 2.0, "write_kib": 4112, "write_factor": 1.0},
+    4: {"kernel_sources": "ce983f808d7e7940",
         "plan": {"kernel": 1, "rows": 8, "waves_per_group": 4, "splits": 4, "grid": 512, "balanced": 1, "pieces": 0, "queue": 0},
-        "fetch_kib": 190051, "fetch_factor": 2.0, "write_kib": 3992, "write_factor": 1.0},
-    5: {"kernel_sources": "d0b6db116c6c27bd",
+        "fetch_kib": 189527, "fetch_factor": 2.0, "write_kib": 3997, "write_factor": 1.0},
+    5: {"kernel_sources": "ce983f808d7e7940",
         "plan": {"kernel": 1, "rows": 20, "waves_per_group": 4, "splits": 16, "grid": 512, "balanced": 2, "pieces": 4096, "queue": 1},
-        "fetch_kib": 838489, "fetch_factor": 2.0, "write_kib": 35636, "write_factor": 1.0},
+        "fetch_kib": 838486, "fetch_factor": 2.0, "write_kib": 35636, "write_factor": 1.0},
 }
 KERNEL_SOURCES = {0: ("pa_device.h", "pa_common.h", "pa_valu.hip"), 1: ("pa_device.h", "pa_common.h", "pa_mfma.hip")}
 
@@ -120,10 +122,70 @@ def parse():
                     help="time a paged prefill workload instead of a decode step (1 local layer, 2 global, 3 int8)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="decode: stamp the attention kernel's dispatch with a HIP event pair on every Nth timed "
-                         "step (a pair on every step adds ~4.5 us of GPU time and ~20 us of host time per step)")
+                         "step (a pair on every step adds GPU and host time to each step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
     return ap.parse_args()
+
+
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence.
+
+    torch.cuda.Event records with a system-scope fence, which writes back and
+    invalidates the caches at each record: ~4.5 us of GPU time per stamped
+    step on MI355X, and a slower start for the kernel that follows (the
+    Gemma4-like global-layer step, 16 sequences of 4K-32K tokens on one KV
+    head, measured 29.2 us after one vs 26.8 us without). The
+    event is made through the process's HIP runtime (the one torch loaded,
+    which libpa's kernels also run on); only its handle is handed to libpa,
+    whose launch stamps it from the kernel's own dispatch.
+    """
+
+    FLAGS = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
+    _hip = None
+
+    def __init__(self, torch):
+        import ctypes
+        if TimingEvent._hip is None:
+            torch.cuda.init()
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._torch = torch
+        h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self) -> None:
+        import ctypes
+        stream = self._torch.cuda.current_stream().cuda_stream
+        rc = TimingEvent._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                                  ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        import ctypes
+        if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
+            TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+
+
+def event_pair(torch):
+    return TimingEvent(torch), TimingEvent(torch)
 
 
 def measure_append(pa, accounting, torch, np, x, k, v, ks, vs, *, reps: int) -> dict:
@@ -151,7 +213,7 @@ def measure_append(pa, accounting, torch, np, x, k, v, ks, vs, *, reps: int) -> 
         sl = torch.from_numpy(slots).to(dev)
         for _ in range(3):
             pa.cache_write(kn, vn, sl, k, v, ks, vs)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        evs = [event_pair(torch) for _ in range(reps)]
         for a, b in evs:   # materialise the HIP events before the kernel stamps them
             a.record()
             b.record()
@@ -235,7 +297,7 @@ def main_prefill(args) -> int:
     out = torch.empty_like(q)
     kw = dict(max_q_len=int(np.diff(x.q_start).max()), window=x.window, scale=x.scale, max_seq_len=x.max_seq_len,
               k_scale=ks, v_scale=vs)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [event_pair(torch) for _ in range(args.steps)]
     for a, b in ev:
         a.record()
         b.record()
@@ -374,7 +436,7 @@ def main() -> int:
     # (hipExtLaunchKernel), whose mean is the kernel duration below.
     every = max(1, args.event_every)
     stamped = list(range(0, args.steps, every))
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in stamped}
+    ev = {i: event_pair(torch) for i in stamped}
     for a, b in ev.values():   # materialise the underlying HIP events before handing their handles over
         a.record()
         b.record()

@@ -215,8 +215,8 @@ int make_plan(const pa_args* a, Plan* pl) {
   if (balanced) {
     // Few units (at most one per two CUs) are cut into one piece per
     // workgroup: one 8-wave workgroup per CU streams them as fast as two of
-    // 4 waves (C3: 29.4 vs 29.2 us) and leaves half the partials to merge
-    // (step 34.9 vs 37.0 us).
+    // 4 waves and leaves half the partials to merge (16 sequences of 4K-32K
+    // tokens on one KV head: kernel 29.4 vs 29.2 us, step 34.9 vs 37.0 us).
     if (!nw_forced && P.kernel == 1 && 2 * units <= (int64_t)cu_count()) P.nw = 8;
     P.nwg = cu_count() * (8 / P.nw);
     if (const char* e = getenv("PA_OVERSUB")) { const int v = atoi(e); if (v >= 1 && v <= 64) P.nwg *= v; }
