@@ -276,7 +276,10 @@ typedef struct {
   const void* k_pool;         /* [num_blocks][block_size][Hkv][D], bf16 or int8 */
   const void* v_pool;         /* same; may equal k_pool */
   const float* k_scale;       /* int8 only: as in pa_args (per token, or per head with scale_per_head) */
-  const float* v_scale;
+  const float* v_scale;       /* int8 only: every value scale the chunk's keys use must be below 255
+                                 (dequantized values below ~32500 in magnitude): the kernel hands
+                                 each softmax weight (<= 256) times its value scale to the matrix
+                                 cores as one f16 value; larger scales overflow it */
   const int32_t* block_table; /* [B][max_blocks_per_seq]; ring rows with ring_blocks > 0 */
   const int32_t* seq_lens;    /* [B] cached tokens, this chunk's included; >= the chunk's length */
   int32_t num_seqs;           /* B >= 0 */

@@ -24,6 +24,18 @@
 // every score outside a row's [first visible key, own position] is removed
 // by select; steps whose keys every row of the tile sees skip the masks.
 //
+// int8 caches: K codes widen to bf16 (the query's type, so S^T keeps the bf16
+// MFMA) and V codes to f16, both exactly (|code| <= 127). The key scale, times
+// the softmax's scale*log2(e), multiplies each score; the value scale
+// multiplies each weight (dequantize after the gather, tiniestgpt notes, KV
+// cache quantization). The weights then go to the matrix cores as one f16
+// value each (11 significant bits, rounded to nearest), against the f16 V^T
+// of both 16-key halves in one v_mfma_f32_16x16x32_f16 per output tile: half
+// the P.V instructions of the bf16 path's [P_hi; P_lo] split, which a bf16
+// cache needs because its V cannot be widened to f16 exactly. A weight times
+// its value scale must stay within f16 range: value scales below 255, i.e.
+// dequantized values below ~32500 in magnitude.
+//
 // The running max is moved lazily: a row's reference max only changes when
 // its block max exceeds it by more than kRescaleSlack (log2 units), so the
 // accumulator is rescaled a handful of times per row instead of at nearly
@@ -35,6 +47,25 @@
 #include "pa_prefill.h"
 
 namespace pa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 16 int8 codes widened to 16 f16 values (exact: |code| <= 128 fits f16's 11
+// significant bits, so the truncating pack loses nothing), in order.
+__device__ __forceinline__ void i8x16_to_f16(const uint4& w, uint4& lo, uint4& hi) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = (float)(int32_t)(int8_t)(x[i]), b = (float)(int32_t)(int8_t)(x[i] >> 8);
+    const float c = (float)(int32_t)(int8_t)(x[i] >> 16), d = (float)(int32_t)(int8_t)(x[i] >> 24);
+    r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(c, d));
+  }
+  lo = make_uint4(r[0], r[1], r[2], r[3]);
+  hi = make_uint4(r[4], r[5], r[6], r[7]);
+}
 
 template <bool INT8, int D>
 struct PrefillShape {
@@ -151,10 +182,10 @@ pa_prefill_kernel(const PrefillParams p) {
       qt[mt][c] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  float ksh = 1.f, vsh = 1.f;   // per-head int8 scales
+  float ksh = 1.f, vsh = 1.f;   // per-head int8 scales (the key scale times scale*log2(e))
   if constexpr (INT8) {
     if (p.head_scales) {
-      ksh = p.k_scale[g];
+      ksh = p.k_scale[g] * p.scale_log2;
       vsh = p.v_scale[g];
     }
   }
@@ -287,14 +318,23 @@ pa_prefill_kernel(const PrefillParams p) {
       char* dst = buf + (isv ? S::TILE : 0) + row * RS;
       if constexpr (INT8) {
         uint4 lo, hi;
-        i8x16_to_bf16(w, lo, hi);
+        if (isv) i8x16_to_f16(w, lo, hi);
+        else i8x16_to_bf16(w, lo, hi);
         *reinterpret_cast<uint4*>(dst + 32 * chunk) = lo;
         *reinterpret_cast<uint4*>(dst + 32 * chunk + 16) = hi;
       } else {
         *reinterpret_cast<uint4*>(dst + 16 * chunk) = w;
       }
     }
-    if (token_scales && wave < 2 && lane < KB) reinterpret_cast<float*>(buf + 2 * S::TILE)[wave * KB + lane] = lsc;
+    // Key scales carry the softmax's scale*log2(e); a value scale of a key
+    // outside [klo, khi] is stored as 0, so its weight (0) times it stays 0
+    // whatever the unread scale slot holds.
+    if (token_scales && wave < 2 && lane < KB) {
+      const int32_t key = key0 + lane;
+      const bool ok = key >= klo && key <= khi;
+      reinterpret_cast<float*>(buf + 2 * S::TILE)[wave * KB + lane] =
+          wave == 0 ? lsc * p.scale_log2 : (ok ? lsc : 0.f);
+    }
   };
 
   // Step s from LDS buffer `buf`.
@@ -339,8 +379,11 @@ pa_prefill_kernel(const PrefillParams p) {
         vsc[4 * half + 0] = v.x; vsc[4 * half + 1] = v.y; vsc[4 * half + 2] = v.z; vsc[4 * half + 3] = v.w;
       }
     }
-    // Online softmax per row over the step's 32 keys; P leaves as hi/lo bf16 parts.
+    // Online softmax per row over the step's 32 keys; P leaves as hi/lo bf16
+    // parts (bf16 caches) or as one f16 value per key times its value scale
+    // (int8 caches; weight e of the lane is key 16*(e/4) + 4*q4 + e%4).
     bf16x8 pbv[MT][2];
+    f16x8 pbh[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float sc[8];
@@ -350,8 +393,7 @@ pa_prefill_kernel(const PrefillParams p) {
       for (int e = 0; e < 8; ++e) {
         const int32_t j = key0 + 16 * (e >> 2) + 4 * q4 + (e & 3);
         ok[e] = interior || (j >= row_lo[mt] && j <= row_hi[mt]);
-        float x = sacc[mt][e >> 2][e & 3] * p.scale_log2;
-        if constexpr (INT8) x *= ksc[e];
+        const float x = sacc[mt][e >> 2][e & 3] * (INT8 ? ksc[e] : p.scale_log2);
         sc[e] = ok[e] ? x : -INFINITY;
         mb = fmaxf(mb, sc[e]);
       }
@@ -371,7 +413,13 @@ pa_prefill_kernel(const PrefillParams p) {
       for (int e = 0; e < 8; ++e) {
         pe[e] = fast_exp2(sc[e] - msafe);
         l[mt] += pe[e];
-        if constexpr (INT8) pe[e] = ok[e] ? pe[e] * vsc[e] : 0.f;
+      }
+      if constexpr (INT8) {
+        // A masked key's weight is exactly 0 (2^-inf), and its value scale is
+        // finite (0 outside [klo, khi]).
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pbh[mt][e] = (_Float16)(pe[e] * vsc[e]);
+        continue;
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -384,6 +432,25 @@ pa_prefill_kernel(const PrefillParams p) {
         pbv[mt][half] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]),
                                                               pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])));
       }
+    }
+    if constexpr (INT8) {
+      // O^T += V^T P^T over all 32 keys: A holds the transposed f16 V reads of
+      // both halves (lane: keys 4*q4 .. +3, then 16 + 4*q4 .. +3, one dim),
+      // the order of the lane's weights in pbh.
+      const int vrow0 = 4 * q4 + (n >> 2);
+      const char* vread0 = vst + vrow0 * RS + 8 * (n & 1);
+      const char* vread1 = vread0 + 16 * RS;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int chunk = 2 * j + ((n & 3) >> 1);
+        const uint2 a0 = lds_read_tr16(vread0 + 16 * chunk);
+        const uint2 a1 = lds_read_tr16(vread1 + 16 * chunk);
+        const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbh[mt], o[mt][j], 0, 0, 0);
+      }
+      return;
     }
     // O^T += V^T [P_hi; P_lo] for each half, V^T read transposed from LDS.
 #pragma unroll

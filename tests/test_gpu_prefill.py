@@ -125,3 +125,20 @@ def test_prefill_full_size_workloads(idx):
     err = max_err(sub, ref)
     _log(f"{x.name}: max|err| over {rows.size} rows = {err:.3e}")
     assert err <= TOL[x.kv_dtype]
+
+
+@pytest.mark.parametrize("head_scales", [False, True])
+def test_prefill_int8_large_value_scales(head_scales):
+    # The int8 path hands each weight to the matrix cores as an f16 product
+    # (weight <= 256) x (value scale). Value scales of ~100 (dequantized values
+    # up to ~12700) stay well inside f16 range; the bar scales with the values
+    # (plus the bf16 output's own rounding).
+    c = ([300, 40, 0], [200, 64, 33], 16, 2, 128, 0, "int8", {"head_scales": head_scales})
+    x = _inputs(c, 78 + head_scales)
+    x.v_scale[...] = x.v_scale * np.float32(100.0)
+    _log(f"prefill int8, value scales x100, head_scales={head_scales}: max scale {float(x.v_scale.max()):.1f}")
+    got = run_prefill(x).float().cpu().numpy().astype(np.float64)
+    ref = oracle.attention(oracle.Problem.from_inputs(x))
+    assert not np.isnan(got).any() and not np.isinf(got).any()
+    bar = TOL["int8"] * 100.0 + np.abs(ref) * 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= bar), float(np.max(np.abs(got - ref) - bar))
