@@ -169,7 +169,10 @@ int make_plan(const pa_args* a, Plan* pl) {
   bool nw_forced = false;
   if (const char* e = getenv("PA_WAVES")) {
     const int v = atoi(e);
-    if (v == 4 || v == 8 || (P.kernel == 1 && v == 2)) P.nw = v, nw_forced = true;
+    if (v == 4 || v == 8 || (P.kernel == 1 && v == 2)) {
+      P.nw = v;
+      nw_forced = true;
+    }
   }
   if (const char* e = getenv("PA_BLOCKS_PER_WAVE")) bpw_force = atoi(e);
 

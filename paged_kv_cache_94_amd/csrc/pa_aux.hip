@@ -29,15 +29,15 @@ __host__ __device__ inline int combine_row_groups(const Params& p) {
   return combine_groups(p) >= 1024 ? 1 : (p.rows + kCombineWaves - 1) / kCombineWaves;
 }
 
-// Workgroup (grp, rg) merges one unit's partials for query rows
-// rg*4 + w, rg*4 + w + 4*RG, ... (w = its wavefront, RG workgroups per
-// unit). For a row, lane s holds split s's (m, l) (64 splits
-// at a time); the row max, the weights 2^(m_s - M) and the weighted sum of l
-// come from wave reductions, and the D dims of the row are spread over the
-// lanes (D/64 consecutive floats each), so every partial row is read with
-// one coalesced load per lane. The first partial rows of a chunk are
-// requested together with its (m, l), so a row costs one memory round trip
-// after its unit's bounds are known.
+// Workgroup (grp, rg) merges one unit's partials for query rows rg*4 + w,
+// rg*4 + w + 4*RG, ... (w = its wavefront, RG workgroups per unit). For a
+// row, lane s holds split s's (m, l) (64 splits at a time); the row max, the
+// weights 2^(m_s - M) and the weighted sum of l come from wave reductions,
+// and the D dims of the row are spread over the lanes (D/64 consecutive
+// floats each), so every partial row is read with one coalesced load per
+// lane. The first partial rows of a chunk are requested together with its
+// (m, l), so a row costs one memory round trip once its unit's bounds are
+// known.
 template <typename OutT, int D>
 __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Params p) {
   constexpr int PER = D / 64;   // dims per lane
