@@ -264,3 +264,21 @@ def test_longest_global_context():
                     kv_dtype="bf16", alias_v=True, poison=True, seed=12, max_blocks=2048)
     got = Dev(x).run_f64()
     assert max_err(got, _oracle(x)) <= 1e-2
+
+
+@pytest.mark.parametrize("splits", [20, 80, 150])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_many_splits(splits, kernel):
+    # Forced split counts past the combine's batch of 16 partial rows (20) and its
+    # chunk of 64 (m, l) pairs (80, 150), on long contexts, for both kernel families.
+    hq, kvd, qd = (4, "f32", "f32") if kernel == "valu" else (32, "bf16", "bf16")
+    x = make_inputs([16000, 9000, 37], q_len=1, num_q_heads=hq, num_kv_heads=2, head_dim=128, q_dtype=qd,
+                    kv_dtype=kvd, poison=True, seed=300 + splits)
+    dev = Dev(x)
+    plan = dev.plan(num_splits=splits)
+    _log(f"many splits {kernel} {splits}: plan {plan}")
+    # The plan rounds to whole blocks per split: 1000 blocks in 20, 77 or 143 splits.
+    assert plan["kernel"] == (0 if kernel == "valu" else 1) and plan["splits"] > (64 if splits > 64 else 16)
+    got = dev.run_f64(num_splits=splits)
+    assert not np.isnan(got).any()
+    assert max_err(got, _oracle(x)) <= TOL[kvd]
