@@ -179,9 +179,13 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        import ctypes
-        if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
-            TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+        # At interpreter shutdown the runtime may already be gone: nothing to release then.
+        try:
+            import ctypes
+            if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
+                TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+        except Exception:
+            pass
 
 
 def event_pair(torch):
