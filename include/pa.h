@@ -145,10 +145,13 @@ typedef struct {
 /*
  * Bytes of workspace the call needs for these arguments (0 when the key
  * range is not split). Depends on the shapes, max_seq_len, window,
- * num_splits, the device's compute-unit count and the tuning variables
- * PA_WAVES / PA_BLOCKS_PER_WAVE / PA_QUEUE / PA_PIECES_PER_WG (read at every
- * call), never on device data. Returns (size_t)-1 if the arguments are
- * invalid.
+ * num_splits, the device's compute-unit count and the plan's tuning
+ * variables (read from the environment at every call, for experiments
+ * only): PA_WAVES (wavefronts per workgroup), PA_BLOCKS_PER_WAVE,
+ * PA_BALANCED=0 (aligned splits only), PA_PIECES=0|1 (piece partition off
+ * or on), PA_QUEUE=0|1, PA_PIECES_PER_WG and PA_OVERSUB (workgroups per
+ * resident slot). Never on device data. Returns (size_t)-1 if the arguments
+ * are invalid.
  */
 size_t pa_workspace_size(const pa_args* args);
 
