@@ -199,7 +199,10 @@ int pa_debug_gather(const pa_args* args, int32_t which, void* dst, int64_t dst_t
 enum {
   PA_BAD_LEN_SHORT = 1, /* seq_len < q_len */
   PA_BAD_LEN_LONG = 2,  /* seq_len > max_seq_len, or (linear table) > max_blocks_per_seq * block_size */
-  PA_BAD_BLOCK = 4      /* a table entry the step would read is outside [0, num_blocks) */
+  PA_BAD_BLOCK = 4,     /* a table entry the step would read is outside [0, num_blocks) */
+  PA_BAD_SCALE = 8,     /* int8: a K or V scale of a key the step sees is NaN or infinite */
+  PA_BIG_V_SCALE = 16   /* int8: a V scale of a key the step sees is 255 or more in magnitude; decode
+                           takes it, pa_prefill does not (see its v_scale) */
 };
 
 /*
@@ -209,8 +212,14 @@ enum {
  * d_status: device int32 [num_seqs + 1]. Entry 1 + b receives the PA_BAD_*
  * bits of sequence b (0 when it is fine); entry 0 receives the OR of all
  * of them and must be zero before the call. Only table entries inside each
- * row are read, whatever the lengths say. Same argument rules as pa_verify
- * (q and out must be non-NULL but are not read). Asynchronous on stream.
+ * row are read, whatever the lengths say. For an int8 cache with both scale
+ * arrays given, the scales of the keys some query of the step sees
+ * (positions max(0, L - q_len - window + 1) .. L - 1 with a window, else
+ * 0 .. L - 1; only those in valid blocks) are checked as well; scales of
+ * other slots are never used and may hold anything. Without a window this
+ * covers every key of a pa_prefill chunk that ends at L. Same argument rules
+ * as pa_verify (q and out must be non-NULL but are not read). Asynchronous
+ * on stream.
  */
 int pa_validate(const pa_args* args, int32_t* d_status, pa_stream_t stream);
 

@@ -30,7 +30,7 @@ __all__ = ["decode", "decode_int8", "verify", "prefill", "cache_write", "debug_g
            "workspace_size", "PaError", "library_path"]
 
 # Status bits of validate() (include/pa.h).
-BAD_LEN_SHORT, BAD_LEN_LONG, BAD_BLOCK = 1, 2, 4
+BAD_LEN_SHORT, BAD_LEN_LONG, BAD_BLOCK, BAD_SCALE, BIG_V_SCALE = 1, 2, 4, 8, 16
 
 
 def library_path() -> str:
@@ -305,15 +305,16 @@ def debug_gather(which: int, dst, q, k_pool, v_pool, block_table, seq_lens, *, w
 
 
 def validate(q, k_pool, v_pool, block_table, seq_lens, *, window=0, max_seq_len=None, ring_blocks=0,
-             stream=None):
-    """Device check of the lengths and table entries a step would use: int32 [B+1] status.
+             k_scale=None, v_scale=None, stream=None):
+    """Device check of the lengths, table entries and (int8, given both scales) scales a step would use.
 
-    Entry 1+b holds sequence b's BAD_* bits (0 when fine), entry 0 their OR.
+    Returns int32 [B+1]: entry 1+b holds sequence b's BAD_* / BIG_V_SCALE
+    bits (0 when fine), entry 0 their OR.
     """
     torch = _torch()
     lib = _lib.load()
     a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=1.0,
-                    max_seq_len=max_seq_len, k_scale=None, v_scale=None, num_splits=0, debug_visits=None,
+                    max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=0, debug_visits=None,
                     ring_blocks=ring_blocks)
     status = torch.zeros(seq_lens.shape[0] + 1, dtype=torch.int32, device=q.device)
     _lib.check(lib.pa_validate(ctypes.byref(a), ctypes.c_void_p(status.data_ptr()),

@@ -417,7 +417,8 @@ int pa_validate(const pa_args* a, int32_t* d_status, pa_stream_t stream) {
   rc = make_plan(a, &P);
   if (rc) return rc;
   const pa::Params p = make_params(a, P);
-  const hipError_t e = pa::launch_validate(p, a->num_blocks, a->max_seq_len, d_status,
+  const int check_scales = a->kv_dtype == PA_INT8 && a->k_scale && a->v_scale;
+  const hipError_t e = pa::launch_validate(p, a->num_blocks, a->max_seq_len, check_scales, d_status,
                                            reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "validate kernel launch: %s", hipGetErrorString(e));
   return PA_OK;

@@ -217,12 +217,22 @@ hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
   return hipGetLastError();
 }
 
+__device__ __forceinline__ int32_t scale_bits(float ks, float vs) {
+  int32_t bits = 0;
+  if (!__builtin_isfinite(ks) || !__builtin_isfinite(vs)) bits |= 8;
+  if (__builtin_fabsf(vs) >= 255.f) bits |= 16;
+  return bits;
+}
+
 // Precondition check: one workgroup per sequence. Lengths: q_len <= L <=
 // max_seq_len (and, linear tables, L <= maxb * 16). Table: every entry the
 // step reads (logical blocks [blk_lo, blk_hi] through table_entry) lies in
-// [0, num_blocks). Bits as in pa.h: 1 short, 2 long, 4 bad block.
+// [0, num_blocks). Int8 scales (when check_scales): the K and V scales of
+// every key some query sees (positions lo0 .. L-1, in a valid block) are
+// finite, and the V scales are below 255 in magnitude. Bits as in pa.h: 1
+// short, 2 long, 4 bad block, 8 non-finite scale, 16 value scale >= 255.
 __global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_t num_blocks, int32_t max_seq_len,
-                                                          int32_t* status) {
+                                                          int32_t check_scales, int32_t* status) {
   __shared__ int32_t bits;
   const int32_t b = blockIdx.x;
   if (threadIdx.x == 0) bits = 0;
@@ -241,6 +251,23 @@ __global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_
       const int32_t e = p.block_table[(size_t)b * p.maxb + table_entry(p, i)];
       if (e < 0 || e >= num_blocks) mine |= 4;
     }
+    if (check_scales) {
+      const int32_t key_end = p.ring > 0 ? L : min(L, p.maxb * kBlock);   // keys [lo0, key_end)
+      const int32_t nkeys = key_end - kr.lo0;
+      const int32_t H = p.Hkv;
+      if (p.head_scales) {
+        for (int32_t h = threadIdx.x; h < (nkeys > 0 ? H : 0); h += blockDim.x)
+          mine |= scale_bits(p.k_scale[h], p.v_scale[h]);
+      } else {
+        for (int64_t f = threadIdx.x; f < (int64_t)max(nkeys, 0) * H; f += blockDim.x) {
+          const int32_t j = kr.lo0 + (int32_t)(f / H), h = (int32_t)(f % H);
+          const int32_t e = p.block_table[(size_t)b * p.maxb + table_entry(p, j / kBlock)];
+          if (e < 0 || e >= num_blocks) continue;                        // already flagged as a bad block
+          const size_t at = ((size_t)e * H + h) * kBlock + j % kBlock;
+          mine |= scale_bits(p.k_scale[at], p.v_scale[at]);
+        }
+      }
+    }
   }
   if (mine) atomicOr(&bits, mine);
   __syncthreads();
@@ -250,10 +277,11 @@ __global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_
   }
 }
 
-hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_len, int32_t* status,
-                           hipStream_t st) {
+hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_len, int check_scales,
+                           int32_t* status, hipStream_t st) {
   if (p.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(pa_validate_kernel, dim3((unsigned)p.B), dim3(256), 0, st, p, num_blocks, max_seq_len, status);
+  hipLaunchKernelGGL(pa_validate_kernel, dim3((unsigned)p.B), dim3(256), 0, st, p, num_blocks, max_seq_len,
+                     (int32_t)check_scales, status);
   return hipGetLastError();
 }
 

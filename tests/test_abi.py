@@ -45,6 +45,22 @@ def test_every_declared_symbol_is_exported(lib):
         assert getattr(lib, n)
 
 
+def test_enum_constants_match_header():
+    """Every PA_* enumerator in the headers has the same value in the binding."""
+    import paged_kv_cache_94_amd as pa
+    text = "\n".join(re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S) for h in HEADERS)
+    found = {}
+    for body in re.findall(r"enum\s*\{(.*?)\}", text, flags=re.S):
+        for name, value in re.findall(r"\b(PA_\w+)\s*=\s*(\d+)", body):
+            found[name] = int(value)
+    assert {"PA_INT8", "PA_ERR_NO_BLOCKS", "PA_BAD_BLOCK", "PA_BIG_V_SCALE"} <= set(found)
+    for name, value in found.items():
+        if name.startswith(("PA_BAD_", "PA_BIG_")):
+            assert getattr(pa, name[3:]) == value, name
+        else:
+            assert getattr(_lib, name) == value, name
+
+
 def test_struct_layout_matches_header():
     src = r'''
 #include <stdio.h>
