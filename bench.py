@@ -59,19 +59,19 @@ METRIC = "decode-attention queries/s and achieved KV HBM GB/s (% of MI355X peak)
 # holds only for the kernel sources and the launch plan it was taken with;
 # for anything else the record's traffic is null.
 MEASURED_TRAFFIC = {
-    1: {"kernel_sources": "8e3ced7a55775b45",
+    1: {"kernel_sources": "bcf777cd3beef791",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 4, "balanced": 0, "pieces": 0, "queue": 0},
         "fetch_kib": 93, "fetch_factor": 2.0, "write_kib": 2, "write_factor": 1.0},
-    2: {"kernel_sources": "8e3ced7a55775b45",
+    2: {"kernel_sources": "bcf777cd3beef791",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256, "balanced": 0, "pieces": 0, "queue": 0},
-        "fetch_kib": 132875, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
-    3: {"kernel_sources": "ce983f808d7e7940",
+        "fetch_kib": 132873, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
+    3: {"kernel_sources": "be88d9a4f62d2ca4",
         "plan": {"kernel": 1, "rows": 16, "waves_per_group": 8, "splits": 57, "grid": 256, "balanced": 2, "pieces": 256, "queue": 0},
         "fetch_kib": 61350, "fetch_factor": 2.0, "write_kib": 4112, "write_factor": 1.0},
-    4: {"kernel_sources": "ce983f808d7e7940",
+    4: {"kernel_sources": "be88d9a4f62d2ca4",
         "plan": {"kernel": 1, "rows": 8, "waves_per_group": 4, "splits": 4, "grid": 512, "balanced": 1, "pieces": 0, "queue": 0},
         "fetch_kib": 189527, "fetch_factor": 2.0, "write_kib": 3997, "write_factor": 1.0},
-    5: {"kernel_sources": "ce983f808d7e7940",
+    5: {"kernel_sources": "be88d9a4f62d2ca4",
         "plan": {"kernel": 1, "rows": 20, "waves_per_group": 4, "splits": 16, "grid": 512, "balanced": 2, "pieces": 4096, "queue": 1},
         "fetch_kib": 838486, "fetch_factor": 2.0, "write_kib": 35636, "write_factor": 1.0},
 }
