@@ -34,7 +34,9 @@
  *     stream). A return of PA_OK means the work was enqueued; device-side
  *     data errors are not detected (see the preconditions).
  *   - The library keeps no state between calls except a per-device cache of
- *     the compute-unit count; it is safe to call from several host threads.
+ *     the compute-unit count, and reads no environment variable: the launch
+ *     plan depends only on the arguments (pa_args.tuning overrides it
+ *     explicitly). It is safe to call from several host threads.
  *   - On failure the entry point returns a PA_ERR_* code, enqueues nothing,
  *     and pa_last_error() returns a message for the calling thread.
  *
@@ -70,6 +72,28 @@ enum {
   PA_ERR_NO_BLOCKS = 5    /* block allocator (pa_alloc.h): too few free blocks; nothing changed */
 };
 
+/*
+ * Explicit overrides of the launch plan, for tests and tuning experiments
+ * (pa_args.tuning). A zero field keeps the library's own choice; every
+ * partition computes the same attention up to floating-point rounding order.
+ * A request the chosen kernel cannot honour returns PA_ERR_UNSUPPORTED.
+ */
+enum {
+  PA_PART_AUTO = 0,      /* the library's choice */
+  PA_PART_ALIGNED = 1,   /* each workgroup owns one aligned split of one (sequence, KV head) */
+  PA_PART_LIST = 2,      /* matrix-core kernel: equal shares of the flattened (sequence, KV head, block) list */
+  PA_PART_PIECES = 3,    /* matrix-core kernel: units cut into near-equal pieces, one per workgroup */
+  PA_PART_QUEUE = 4      /* matrix-core kernel: pieces handed out through the workspace queue */
+};
+
+typedef struct {
+  int32_t waves;              /* wavefronts per workgroup: 4 or 8 (also 2 for the matrix-core kernel); 0 auto */
+  int32_t blocks_per_wave;    /* aligned splits without num_splits: blocks per wavefront per split; 0 auto */
+  int32_t partition;          /* PA_PART_* */
+  int32_t pieces_per_wg;      /* PA_PART_QUEUE: pieces per workgroup the queue aims for, 1..64; 0 auto */
+  int32_t oversub;            /* list / piece partitions: workgroups per resident slot, 1..64; 0 auto */
+} pa_tuning;
+
 typedef struct {
   void* out;                  /* [B][q_len][Hq][D], q_dtype */
   const void* q;              /* [B][q_len][Hq][D], q_dtype */
@@ -78,7 +102,8 @@ typedef struct {
   const float* k_scale;       /* int8 cache only: [num_blocks][Hkv][block_size], one fp32 per (token,
                                  KV head), a block's 16 scales of one head contiguous; or [Hkv],
                                  one per KV head, when scale_per_head is 1; else NULL */
-  const float* v_scale;       /* int8 cache only: same shape; else NULL */
+  const float* v_scale;       /* int8 cache only: same shape; else NULL. When v_pool == k_pool the
+                                 values are the keys, so v_scale must equal k_scale */
   const int32_t* block_table; /* [B][max_blocks_per_seq] physical block ids; with ring_blocks > 0 each
                                  row's first ring_blocks entries form the sequence's ring */
   const int32_t* seq_lens;    /* [B] cached tokens per sequence, this step's q_len tokens included */
@@ -122,6 +147,8 @@ typedef struct {
   int32_t scale_per_head;     /* int8 caches: 0 scales per token (k_scale layout above); 1 one scale
                                  per KV head for the whole cache, k_scale / v_scale [Hkv] (tiniestgpt
                                  notes, "Quantization": per_head granularity, a smaller scale table) */
+  const pa_tuning* tuning;    /* NULL: the library's launch plan; else explicit overrides (host memory,
+                                 read during the call only) */
 } pa_args;
 
 /* Plan the library would use for these arguments (informational). */
@@ -145,13 +172,8 @@ typedef struct {
 /*
  * Bytes of workspace the call needs for these arguments (0 when the key
  * range is not split). Depends on the shapes, max_seq_len, window,
- * num_splits, the device's compute-unit count and the plan's tuning
- * variables (read from the environment at every call, for experiments
- * only): PA_WAVES (wavefronts per workgroup), PA_BLOCKS_PER_WAVE,
- * PA_BALANCED=0 (aligned splits only), PA_PIECES=0|1 (piece partition off
- * or on), PA_QUEUE=0|1, PA_PIECES_PER_WG and PA_OVERSUB (workgroups per
- * resident slot). Never on device data. Returns (size_t)-1 if the arguments
- * are invalid.
+ * num_splits, tuning and the device's compute-unit count; never on device
+ * data. Returns (size_t)-1 if the arguments are invalid.
  */
 size_t pa_workspace_size(const pa_args* args);
 
@@ -188,8 +210,12 @@ int pa_verify(const pa_args* args, pa_stream_t stream);
  * (which = 0: keys, 1: values) into dst, [B][dst_tokens][Hkv][D] elements of
  * kv_dtype. Entry w of sequence b holds key first(b)+w, first(b) being the
  * first key visible to query token 0; entries past seq_lens[b]-1 are left
- * untouched. Uses the same block-range and address computation as the
- * attention kernels, so a bit-exact comparison checks the gather itself.
+ * untouched. It computes the key range, the table entry of a logical
+ * block and a row's pool address with the device functions the attention,
+ * prefill and append kernels use for theirs (the tile of a (block, KV head)
+ * and the stride from one token's row to the next), so a bit-exact
+ * comparison checks that shared addressing; the order in which a kernel's
+ * lanes read the rows of a tile is checked by the poisoned parity tests.
  * dst_tokens must be >= window + q_len - 1 (window > 0) or >= max_seq_len.
  */
 int pa_debug_gather(const pa_args* args, int32_t which, void* dst, int64_t dst_tokens,
@@ -201,8 +227,10 @@ enum {
   PA_BAD_LEN_LONG = 2,  /* seq_len > max_seq_len, or (linear table) > max_blocks_per_seq * block_size */
   PA_BAD_BLOCK = 4,     /* a table entry the step would read is outside [0, num_blocks) */
   PA_BAD_SCALE = 8,     /* int8: a K or V scale of a key the step sees is NaN or infinite */
-  PA_BIG_V_SCALE = 16   /* int8: a V scale of a key the step sees is 255 or more in magnitude; decode
+  PA_BIG_V_SCALE = 16,  /* int8: a V scale of a key the step sees is 255 or more in magnitude; decode
                            takes it, pa_prefill does not (see its v_scale) */
+  PA_BAD_WORKSPACE = 32 /* (entry 0 only) the call would hand pieces out through the workspace queue
+                           and the queue's counters in the workspace header are not zero */
 };
 
 /*
@@ -217,9 +245,11 @@ enum {
  * (positions max(0, L - q_len - window + 1) .. L - 1 with a window, else
  * 0 .. L - 1; only those in valid blocks) are checked as well; scales of
  * other slots are never used and may hold anything. Without a window this
- * covers every key of a pa_prefill chunk that ends at L. Same argument rules
- * as pa_verify (q and out must be non-NULL but are not read). Asynchronous
- * on stream.
+ * covers every key of a pa_prefill chunk that ends at L. When the plan for
+ * these arguments hands pieces out through the workspace queue and a
+ * workspace is given, its header's queue counters are checked too
+ * (PA_BAD_WORKSPACE in entry 0). Same argument rules as pa_verify (q and
+ * out must be non-NULL but are not read). Asynchronous on stream.
  */
 int pa_validate(const pa_args* args, int32_t* d_status, pa_stream_t stream);
 
@@ -238,7 +268,7 @@ typedef struct {
   void* k_pool;               /* [num_blocks][block_size][Hkv][D], kv_dtype */
   void* v_pool;               /* same; may equal k_pool (then the rows are written once) */
   float* k_scale;             /* int8 cache only: [num_blocks][Hkv][block_size]; else NULL */
-  float* v_scale;             /* int8 cache only: same; else NULL */
+  float* v_scale;             /* int8 cache only: same; else NULL. Must equal k_scale when v_pool == k_pool */
   int32_t num_tokens;         /* T >= 0 (0 enqueues nothing) */
   int32_t num_kv_heads;       /* Hkv */
   int32_t head_dim;           /* D: 64, 128 or 256 */
@@ -288,7 +318,8 @@ typedef struct {
   const void* k_pool;         /* [num_blocks][block_size][Hkv][D], bf16 or int8 */
   const void* v_pool;         /* same; may equal k_pool */
   const float* k_scale;       /* int8 only: as in pa_args (per token, or per head with scale_per_head) */
-  const float* v_scale;       /* int8 only: every value scale the chunk's keys use must be below 255
+  const float* v_scale;       /* int8 only (equal to k_scale when v_pool == k_pool): every value
+                                 scale the chunk's keys use must be below 255
                                  (dequantized values below ~32500 in magnitude): the kernel hands
                                  each softmax weight (<= 256) times its value scale to the matrix
                                  cores as one f16 value; larger scales overflow it */
@@ -329,6 +360,12 @@ const char* pa_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int pa_version(void);
+
+/* Identifier of the sources this library was built from: 16 hex digits of
+ * a SHA-256 over the C/HIP sources and headers, computed by the build. A
+ * binding that has the sources can compare it with their current hash and
+ * refuse a library built from other sources. */
+const char* pa_build_id(void);
 
 #ifdef __cplusplus
 }

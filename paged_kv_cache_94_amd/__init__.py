@@ -2,8 +2,15 @@
 
 A thin binding over libpa.so (the C ABI in include/pa.h). Every step of the
 attention runs in the library's HIP kernels; this module only checks tensor
-shapes, dtypes and devices, passes raw pointers plus the current HIP stream,
-and allocates the split workspace through PyTorch's caching allocator.
+shapes, dtypes and devices, passes raw pointers plus the HIP stream, and
+allocates the split workspace through PyTorch's caching allocator -- on the
+stream the kernels are launched on, so its zero-fill is ordered before them
+and the block is not handed out again before they finish.
+
+``tuning`` (decode / verify / plan): a dict of pa_tuning fields (waves,
+blocks_per_wave, partition, pieces_per_wg, oversub) overriding the launch
+plan for tests and experiments; ``partition`` takes "aligned", "list",
+"pieces" or "queue".
 
 Layouts (row-major, all tensors on the same GPU):
     q, out       [B, q_len, Hq, D]            float32 or bfloat16
@@ -30,7 +37,7 @@ __all__ = ["decode", "decode_int8", "verify", "prefill", "cache_write", "debug_g
            "workspace_size", "PaError", "library_path"]
 
 # Status bits of validate() (include/pa.h).
-BAD_LEN_SHORT, BAD_LEN_LONG, BAD_BLOCK, BAD_SCALE, BIG_V_SCALE = 1, 2, 4, 8, 16
+BAD_LEN_SHORT, BAD_LEN_LONG, BAD_BLOCK, BAD_SCALE, BIG_V_SCALE, BAD_WORKSPACE = 1, 2, 4, 8, 16, 32
 
 
 def library_path() -> str:
@@ -62,9 +69,25 @@ def _require(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+PARTITIONS = {"auto": _lib.PA_PART_AUTO, "aligned": _lib.PA_PART_ALIGNED, "list": _lib.PA_PART_LIST,
+              "pieces": _lib.PA_PART_PIECES, "queue": _lib.PA_PART_QUEUE}
+
+
+def _tuning(tuning) -> Optional[_lib.PaTuning]:
+    if tuning is None:
+        return None
+    t = _lib.PaTuning()
+    for key, value in dict(tuning).items():
+        if key == "partition" and isinstance(value, str):
+            value = PARTITIONS[value]
+        _require(key in dict(t._fields_), f"unknown tuning field {key!r}")
+        setattr(t, key, int(value))
+    return t
+
+
 def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, scale: Optional[float],
                 max_seq_len: Optional[int], k_scale, v_scale, num_splits: int, debug_visits,
-                ring_blocks: int = 0) -> _lib.PaArgs:
+                ring_blocks: int = 0, tuning=None) -> _lib.PaArgs:
     torch = _torch()
     tensors = [t for t in (out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, debug_visits)
                if t is not None]
@@ -111,16 +134,30 @@ def _build_args(out, q, k_pool, v_pool, block_table, seq_lens, *, window: int, s
     a.debug_visits = _ptr(debug_visits) or None
     a.ring_blocks = int(ring_blocks)
     a.scale_per_head = per_head
+    t = _tuning(tuning)
+    a._tuning_ref = t   # keeps the struct alive as long as the args
+    a.tuning = ctypes.addressof(t) if t is not None else None
     return a
 
 
-def _stream_handle(stream) -> int:
+def _stream(stream, device=None):
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
-def _attach_workspace(a: _lib.PaArgs, workspace, device) -> object:
+def _stream_handle(stream) -> int:
+    return _stream(stream).cuda_stream
+
+
+def _attach_workspace(a: _lib.PaArgs, workspace, device, stream) -> object:
+    """Attach the caller's workspace, or allocate one on `stream` (the launch stream).
+
+    A new workspace is allocated and zero-filled under `stream`: the fill is
+    ordered before the kernels launched on it, and when the tensor is
+    released the caching allocator hands the block out again only to later
+    work on that same stream. A caller's own workspace is the caller's to
+    order (its first 4096 bytes must be zero before the first call).
+    """
     lib = _lib.load()
     need = lib.pa_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
@@ -131,7 +168,8 @@ def _attach_workspace(a: _lib.PaArgs, workspace, device) -> object:
         torch = _torch()
         # Zero-filled: the library keeps the header words of the piece queue
         # at zero between calls but needs them zero before the first one.
-        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     _require(workspace.numel() * workspace.element_size() >= need, f"workspace needs {need} bytes")
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -140,18 +178,19 @@ def _attach_workspace(a: _lib.PaArgs, workspace, device) -> object:
 
 def _run(entry: str, out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None,
          k_scale=None, v_scale=None, num_splits=0, workspace=None, debug_visits=None, stream=None,
-         timing=None, ring_blocks=0):
+         timing=None, ring_blocks=0, tuning=None):
     lib = _lib.load()
     a = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
                     max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
-                    debug_visits=debug_visits, ring_blocks=ring_blocks)
-    ws = _attach_workspace(a, workspace, q.device)
+                    debug_visits=debug_visits, ring_blocks=ring_blocks, tuning=tuning)
+    s = _stream(stream, q.device)
+    ws = _attach_workspace(a, workspace, q.device, s)
     if timing is not None:
         a.timing_start = ctypes.c_void_p(timing[0].cuda_event if hasattr(timing[0], "cuda_event") else timing[0])
         a.timing_stop = ctypes.c_void_p(timing[1].cuda_event if hasattr(timing[1], "cuda_event") else timing[1])
-    rc = getattr(lib, entry)(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
+    rc = getattr(lib, entry)(ctypes.byref(a), ctypes.c_void_p(s.cuda_stream))
     _lib.check(rc)
-    del ws  # the caching allocator keeps the block stream-ordered until the kernels finish
+    del ws  # allocated on s: reused only by later work on s, after these kernels
     return out
 
 
@@ -274,12 +313,12 @@ def prefill(out, q, q_start, k_pool, v_pool, block_table, seq_lens, *, max_q_len
 
 
 def plan(q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None, k_scale=None,
-         v_scale=None, num_splits=0, ring_blocks=0) -> dict:
+         v_scale=None, num_splits=0, ring_blocks=0, tuning=None) -> dict:
     """The launch plan libpa would use for these tensors (no launch)."""
     lib = _lib.load()
     a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
                     max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
-                    debug_visits=None, ring_blocks=ring_blocks)
+                    debug_visits=None, ring_blocks=ring_blocks, tuning=tuning)
     info = _lib.PaPlanInfo()
     _lib.check(lib.pa_plan(ctypes.byref(a), ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in info._fields_}
@@ -305,20 +344,27 @@ def debug_gather(which: int, dst, q, k_pool, v_pool, block_table, seq_lens, *, w
 
 
 def validate(q, k_pool, v_pool, block_table, seq_lens, *, window=0, max_seq_len=None, ring_blocks=0,
-             k_scale=None, v_scale=None, stream=None):
+             k_scale=None, v_scale=None, stream=None, workspace=None, num_splits=0, tuning=None):
     """Device check of the lengths, table entries and (int8, given both scales) scales a step would use.
 
     Returns int32 [B+1]: entry 1+b holds sequence b's BAD_* / BIG_V_SCALE
-    bits (0 when fine), entry 0 their OR.
+    bits (0 when fine), entry 0 their OR. With ``workspace`` (and the plan
+    that ``num_splits`` / ``tuning`` give), entry 0 also gets BAD_WORKSPACE
+    if the call would use the piece queue and the workspace's queue counters
+    are not zero.
     """
     torch = _torch()
     lib = _lib.load()
     a = _build_args(q, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=1.0,
-                    max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=0, debug_visits=None,
-                    ring_blocks=ring_blocks)
-    status = torch.zeros(seq_lens.shape[0] + 1, dtype=torch.int32, device=q.device)
-    _lib.check(lib.pa_validate(ctypes.byref(a), ctypes.c_void_p(status.data_ptr()),
-                               ctypes.c_void_p(_stream_handle(stream))))
+                    max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
+                    debug_visits=None, ring_blocks=ring_blocks, tuning=tuning)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    s = _stream(stream, q.device)
+    with torch.cuda.stream(s):   # zero-filled on the stream the check runs on
+        status = torch.zeros(seq_lens.shape[0] + 1, dtype=torch.int32, device=q.device)
+    _lib.check(lib.pa_validate(ctypes.byref(a), ctypes.c_void_p(status.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
     return status
 
 
@@ -329,18 +375,29 @@ class Prepared:
     tiniestgpt notes' rule for replaying a decode step: static buffers, no
     host sync per step); ``launch`` only enqueues the kernels on a stream.
     The tensors must stay alive and keep their storage while this object is
-    used.
+    used. A workspace the object allocates is zero-filled at construction,
+    which waits for the fill, so launches on any stream find it ready; every
+    other stream a launch uses is recorded on it, so the caching allocator
+    does not hand the block out again while that stream's kernels may still
+    use it.
     """
 
     def __init__(self, entry: str, out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None,
-                 max_seq_len=None, k_scale=None, v_scale=None, num_splits=0, workspace=None, ring_blocks=0):
+                 max_seq_len=None, k_scale=None, v_scale=None, num_splits=0, workspace=None, ring_blocks=0,
+                 tuning=None, entry_point: Optional[str] = None):
         self._lib = _lib.load()
-        self._fn = getattr(self._lib, {"decode": "pa_decode", "decode_int8": "pa_decode_int8",
-                                       "verify": "pa_verify"}[entry])
+        self._fn = getattr(self._lib, entry_point or {"decode": "pa_decode", "decode_int8": "pa_decode_int8",
+                                                      "verify": "pa_verify"}[entry])
         self.args = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
                                 max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale,
-                                num_splits=num_splits, debug_visits=None, ring_blocks=ring_blocks)
-        self.workspace = _attach_workspace(self.args, workspace, q.device)
+                                num_splits=num_splits, debug_visits=None, ring_blocks=ring_blocks, tuning=tuning)
+        home = _stream(None, q.device)
+        owned = workspace is None
+        self.workspace = _attach_workspace(self.args, workspace, q.device, home)
+        if owned and self.workspace is not None:
+            home.synchronize()   # the zero-fill is done before any stream launches
+        self._home = home.cuda_stream
+        self._recorded = set()
         self._keep = (out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale)
 
     def launch(self, stream=None, timing=None) -> None:
@@ -350,7 +407,11 @@ class Prepared:
         else:
             self.args.timing_start = None
             self.args.timing_stop = None
-        _lib.check(self._fn(ctypes.byref(self.args), ctypes.c_void_p(_stream_handle(stream))))
+        s = _stream(stream)
+        if self.workspace is not None and s.cuda_stream != self._home and s.cuda_stream not in self._recorded:
+            self.workspace.record_stream(s)
+            self._recorded.add(s.cuda_stream)
+        _lib.check(self._fn(ctypes.byref(self.args), ctypes.c_void_p(s.cuda_stream)))
 
 
 __all__.append("Prepared")

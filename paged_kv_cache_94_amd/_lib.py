@@ -1,4 +1,9 @@
-"""ctypes view of libpa.so (include/pa.h). Marshalling only, no compute."""
+"""ctypes view of libpa.so (include/pa.h). Marshalling only, no compute.
+
+load() refuses a library whose build id (pa_build_id: a hash of the sources
+it was compiled from) differs from the hash of the sources beside it, so a
+stale binary is never run in place of the code in the tree.
+"""
 
 from __future__ import annotations
 
@@ -11,13 +16,24 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_INT8 = 0, 1, 2
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = 0, 1, 2, 3, 4, 5
+PA_PART_AUTO, PA_PART_ALIGNED, PA_PART_LIST, PA_PART_PIECES, PA_PART_QUEUE = 0, 1, 2, 3, 4
 
 EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write", "pa_prefill",
-            "pa_debug_gather", "pa_validate", "pa_strerror", "pa_last_error", "pa_version",
+            "pa_debug_gather", "pa_validate", "pa_strerror", "pa_last_error", "pa_version", "pa_build_id",
             "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_add_ring", "pa_alloc_append",
             "pa_alloc_append_batch",
             "pa_alloc_release", "pa_alloc_num_free", "pa_alloc_block_table", "pa_alloc_stats",
             "pa_alloc_free_queue")
+
+
+class PaTuning(ctypes.Structure):
+    _fields_ = [
+        ("waves", ctypes.c_int32),
+        ("blocks_per_wave", ctypes.c_int32),
+        ("partition", ctypes.c_int32),
+        ("pieces_per_wg", ctypes.c_int32),
+        ("oversub", ctypes.c_int32),
+    ]
 
 
 class PaArgs(ctypes.Structure):
@@ -51,6 +67,7 @@ class PaArgs(ctypes.Structure):
         ("timing_stop", ctypes.c_void_p),
         ("ring_blocks", ctypes.c_int32),
         ("scale_per_head", ctypes.c_int32),
+        ("tuning", ctypes.c_void_p),
     ]
 
 
@@ -133,8 +150,27 @@ _lock = threading.Lock()
 _lib = None
 
 
+def check_build_id(lib, root=None) -> None:
+    """Raise unless lib was built from the sources under root (default: this checkout).
+
+    Without the sources (an installed copy) there is nothing to compare with
+    and the library is taken as it is.
+    """
+    from . import build
+    root = root or build.ROOT
+    if not os.path.isdir(os.path.join(root, "paged_kv_cache_94_amd", "csrc")):
+        return
+    lib.pa_build_id.restype = ctypes.c_char_p
+    have = lib.pa_build_id().decode()
+    want = build.source_hash(root)
+    if have != want:
+        raise RuntimeError(f"libpa.so was built from other sources (build id {have}, sources {want}): "
+                           "rebuild it with `python -m paged_kv_cache_94_amd.build`")
+
+
 def load(path: str = LIB_PATH):
-    """Load libpa.so. Raises if it has not been built: there is no fallback."""
+    """Load libpa.so. Raises if it has not been built, or was built from other
+    sources: there is no fallback."""
     global _lib
     with _lock:
         if _lib is not None:
@@ -143,6 +179,7 @@ def load(path: str = LIB_PATH):
             raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_94_amd.build` "
                                "(the paged-attention kernels have no CPU or PyTorch fallback)")
         lib = ctypes.CDLL(path)
+        check_build_id(lib)
         P = ctypes.POINTER(PaArgs)
         lib.pa_workspace_size.argtypes = [P]
         lib.pa_workspace_size.restype = ctypes.c_size_t
@@ -160,34 +197,43 @@ def load(path: str = LIB_PATH):
         lib.pa_debug_gather.restype = ctypes.c_int
         lib.pa_validate.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
         lib.pa_validate.restype = ctypes.c_int
-        lib.pa_strerror.argtypes = [ctypes.c_int]
-        lib.pa_strerror.restype = ctypes.c_char_p
-        lib.pa_last_error.restype = ctypes.c_char_p
         lib.pa_version.restype = ctypes.c_int
-        V, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        alloc_sigs = {
-            "pa_alloc_create": ([I32, I32, I32, ctypes.POINTER(V)], ctypes.c_int),
-            "pa_alloc_destroy": ([V], None),
-            "pa_alloc_add": ([V, I64], ctypes.c_int),
-            "pa_alloc_add_ring": ([V, I64, I32], ctypes.c_int),
-            "pa_alloc_append": ([V, I64, I32, V, V, V], ctypes.c_int),
-            "pa_alloc_append_batch": ([V, I32, V, V, V, V, V, V], ctypes.c_int),
-            "pa_alloc_release": ([V, I64], ctypes.c_int),
-            "pa_alloc_num_free": ([V], I32),
-            "pa_alloc_block_table": ([V, I32, V, I32, V, V], ctypes.c_int),
-            "pa_alloc_stats": ([V, V, V], ctypes.c_int),
-            "pa_alloc_free_queue": ([V, V, I32, V], ctypes.c_int),
-        }
-        for name, (args, res) in alloc_sigs.items():
-            fn = getattr(lib, name)
-            fn.argtypes = args
-            fn.restype = res
+        lib.pa_build_id.restype = ctypes.c_char_p
+        bind_host(lib)
         _lib = lib
         return lib
 
 
-def check(rc: int) -> None:
+def bind_host(lib):
+    """Declare the signatures of the host-only calls (error strings, block
+    allocator) on lib: libpa.so, or a separate host build of those sources."""
+    lib.pa_strerror.argtypes = [ctypes.c_int]
+    lib.pa_strerror.restype = ctypes.c_char_p
+    lib.pa_last_error.restype = ctypes.c_char_p
+    V, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    alloc_sigs = {
+        "pa_alloc_create": ([I32, I32, I32, ctypes.POINTER(V)], ctypes.c_int),
+        "pa_alloc_destroy": ([V], None),
+        "pa_alloc_add": ([V, I64], ctypes.c_int),
+        "pa_alloc_add_ring": ([V, I64, I32], ctypes.c_int),
+        "pa_alloc_append": ([V, I64, I32, V, V, V], ctypes.c_int),
+        "pa_alloc_append_batch": ([V, I32, V, V, V, V, V, V], ctypes.c_int),
+        "pa_alloc_release": ([V, I64], ctypes.c_int),
+        "pa_alloc_num_free": ([V], I32),
+        "pa_alloc_block_table": ([V, I32, V, I32, V, V], ctypes.c_int),
+        "pa_alloc_stats": ([V, V, V], ctypes.c_int),
+        "pa_alloc_free_queue": ([V, V, I32, V], ctypes.c_int),
+    }
+    for name, (args, res) in alloc_sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+def check(rc: int, lib=None) -> None:
+    """Raise PaError for a failed call; lib is the library that made it (default libpa.so)."""
     if rc != PA_OK:
-        lib = load()
+        lib = lib or load()
         detail = lib.pa_last_error().decode() or lib.pa_strerror(rc).decode()
         raise PaError(rc, detail)

@@ -26,14 +26,19 @@ def _p(a: Optional[np.ndarray]):
 class BlockAllocator:
     """Blocks on demand, release at the end of a sequence, prefix caching of complete blocks."""
 
-    def __init__(self, num_blocks: int, block_size: int = 16, prefix_cache: bool = True):
-        self._lib = _lib.load()
+    def __init__(self, num_blocks: int, block_size: int = 16, prefix_cache: bool = True, lib=None):
+        # lib: libpa.so (default), or another build of the allocator's host sources with the same
+        # signatures bound (_lib.bind_host); the host-sanitizer test passes one.
+        self._lib = lib or _lib.load()
         h = ctypes.c_void_p()
-        _lib.check(self._lib.pa_alloc_create(int(num_blocks), int(block_size), int(bool(prefix_cache)),
+        self._check(self._lib.pa_alloc_create(int(num_blocks), int(block_size), int(bool(prefix_cache)),
                                              ctypes.byref(h)))
         self._h = h
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
+
+    def _check(self, rc: int) -> None:
+        _lib.check(rc, self._lib)
 
     def close(self) -> None:
         if getattr(self, "_h", None):
@@ -46,9 +51,9 @@ class BlockAllocator:
     def add(self, seq_id: int, ring_blocks: int = 0) -> None:
         """Start a sequence; ring_blocks > 0 makes it a ring of that many blocks (window layers)."""
         if ring_blocks:
-            _lib.check(self._lib.pa_alloc_add_ring(self._h, int(seq_id), int(ring_blocks)))
+            self._check(self._lib.pa_alloc_add_ring(self._h, int(seq_id), int(ring_blocks)))
         else:
-            _lib.check(self._lib.pa_alloc_add(self._h, int(seq_id)))
+            self._check(self._lib.pa_alloc_add(self._h, int(seq_id)))
 
     def append(self, seq_id: int, n: int, tokens: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, int]:
         """Grow a sequence by n tokens: (slot ids, -1 where cached; number of cached leading tokens)."""
@@ -57,7 +62,7 @@ class BlockAllocator:
             raise ValueError("tokens must hold n ids")
         slots = np.empty(max(n, 0), dtype=np.int64)
         cached = ctypes.c_int32(0)
-        _lib.check(self._lib.pa_alloc_append(self._h, int(seq_id), int(n), _p(toks), _p(slots),
+        self._check(self._lib.pa_alloc_append(self._h, int(seq_id), int(n), _p(toks), _p(slots),
                                              ctypes.byref(cached)))
         return slots, cached.value
 
@@ -82,7 +87,7 @@ class BlockAllocator:
         return slots, cached
 
     def release(self, seq_id: int) -> None:
-        _lib.check(self._lib.pa_alloc_release(self._h, int(seq_id)))
+        self._check(self._lib.pa_alloc_release(self._h, int(seq_id)))
 
     def num_free(self) -> int:
         return int(self._lib.pa_alloc_num_free(self._h))
@@ -91,17 +96,17 @@ class BlockAllocator:
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         table = np.empty((ids.size, max_blocks), dtype=np.int32)
         lens = np.empty(ids.size, dtype=np.int32)
-        _lib.check(self._lib.pa_alloc_block_table(self._h, int(ids.size), _p(ids), int(max_blocks), _p(table),
+        self._check(self._lib.pa_alloc_block_table(self._h, int(ids.size), _p(ids), int(max_blocks), _p(table),
                                                   _p(lens)))
         return table, lens
 
     def stats(self) -> Tuple[int, int]:
         q, h = ctypes.c_int64(0), ctypes.c_int64(0)
-        _lib.check(self._lib.pa_alloc_stats(self._h, ctypes.byref(q), ctypes.byref(h)))
+        self._check(self._lib.pa_alloc_stats(self._h, ctypes.byref(q), ctypes.byref(h)))
         return q.value, h.value
 
     def free_queue(self) -> np.ndarray:
         out = np.empty(self.num_blocks, dtype=np.int32)
         n = ctypes.c_int32(0)
-        _lib.check(self._lib.pa_alloc_free_queue(self._h, _p(out), int(out.size), ctypes.byref(n)))
+        self._check(self._lib.pa_alloc_free_queue(self._h, _p(out), int(out.size), ctypes.byref(n)))
         return out[:n.value].copy()

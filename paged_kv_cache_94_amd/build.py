@@ -1,13 +1,16 @@
 """Build libpa.so (the HIP kernels plus the C-ABI) for gfx950, in-tree.
 
 Every HIP source is compiled by hipcc for gfx950 only, with packed-fp32
-instructions disabled, and linked into paged_kv_cache_94_amd/libpa.so.
+instructions disabled, and linked into paged_kv_cache_94_amd/libpa.so. The
+library carries the hash of the sources it was built from (pa_build_id);
+the binding refuses a library whose hash differs from its sources'.
 Run as ``python -m paged_kv_cache_94_amd.build``.
 """
 
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -21,7 +24,23 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_valu.hip", "pa_mfma.hip", "pa_aux.hip", "pa_write.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.cpp", "pa_error.cpp", "pa_alloc.cpp", "pa_valu.hip", "pa_mfma.hip", "pa_aux.hip", "pa_write.hip",
+           "pa_prefill.hip"]
+SOURCE_SUFFIXES = (".cpp", ".hip", ".h")
+
+
+def source_hash(root: str = ROOT) -> str:
+    """16 hex digits of a SHA-256 over the library's sources and headers (names and contents)."""
+    h = hashlib.sha256()
+    for sub in (os.path.join("paged_kv_cache_94_amd", "csrc"), "include"):
+        d = os.path.join(root, sub)
+        for name in sorted(os.listdir(d)):
+            if name.endswith(SOURCE_SUFFIXES):
+                h.update(f"{sub}/{name}\0".encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+                h.update(b"\0")
+    return h.hexdigest()[:16]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -51,7 +70,7 @@ def _compile(src: str, extra: list) -> str:
 def build(verbose: bool = False, extra_flags: list | None = None) -> str:
     """Compile every source and link libpa.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra_flags or [])
+    extra = list(extra_flags or []) + [f'-DPA_BUILD_ID="{source_hash()}"']
     jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))

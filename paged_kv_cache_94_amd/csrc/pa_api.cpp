@@ -4,40 +4,15 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <cstdarg>
 #include <cmath>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
-#include <string>
 
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_error.h"
 #include "pa_prefill.h"
 #include "pa_write.h"
-
-namespace pa {
-
-namespace {
-thread_local std::string g_last_error;
-}  // namespace
-
-int fail(int code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return code;
-}
-
-void clear_error() { g_last_error.clear(); }
-
-const char* last_error() { return g_last_error.c_str(); }
-
-}  // namespace pa
 
 namespace {
 
@@ -102,6 +77,8 @@ int validate(const pa_args* a, Entry entry) {
     return fail(PA_ERR_INVALID_ARG, "pa_decode_int8 needs q_dtype PA_BF16 and kv_dtype PA_INT8");
   if (entry != kGather && a->kv_dtype == PA_INT8 && (!a->k_scale || !a->v_scale))
     return fail(PA_ERR_INVALID_ARG, "int8 cache needs k_scale and v_scale");
+  if (a->kv_dtype == PA_INT8 && a->v_pool == a->k_pool && a->v_scale != a->k_scale)
+    return fail(PA_ERR_INVALID_ARG, "values that alias the keys (v_pool == k_pool) need v_scale == k_scale");
   if (a->kv_dtype != PA_INT8 && a->kv_dtype != a->q_dtype)
     return fail(PA_ERR_UNSUPPORTED, "a floating-point cache must have the query's dtype");
   if (a->kv_dtype == PA_INT8 && a->q_dtype != PA_BF16)
@@ -134,6 +111,8 @@ int validate(const pa_args* a, Entry entry) {
 int make_plan(const pa_args* a, Plan* pl) {
   const int G = a->num_q_heads / a->num_kv_heads;
   const int D = a->head_dim;
+  static const pa_tuning kNoTuning = {0, 0, PA_PART_AUTO, 0, 0};
+  const pa_tuning& tu = a->tuning ? *a->tuning : kNoTuning;
   Plan P;
   P.rows = G * a->q_len;
   const int valu_max_rows = 512 / D;   // query rows the vector kernel keeps in registers
@@ -154,6 +133,23 @@ int make_plan(const pa_args* a, Plan* pl) {
   }
   P.nw = P.kernel == 1 ? 4 : 8;   // matrix-core: two 4-wave workgroups per CU measured faster than one of 8
 
+  // Explicit overrides (pa_tuning): checked against what the chosen kernel supports.
+  if (tu.waves != 0 && tu.waves != 4 && tu.waves != 8 && !(P.kernel == 1 && tu.waves == 2))
+    return fail(PA_ERR_UNSUPPORTED, "tuning.waves = %d: the %s kernel takes 4 or 8%s", tu.waves,
+                P.kernel ? "matrix-core" : "vector", P.kernel ? " (or 2)" : "");
+  if (tu.blocks_per_wave < 0 || tu.blocks_per_wave > 64)
+    return fail(PA_ERR_INVALID_ARG, "tuning.blocks_per_wave must be 0..64 (got %d)", tu.blocks_per_wave);
+  if (tu.partition < PA_PART_AUTO || tu.partition > PA_PART_QUEUE)
+    return fail(PA_ERR_INVALID_ARG, "tuning.partition must be a PA_PART_* value (got %d)", tu.partition);
+  if (P.kernel == 0 && tu.partition > PA_PART_ALIGNED)
+    return fail(PA_ERR_UNSUPPORTED, "the vector kernel only takes aligned splits");
+  if (a->num_splits > 0 && tu.partition > PA_PART_ALIGNED)
+    return fail(PA_ERR_INVALID_ARG, "num_splits asks for aligned splits; tuning.partition asks otherwise");
+  if (tu.pieces_per_wg < 0 || tu.pieces_per_wg > 64 || tu.oversub < 0 || tu.oversub > 64)
+    return fail(PA_ERR_INVALID_ARG, "tuning.pieces_per_wg and tuning.oversub must be 0..64");
+  const bool nw_forced = tu.waves != 0;
+  if (nw_forced) P.nw = tu.waves;
+
   const int bs = a->block_size;
   int n_blk_max = (a->max_seq_len + bs - 1) / bs;
   if (a->window > 0) {
@@ -163,18 +159,6 @@ int make_plan(const pa_args* a, Plan* pl) {
   }
   if (n_blk_max < 1) n_blk_max = 1;
   P.n_blk_max = n_blk_max;
-
-  // Tuning knobs for experiments: waves per workgroup (4 or 8), blocks per wave.
-  int bpw_force = 0;
-  bool nw_forced = false;
-  if (const char* e = getenv("PA_WAVES")) {
-    const int v = atoi(e);
-    if (v == 4 || v == 8 || (P.kernel == 1 && v == 2)) {
-      P.nw = v;
-      nw_forced = true;
-    }
-  }
-  if (const char* e = getenv("PA_BLOCKS_PER_WAVE")) bpw_force = atoi(e);
 
   const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
   int S;
@@ -190,7 +174,7 @@ int make_plan(const pa_args* a, Plan* pl) {
     const int64_t per_unit = a->window > 0 ? n_blk_max : (n_blk_max + 1) / 2;
     int64_t bpw = (units * per_unit + slots - 1) / (slots > 0 ? slots : 1);
     bpw = bpw < 4 ? 4 : (bpw > 16 ? 16 : bpw);
-    if (bpw_force > 0) bpw = bpw_force;
+    if (tu.blocks_per_wave > 0) bpw = tu.blocks_per_wave;
     const int64_t bps = bpw * P.nw;
     S = (int)((n_blk_max + bps - 1) / bps);
     if (S < 1) S = 1;
@@ -204,25 +188,25 @@ int make_plan(const pa_args* a, Plan* pl) {
   // many workgroups as are resident at once (two per compute unit at 4
   // waves, one at 8). With few units (sequence, KV head) -- long contexts on
   // one or two KV heads -- units are cut on the device into near-equal
-  // pieces, one per workgroup (partition 2). With many, pieces are handed out
-  // to the workgroups through a sharded queue in the workspace (partition 2
-  // with the queue). In between, and for batches beyond the piece
-  // partition's LDS tables, each workgroup takes an equal share of the
-  // flattened (unit, block) list (partition 1). Forced splits and the vector
-  // kernel keep the aligned splits. For tests and experiments:
-  // PA_BALANCED=0 / PA_PIECES=0|1 turn the balanced partitions off / the
-  // piece partition off or on, PA_QUEUE=0|1 forces the queue off or on, and
-  // PA_PIECES_PER_WG sets the pieces per workgroup the queue aims for.
-  bool balanced = P.kernel == 1 && a->num_splits == 0 && a->num_seqs <= pa::balanced_seq_limit(P.nw);
-  if (const char* e = getenv("PA_BALANCED")) balanced = balanced && atoi(e) != 0;
-  if (balanced) {
+  // pieces, one per workgroup. With many, pieces are handed out to the
+  // workgroups through a sharded queue in the workspace. In between, and for
+  // batches beyond the piece partition's LDS tables, each workgroup takes an
+  // equal share of the flattened (unit, block) list. Forced splits and the
+  // vector kernel keep the aligned splits.
+  const int part = tu.partition;
+  const bool balanced = P.kernel == 1 && a->num_splits == 0 && part != PA_PART_ALIGNED;
+  if (balanced && a->num_seqs > pa::balanced_seq_limit(P.nw)) {
+    if (part != PA_PART_AUTO)
+      return fail(PA_ERR_UNSUPPORTED, "the balanced partitions take at most %d sequences at %d waves",
+                  pa::balanced_seq_limit(P.nw), P.nw);
+  } else if (balanced) {
     // Few units (at most one per two CUs) are cut into one piece per
     // workgroup: one 8-wave workgroup per CU streams them as fast as two of
     // 4 waves and leaves half the partials to merge (16 sequences of 4K-32K
     // tokens on one KV head: kernel 29.4 vs 29.2 us, step 34.9 vs 37.0 us).
-    if (!nw_forced && P.kernel == 1 && 2 * units <= (int64_t)cu_count()) P.nw = 8;
+    if (!nw_forced && 2 * units <= (int64_t)cu_count()) P.nw = 8;
     P.nwg = cu_count() * (8 / P.nw);
-    if (const char* e = getenv("PA_OVERSUB")) { const int v = atoi(e); if (v >= 1 && v <= 64) P.nwg *= v; }
+    if (tu.oversub > 0) P.nwg *= tu.oversub;
     // Measured on MI355X: one piece per workgroup is best for few units
     // (<= nwg/2: 16 long contexts on one KV head), the flattened list for
     // about as many units as workgroups (512 units of 1-4K tokens: 90 us vs
@@ -230,26 +214,42 @@ int make_plan(const pa_args* a, Plan* pl) {
     // length: 333 us vs 347 us for the flattened list).
     const bool few = 2 * units <= P.nwg;
     const bool many = units >= 2 * (int64_t)P.nwg;
-    bool pieces = a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4 && (few || many);
-    if (const char* e = getenv("PA_PIECES")) pieces = a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4 && atoi(e) != 0;
+    const bool pieces_ok = a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4;
+    const bool queue_ok = P.nwg >= pa::kQueueShards;
+    bool pieces, queue;
+    switch (part) {
+      case PA_PART_LIST:
+        pieces = queue = false;
+        break;
+      case PA_PART_PIECES:
+        if (!pieces_ok || !few)
+          return fail(PA_ERR_UNSUPPORTED, "one piece per workgroup needs at most %d sequences, 4+ waves and "
+                      "2 x units <= workgroups (%lld units, %d workgroups)", pa::kMaxPieceSeqs,
+                      (long long)units, P.nwg);
+        pieces = true;
+        queue = false;
+        break;
+      case PA_PART_QUEUE:
+        if (!pieces_ok || !queue_ok)
+          return fail(PA_ERR_UNSUPPORTED, "queued pieces need at most %d sequences, 4+ waves and %d+ workgroups",
+                      pa::kMaxPieceSeqs, pa::kQueueShards);
+        pieces = queue = true;
+        break;
+      default:
+        pieces = pieces_ok && (few || many);
+        queue = !few && queue_ok;
+        if (pieces && !few && !queue) pieces = false;   // (a device too small for the queue)
+        break;
+    }
     P.balanced = pieces ? 2 : 1;
     P.grid = P.nwg;
     if (pieces) {
-      bool queue = !few;
-      int64_t per_wg = 4;
-      if (const char* e = getenv("PA_QUEUE")) queue = atoi(e) != 0;
-      if (const char* e = getenv("PA_PIECES_PER_WG")) { const int v = atoi(e); if (v >= 1 && v <= 64) per_wg = v; }
-      P.queue = queue && P.nwg >= pa::kQueueShards;
+      P.queue = queue;
+      const int64_t per_wg = tu.pieces_per_wg > 0 ? tu.pieces_per_wg : 4;
       P.pieces = queue ? per_wg * P.nwg : P.nwg;
       if (P.pieces < 2 * units) P.pieces = 2 * units;   // the device's search for the piece size needs this
-      if (!P.queue && P.pieces > P.nwg) {               // one piece per workgroup: more pieces need the queue
-        P.queue = P.nwg >= pa::kQueueShards;
-        if (!P.queue) pieces = false;                     // (a device too small for the queue)
-      }
-      if (pieces) P.slots = P.pieces;
-    }
-    if (!pieces) {
-      P.balanced = 1;
+      P.slots = P.pieces;
+    } else {
       P.queue = false;
       P.pieces = 0;
       P.slots = P.nwg + units;
@@ -418,7 +418,12 @@ int pa_validate(const pa_args* a, int32_t* d_status, pa_stream_t stream) {
   if (rc) return rc;
   const pa::Params p = make_params(a, P);
   const int check_scales = a->kv_dtype == PA_INT8 && a->k_scale && a->v_scale;
-  const hipError_t e = pa::launch_validate(p, a->num_blocks, a->max_seq_len, check_scales, d_status,
+  // The piece queue's counters must be zero when a call starts (each call
+  // leaves them so): check them when the call would use the queue.
+  const int32_t* header = (P.queue && a->workspace && a->workspace_bytes >= P.ws_bytes)
+                              ? reinterpret_cast<const int32_t*>(a->workspace)
+                              : nullptr;
+  const hipError_t e = pa::launch_validate(p, a->num_blocks, a->max_seq_len, check_scales, header, d_status,
                                            reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "validate kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
@@ -455,6 +460,8 @@ int pa_cache_write(const pa_write_args* a, pa_stream_t stream) {
   const bool alias = a->v_pool == a->k_pool;
   if (alias && a->v_new != a->k_new)
     return fail(PA_ERR_INVALID_ARG, "v_pool is k_pool but v_new is not k_new");
+  if (alias && a->kv_dtype == PA_INT8 && a->v_scale != a->k_scale)
+    return fail(PA_ERR_INVALID_ARG, "v_pool is k_pool but v_scale is not k_scale");
   if ((int64_t)a->num_tokens * a->num_kv_heads > (int64_t)0x7FFFFFFF * 4)
     return fail(PA_ERR_UNSUPPORTED, "launch too large");
   pa::WriteParams p{};
@@ -503,6 +510,8 @@ int pa_prefill(const pa_prefill_args* a, pa_stream_t stream) {
     return fail(PA_ERR_INVALID_ARG, "scale_per_head is 0, or 1 for an int8 cache");
   if (a->kv_dtype == PA_INT8 && (!a->k_scale || !a->v_scale))
     return fail(PA_ERR_INVALID_ARG, "an int8 cache needs k_scale and v_scale");
+  if (a->kv_dtype == PA_INT8 && a->v_pool == a->k_pool && a->v_scale != a->k_scale)
+    return fail(PA_ERR_INVALID_ARG, "values that alias the keys (v_pool == k_pool) need v_scale == k_scale");
   if (a->num_seqs == 0 || a->total_q == 0) return PA_OK;
   if (a->max_q_len < 1) return fail(PA_ERR_INVALID_ARG, "max_q_len must be >= 1");
   if (a->max_seq_len < a->max_q_len)
@@ -554,20 +563,11 @@ int pa_prefill(const pa_prefill_args* a, pa_stream_t stream) {
   return PA_OK;
 }
 
-const char* pa_strerror(int code) {
-  switch (code) {
-    case PA_OK: return "success";
-    case PA_ERR_INVALID_ARG: return "invalid argument";
-    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case PA_ERR_WORKSPACE: return "workspace missing or too small";
-    case PA_ERR_HIP: return "HIP runtime error";
-    case PA_ERR_NO_BLOCKS: return "not enough free cache blocks";
-  }
-  return "unknown error";
-}
+int pa_version(void) { return 10100; }
 
-const char* pa_last_error(void) { return pa::last_error(); }
-
-int pa_version(void) { return 100; }
+#ifndef PA_BUILD_ID
+#define PA_BUILD_ID "unknown"
+#endif
+const char* pa_build_id(void) { return PA_BUILD_ID; }
 
 }  // extern "C"

@@ -170,7 +170,9 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
 }
 
 // Debug gather: copy the cache rows the attention kernels would load, in
-// logical key order, through the same key_range / row_offset_bytes helpers.
+// logical key order, through the same key_range / table_entry helpers and the
+// same pool-addressing functions (tile_offset_bytes, token_stride_bytes) as the
+// attention kernels and the append.
 // grid.x covers tokens (one wavefront per token, 4 per workgroup), grid.y = sequence.
 __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const char* pool, int32_t row_bytes,
                                                           char* dst, int64_t dst_tokens) {
@@ -186,7 +188,8 @@ __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const ch
   const int32_t phys = p.block_table[(size_t)b * p.maxb + table_entry(p, j / kBlock)];
   const int32_t words = row_bytes / 4;
   for (int32_t g = 0; g < p.Hkv; ++g) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(pool + row_offset_bytes(phys, j % kBlock, g, p.Hkv, row_bytes));
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(pool + tile_offset_bytes(phys, g, p.Hkv, row_bytes) +
+                                                               (size_t)(j % kBlock) * token_stride_bytes(p.Hkv, row_bytes));
     uint32_t* out = reinterpret_cast<uint32_t*>(dst + (((size_t)b * dst_tokens + w) * p.Hkv + g) * (size_t)row_bytes);
     for (int32_t k = lane; k < words; k += 64) out[k] = src[k];
   }
@@ -231,8 +234,11 @@ __device__ __forceinline__ int32_t scale_bits(float ks, float vs) {
 // every key some query sees (positions lo0 .. L-1, in a valid block) are
 // finite, and the V scales are below 255 in magnitude. Bits as in pa.h: 1
 // short, 2 long, 4 bad block, 8 non-finite scale, 16 value scale >= 255.
+// queue_header (non-null when the call would use the piece queue): its
+// "next" and "done" counters must all be zero; bit 32 in status[0] if not.
 __global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_t num_blocks, int32_t max_seq_len,
-                                                          int32_t check_scales, int32_t* status) {
+                                                          int32_t check_scales, const int32_t* queue_header,
+                                                          int32_t* status) {
   __shared__ int32_t bits;
   const int32_t b = blockIdx.x;
   if (threadIdx.x == 0) bits = 0;
@@ -263,13 +269,15 @@ __global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_
           const int32_t j = kr.lo0 + (int32_t)(f / H), h = (int32_t)(f % H);
           const int32_t e = p.block_table[(size_t)b * p.maxb + table_entry(p, j / kBlock)];
           if (e < 0 || e >= num_blocks) continue;                        // already flagged as a bad block
-          const size_t at = ((size_t)e * H + h) * kBlock + j % kBlock;
+          const size_t at = scale_tile_index(e, h, H) + j % kBlock;
           mine |= scale_bits(p.k_scale[at], p.v_scale[at]);
         }
       }
     }
   }
   if (mine) atomicOr(&bits, mine);
+  if (queue_header && b == 0 && threadIdx.x < 2 * kQueueShards && queue_header[threadIdx.x * kQueueStride] != 0)
+    atomicOr(status, 32);
   __syncthreads();
   if (threadIdx.x == 0) {
     status[1 + b] = bits;
@@ -278,10 +286,10 @@ __global__ void __launch_bounds__(256) pa_validate_kernel(const Params p, int32_
 }
 
 hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_len, int check_scales,
-                           int32_t* status, hipStream_t st) {
+                           const int32_t* queue_header, int32_t* status, hipStream_t st) {
   if (p.B == 0) return hipSuccess;
   hipLaunchKernelGGL(pa_validate_kernel, dim3((unsigned)p.B), dim3(256), 0, st, p, num_blocks, max_seq_len,
-                     (int32_t)check_scales, status);
+                     (int32_t)check_scales, queue_header, status);
   return hipGetLastError();
 }
 

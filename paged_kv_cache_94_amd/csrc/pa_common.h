@@ -109,7 +109,7 @@ hipError_t launch_mfma(const Params& p, int kv_dtype, int D, int row_tiles, int 
                        hipStream_t st, const Timing& tm, bool* supported);
 hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st);
 hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_len, int check_scales,
-                           int32_t* status, hipStream_t st);
+                           const int32_t* queue_header, int32_t* status, hipStream_t st);
 hipError_t launch_gather(const Params& p, int kv_dtype, int D, int which, void* dst, int64_t dst_tokens,
                          hipStream_t st);
 }  // namespace pa

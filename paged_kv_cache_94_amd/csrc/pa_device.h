@@ -276,11 +276,33 @@ __device__ __forceinline__ Piece piece_of(const int32_t* nbs, const int32_t* kp,
   return pc;
 }
 
-// Byte offset of (physical block, slot, kv head) row inside a pool laid out
-// [num_blocks][16][Hkv][D] (tiniestgpt notes, "PagedAttention").
+// ---- pool addressing (tiniestgpt notes, "PagedAttention": the pool is
+// [num_blocks][16][Hkv][D], a block-table entry names its first dimension) --
+//
+// Every kernel that reads or writes the cache, and the debug gather, forms
+// its addresses from these three functions and nothing else, so the gather's
+// bit-exact comparison with the oracle checks the attention kernels'
+// addressing too.
+
+// Bytes from one cached row (token) of a (block, KV head) tile to the next.
+__device__ __forceinline__ int32_t token_stride_bytes(int32_t Hkv, int32_t row_bytes) { return Hkv * row_bytes; }
+
+// Byte offset of the (physical block, KV head) tile: its slot-0 row. Rows of
+// the tile follow at token_stride_bytes apart.
+__device__ __forceinline__ size_t tile_offset_bytes(int32_t phys, int32_t g, int32_t Hkv, int32_t row_bytes) {
+  return ((size_t)phys * kBlock * (size_t)Hkv + (size_t)g) * (size_t)row_bytes;
+}
+
+// Byte offset of the (physical block, slot, KV head) row.
 __device__ __forceinline__ size_t row_offset_bytes(int32_t phys, int32_t slot, int32_t g, int32_t Hkv,
                                                    int32_t row_bytes) {
-  return ((size_t)((int64_t)phys * kBlock + slot) * Hkv + g) * (size_t)row_bytes;
+  return tile_offset_bytes(phys, g, Hkv, row_bytes) + (size_t)slot * (size_t)token_stride_bytes(Hkv, row_bytes);
+}
+
+// Index of the first of a (physical block, KV head) tile's 16 per-token int8
+// scales in a [num_blocks][Hkv][16] scale array (one 64-byte run per tile).
+__device__ __forceinline__ size_t scale_tile_index(int32_t phys, int32_t g, int32_t Hkv) {
+  return ((size_t)phys * (size_t)Hkv + (size_t)g) * kBlock;
 }
 
 // ---- lane permutations -------------------------------------------------

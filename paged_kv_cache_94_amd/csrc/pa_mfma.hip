@@ -158,13 +158,13 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   // A (block, KV head) tile: 16 rows of ROW_BYTES, tok_stride apart. Load
   // instruction u gives lane l row u*RPI + l/LPR, bytes 16*(l%LPR) .. +15:
   // every group of LPR lanes reads one row front to back.
-  const int32_t tok_stride = p.Hkv * ROW_BYTES;
+  const int32_t tok_stride = token_stride_bytes(p.Hkv, ROW_BYTES);
   const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
   const int ld_row = lane / LPR;                      // + u*RPI
   const int ld_chunk = lane % LPR;                    // 16-byte piece of the row
   const int32_t lane_off = ld_row * tok_stride + 16 * ld_chunk;
-  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
-  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool);
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
@@ -210,7 +210,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   auto fetch = [&](int32_t k, Fetched& f) __attribute__((always_inline)) {
     const bool valid = k < nmine;
     const int32_t phys = __builtin_amdgcn_readlane(tbl, valid ? k : 0);
-    const size_t tile = (size_t)phys * kBlock * (size_t)tok_stride;
+    const size_t tile = tile_offset_bytes(phys, g, p.Hkv, ROW_BYTES);
     const auto kd = buffer_rsrc(kpool + tile, valid ? tile_bytes : 0);
 #pragma unroll
     for (int u = 0; u < NLOAD; ++u) f.k[u] = buffer_load16<CPOL>(kd, lane_off, u * RPI * tok_stride);
@@ -222,7 +222,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     if constexpr (INT8) {
       // The block's 16 scales of this KV head: one 64-byte run ([block][head][slot]);
       // with per-head scales every lane reads the head's one scale.
-      const size_t s0 = p.head_scales ? (size_t)g : ((size_t)phys * p.Hkv + g) * kBlock;
+      const size_t s0 = p.head_scales ? (size_t)g : scale_tile_index(phys, g, p.Hkv);
       const int32_t sbytes = valid ? (p.head_scales ? 4 : kBlock * 4) : 0;
       const int32_t soff = p.head_scales ? 0 : (lane & 15) * 4;
       f.ks = buffer_load_f32(buffer_rsrc(p.k_scale + s0, sbytes), soff);

@@ -204,11 +204,11 @@ pa_prefill_kernel(const PrefillParams p) {
   // or V, cached row (pi % (32*LPR)) / LPR of the step, 16-byte chunk pi % LPR.
   // A wavefront's 64 pieces of one k lie in one half (one cache block) of one
   // of K and V, so its buffer descriptor is wave-uniform.
-  const int32_t tok_stride = p.Hkv * ROW_BYTES;
+  const int32_t tok_stride = token_stride_bytes(p.Hkv, ROW_BYTES);
   const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
-  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
-  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool);
   const bool token_scales = INT8 && !p.head_scales;
   const bool alias = p.v_pool == p.k_pool;   // V is K: its tile is loaded once and read as both
 
@@ -236,7 +236,7 @@ pa_prefill_kernel(const PrefillParams p) {
     const bool mine1 = wave >= 2;
     const int32_t ph = __builtin_amdgcn_readlane(tbl, (mine1 && has1 ? i0 + 1 : i0) - tbl_base);
     const bool ok = mine1 ? has1 : live;
-    const size_t tb = (size_t)ph * kBlock * (size_t)tok_stride;
+    const size_t tb = tile_offset_bytes(ph, g, p.Hkv, ROW_BYTES);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(buf) + wave * S::IPW * 1024;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {            // K tile, then V tile
@@ -273,8 +273,8 @@ pa_prefill_kernel(const PrefillParams p) {
     const bool has1 = (i0 + 1) * kBlock <= khi;
     const int32_t ph0 = table[table_entry(p, i0)];
     const int32_t ph1 = has1 ? table[table_entry(p, i0 + 1)] : 0;
-    const size_t t0b = (size_t)ph0 * kBlock * (size_t)tok_stride;
-    const size_t t1b = (size_t)ph1 * kBlock * (size_t)tok_stride;
+    const size_t t0b = tile_offset_bytes(ph0, g, p.Hkv, ROW_BYTES);
+    const size_t t1b = tile_offset_bytes(ph1, g, p.Hkv, ROW_BYTES);
     const auto k0 = buffer_rsrc(kpool + t0b, tile_bytes);
     const auto k1 = buffer_rsrc(kpool + t1b, has1 ? tile_bytes : 0);
     const auto v0 = buffer_rsrc(vpool + t0b, tile_bytes);
@@ -294,7 +294,7 @@ pa_prefill_kernel(const PrefillParams p) {
     if (token_scales && wave < 2 && lane < KB) {
       const float* sc = wave == 0 ? p.k_scale : p.v_scale;
       const int32_t ph = lane < kBlock ? ph0 : ph1;
-      lsc = sc[((size_t)ph * p.Hkv + g) * kBlock + (lane % kBlock)];
+      lsc = sc[scale_tile_index(ph, g, p.Hkv) + (lane % kBlock)];
     }
   };
   // Write step s's loaded pieces into LDS buffer `buf` as bf16; keys outside

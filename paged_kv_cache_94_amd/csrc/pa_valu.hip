@@ -100,11 +100,11 @@ pa_valu_kernel(const Params p) {
 
   // A (block, KV head) tile: 16 rows of ROW_BYTES, tok_stride apart. Lane
   // (tsub, part) reads 16 bytes at column part*16 (+ c*LPT*16) of rows tsub + TPI*u.
-  const int32_t tok_stride = p.Hkv * ROW_BYTES;
+  const int32_t tok_stride = token_stride_bytes(p.Hkv, ROW_BYTES);
   const int32_t tile_bytes = (kBlock - 1) * tok_stride + ROW_BYTES;
   const int32_t lane_off = tsub * tok_stride + part * 16;
-  const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (size_t)g * ROW_BYTES;
-  const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (size_t)g * ROW_BYTES;
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool);
   const int32_t* table = p.block_table + (size_t)b * p.maxb;
   int32_t* visits = p.visits ? p.visits + ((size_t)b * p.Hkv + g) * p.maxb : nullptr;
 
@@ -122,7 +122,7 @@ pa_valu_kernel(const Params p) {
   auto fetch = [&](int32_t k, Tile& kr_, Tile& vr_) __attribute__((always_inline)) {
     const bool valid = k < nmine;
     const int32_t phys = __builtin_amdgcn_readlane(tbl, valid ? k : 0);
-    const size_t tile = (size_t)phys * kBlock * (size_t)tok_stride;
+    const size_t tile = tile_offset_bytes(phys, g, p.Hkv, ROW_BYTES);
     const auto kd = buffer_rsrc(kpool + tile, valid ? tile_bytes : 0);
     const auto vd = buffer_rsrc(vpool + tile, valid ? tile_bytes : 0);
 #pragma unroll

@@ -97,17 +97,18 @@ __global__ void __launch_bounds__(256) pa_cache_write_kernel(const WriteParams p
   // Skipped token, id outside the pool, or a lane past the last row: nothing is stored,
   // but the lane still takes part in the row maximum's shuffles.
   const bool store = s >= 0 && s < (int64_t)p.num_blocks * kBlock;
-  const int64_t blk = store ? s / kBlock : 0;
+  const int32_t blk = store ? (int32_t)(s / kBlock) : 0;
   const int32_t slot = store ? (int32_t)(s % kBlock) : 0;
   const size_t in = ((size_t)t * p.Hkv + g) * D + (size_t)sub * EPL;                    // source element
-  const size_t at = ((size_t)(blk * kBlock + slot) * p.Hkv + g) * D + (size_t)sub * EPL;  // pool element
+  constexpr int ECACHE = KV == 2 ? 1 : ESRC;                                           // bytes per cache element
+  const size_t at = row_offset_bytes(blk, slot, g, p.Hkv, D * ECACHE) + (size_t)sub * EPL * ECACHE;  // pool byte
   const uint4 zero = {0u, 0u, 0u, 0u};
   const uint4 wk = store ? *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.k_new) + in * ESRC) : zero;
   const uint4 wv = store && p.write_v
                        ? *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.v_new) + in * ESRC)
                        : zero;
   if constexpr (KV == 2) {
-    const size_t sat = ((size_t)blk * p.Hkv + g) * kBlock + slot;
+    const size_t sat = scale_tile_index(blk, g, p.Hkv) + slot;
     const bool hs = p.head_scales != 0;
     const float gk = hs && live_row ? p.k_scale[g] : 1.0f;
     const float gv = hs && live_row ? p.v_scale[g] : 1.0f;
@@ -132,8 +133,8 @@ __global__ void __launch_bounds__(256) pa_cache_write_kernel(const WriteParams p
   } else {
     static_assert(KV == (SRC_BF16 ? 1 : 0), "a float cache takes rows of its own type");
     if (store) {
-      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.k_pool) + at * ESRC) = wk;
-      if (p.write_v) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.v_pool) + at * ESRC) = wv;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.k_pool) + at) = wk;
+      if (p.write_v) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.v_pool) + at) = wv;
     }
   }
 }

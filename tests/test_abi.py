@@ -282,7 +282,7 @@ def test_zero_sequences_enqueue_nothing(lib):
 def test_strerror(lib):
     for code in range(6):
         assert lib.pa_strerror(code)
-    assert lib.pa_version() >= 100
+    assert lib.pa_version() >= 10100
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -293,3 +293,85 @@ def test_missing_library_fails_loudly(tmp_path):
             _lib.load(str(tmp_path / "absent.so"))
         finally:
             _lib._lib = _lib._lib_backup
+
+
+def _tuned(a, **fields):
+    t = _lib.PaTuning()
+    for k, v in fields.items():
+        setattr(t, k, v)
+    a._t = t
+    a.tuning = ctypes.addressof(t)
+    return a
+
+
+C3_LIKE = dict(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768, max_blocks_per_seq=2048)
+
+
+@pytest.mark.parametrize("part,balanced,queue", [
+    (_lib.PA_PART_ALIGNED, 0, 0), (_lib.PA_PART_LIST, 1, 0), (_lib.PA_PART_PIECES, 2, 0), (_lib.PA_PART_QUEUE, 2, 1)])
+def test_tuning_selects_the_partition(lib, part, balanced, queue):
+    info = _lib.PaPlanInfo()
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(**C3_LIKE), partition=part)), ctypes.byref(info)) == 0
+    assert info.kernel == 1 and info.balanced == balanced and info.queue == queue
+
+
+def test_tuning_waves_and_rejections(lib):
+    info = _lib.PaPlanInfo()
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(**C3_LIKE), waves=4)), ctypes.byref(info)) == 0
+    assert info.waves_per_group == 4
+    for fields, code in [
+        (dict(waves=3), _lib.PA_ERR_UNSUPPORTED),
+        (dict(partition=9), _lib.PA_ERR_INVALID_ARG),
+        (dict(pieces_per_wg=65), _lib.PA_ERR_INVALID_ARG),
+        (dict(oversub=-1), _lib.PA_ERR_INVALID_ARG),
+        (dict(blocks_per_wave=-2), _lib.PA_ERR_INVALID_ARG),
+    ]:
+        assert lib.pa_plan(ctypes.byref(_tuned(_args(**C3_LIKE), **fields)), ctypes.byref(info)) == code, fields
+    # The vector kernel (2 rows per KV head) has only aligned splits, and only 4 or 8 waves.
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(), partition=_lib.PA_PART_LIST)), ctypes.byref(info)) == \
+        _lib.PA_ERR_UNSUPPORTED
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(), waves=2)), ctypes.byref(info)) == _lib.PA_ERR_UNSUPPORTED
+    # Forced splits are aligned splits.
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(**C3_LIKE, num_splits=4), partition=_lib.PA_PART_QUEUE)),
+                       ctypes.byref(info)) == _lib.PA_ERR_INVALID_ARG
+    # One piece per workgroup cannot take more units than half the workgroups.
+    many = dict(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128, window=0, max_seq_len=16384,
+                max_blocks_per_seq=1024)
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(**many), partition=_lib.PA_PART_PIECES)), ctypes.byref(info)) == \
+        _lib.PA_ERR_UNSUPPORTED
+    assert lib.pa_plan(ctypes.byref(_tuned(_args(**many), partition=_lib.PA_PART_LIST)), ctypes.byref(info)) == 0
+    assert info.balanced == 1
+
+
+def test_library_reads_no_environment():
+    # The launch plan depends on the arguments only: no source calls getenv.
+    csrc = os.path.join(ROOT, "paged_kv_cache_94_amd", "csrc")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        assert "getenv" not in text, name
+
+
+def test_int8_aliased_pools_need_one_scale_array(lib):
+    # Values that are the keys (v_pool == k_pool) are dequantized with the keys' scales.
+    a = _args(kv_dtype=_lib.PA_INT8, num_q_heads=64, head_dim=128, window=0, max_seq_len=4096,
+              max_blocks_per_seq=256, k_pool=16, v_pool=16, k_scale=8, v_scale=24)
+    assert lib.pa_decode_int8(ctypes.byref(a), None) == _lib.PA_ERR_INVALID_ARG
+    assert b"v_scale" in lib.pa_last_error()
+    w = _wargs(k_pool=16, v_pool=16, k_new=16, v_new=16, k_scale=8, v_scale=16)
+    assert lib.pa_cache_write(ctypes.byref(w), None) == _lib.PA_ERR_INVALID_ARG
+    p = _pargs(kv_dtype=_lib.PA_INT8, k_pool=16, v_pool=16, k_scale=8, v_scale=24)
+    assert lib.pa_prefill(ctypes.byref(p), None) == _lib.PA_ERR_INVALID_ARG
+
+
+def test_build_id_matches_sources_and_stale_copies_are_refused(lib, tmp_path):
+    import shutil
+    from paged_kv_cache_94_amd import build
+    assert lib.pa_build_id().decode() == build.source_hash()
+    _lib.check_build_id(lib)                     # the library in the tree is current
+    # A copy of the sources with one kernel edited no longer matches this binary.
+    for sub in (os.path.join("paged_kv_cache_94_amd", "csrc"), "include"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub)
+    with open(tmp_path / "paged_kv_cache_94_amd" / "csrc" / "pa_valu.hip", "a") as f:
+        f.write("\n// edited\n")
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        _lib.check_build_id(lib, root=str(tmp_path))

@@ -125,8 +125,8 @@ def test_small_problems(case, splits):
 # --- the matrix-core kernel's partitions ---------------------------------------------------------
 # Pieces (one run of one unit per workgroup), pieces handed out through the
 # workspace queue, slices of the flattened list (a workgroup may span several
-# units) and aligned splits must each match the oracle; PA_PIECES /
-# PA_BALANCED switch the library's choice off and PA_QUEUE forces the queue.
+# units) and aligned splits must each match the oracle. Each is asked for
+# through the ABI (pa_args.tuning.partition).
 
 PARTITION_CASES = [
     ([300, 1000, 47], 1, 16, 1, 256, 0, "bf16", "bf16", True),
@@ -138,29 +138,25 @@ PARTITION_CASES = [
 
 @pytest.mark.parametrize("case", PARTITION_CASES, ids=_ids)
 @pytest.mark.parametrize("mode", ["pieces", "queue", "list", "aligned"])
-def test_mfma_partitions(case, mode, monkeypatch):
-    monkeypatch.setenv("PA_QUEUE", "1" if mode == "queue" else "0")
-    if mode not in ("pieces", "queue"):
-        monkeypatch.setenv("PA_PIECES", "0")
-    if mode == "aligned":
-        monkeypatch.setenv("PA_BALANCED", "0")
+def test_mfma_partitions(case, mode):
+    tuning = {"partition": mode}
     lens, q_len, Hq, Hkv, D, window, qd, kvd, alias = case
     x = make_inputs(lens, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=qd, kv_dtype=kvd,
                     window=window, alias_v=alias, poison=True, seed=zlib.crc32(repr((case, mode)).encode()))
     _log(f"partition {mode} {_ids(case)}")
     dev = Dev(x)
-    plan = dev.plan()
+    plan = dev.plan(tuning=tuning)
     assert plan["kernel"] == 1 and plan["balanced"] == {"pieces": 2, "queue": 2, "list": 1, "aligned": 0}[mode]
     assert plan["queue"] == (mode == "queue")
     ws = torch.zeros(max(1, plan["workspace_bytes"]), dtype=torch.uint8, device="cuda")
-    got = dev.run_f64(workspace=ws)
+    got = dev.run_f64(workspace=ws, tuning=tuning)
     assert not np.isnan(got).any()
     assert max_err(got, _oracle(x)) <= TOL[kvd]
     # A second call on the same workspace: the queue words must be back at zero.
     assert not ws[:4096].any().item()
-    np.testing.assert_array_equal(dev.run_f64(workspace=ws), got)
+    np.testing.assert_array_equal(dev.run_f64(workspace=ws, tuning=tuning), got)
     visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
-    dev.run(debug_visits=visits)
+    dev.run(debug_visits=visits, tuning=tuning)
     expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
     np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
 
