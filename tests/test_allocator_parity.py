@@ -41,10 +41,10 @@ def _prompt_tokens(rng, vocab):
     return [int(t) for t in stem[:k]] + [int(t) for t in rng.integers(0, vocab, n - k)]
 
 
-def _run(seed, num_blocks, steps, prefix_cache=True, vocab=3, no_ids_rate=0.05, ring_rate=0.15):
+def _run(seed, num_blocks, steps, prefix_cache=True, vocab=3, no_ids_rate=0.05, ring_rate=0.15, lib=None):
     rng = np.random.default_rng(seed)
     ref = A.RefAllocator(num_blocks, BS, prefix_cache)
-    lib = BlockAllocator(num_blocks, BS, prefix_cache)
+    lib = BlockAllocator(num_blocks, BS, prefix_cache, lib=lib)
     next_id = 1000
     errors = 0
     for _ in range(steps):
