@@ -2,28 +2,41 @@
 """Paged decode-attention benchmark on one MI355X.
 
 One step = one paged decode-attention call (attention kernel, plus the
-split-combine kernel when the key range is split) over one batch of the
-synthetic workload, inputs resident in HBM. The default workload is the
-Gemma4-12B-like local layer: 32 sequences, one query token each, 16 query
-heads on 8 KV heads, head_dim 256, bf16, 16-token blocks, a 1024-token
-sliding window, context lengths uniform in [512, 8192], blocks randomly
-permuted in a pool of total need + 10%.
+split-combine kernel when the key range is split) over one batch of a
+synthetic workload, inputs resident in HBM. By default every workload of the
+set is timed in one run, each with the same number of steps:
 
+  C5 verify5-bf16          (the headline: the largest single-GPU workload)
+                           256 sequences x 5 query tokens (speculative verify,
+                           causal within the 5), 32 query heads on 8 KV heads,
+                           head_dim 128, bf16, lognormal lengths (median 1024)
+  C1 tiny-f32              2 sequences (37, 70 tokens), fp32, 4 / 2 heads, D 64
+  C2 gemma4-12b-local-bf16 32 sequences, 16 / 8 heads, D 256, window 1024
+  C3 gemma4-12b-global-bf16 16 sequences of 4K-32K, 16 heads on 1 KV head,
+                           D 256, values are the keys
+  C4 gqa70b-int8kv         64 sequences, 64 / 8 heads, D 128, int8 cache
+
+Blocks are 16 tokens, randomly permuted in a pool of total need + 10%.
 Between steps the call rotates over several device copies of the cache (and
 its own block table) so that no step finds its cache in the 256 MB
 Infinity Cache from the previous one: every step reads from HBM.
 
 Prints ONE JSON line on stdout (the run's record); diagnostics go to stderr.
-  value     = queries per second over the K timed steps (query = one token of
-              one sequence through all heads of the layer)
+  value     = the headline workload's queries per second over the K timed
+              steps (query = one token of one sequence through all heads of
+              the layer)
   roofline  = algorithmic bytes of a step / mean duration of the attention
-              kernel; on every 8th timed step (--event-every) the library
-              stamps a pair of HIP events from that kernel's own dispatch on
-              the launch stream (hipExtLaunchKernel), the same start/end
-              timestamps a kernel trace reports. The events are created
-              without the system-scope fence (hipEventDisableSystemFence),
-              whose cache writeback and invalidation would cost every stamped
-              step GPU time and slow the kernel after it.
+              kernel; on every max(1, K // 16)-th timed step (--event-every)
+              the library stamps a pair of HIP events from that kernel's own
+              dispatch on the launch stream (hipExtLaunchKernel), the same
+              start/end timestamps a kernel trace reports. The events are
+              created without the system-scope fence
+              (hipEventDisableSystemFence), whose cache writeback and
+              invalidation would cost every stamped step GPU time and slow
+              the kernel after it. traffic = HBM bytes per launch from
+              rocprofv3 counters (traffic_source names the summary), or null
+              when no counter pass matches the current kernel sources and plan
+  config.configs = the same figures for every workload of the run
   cpu_baseline = the fp64 oracle on the host's cores, same workload
   block_allocator = host time of the block allocator's work for one step
               of the same batch (grow every sequence by its q_len new
@@ -59,19 +72,19 @@ METRIC = "decode-attention queries/s and achieved KV HBM GB/s (% of MI355X peak)
 # holds only for the kernel sources and the launch plan it was taken with;
 # for anything else the record's traffic is null.
 MEASURED_TRAFFIC = {
-    1: {"kernel_sources": "bcf777cd3beef791",
+    1: {"source": "profiles/pa_valu_kernel-tiny_f32-hbm_counters.txt", "kernel_sources": "bcf777cd3beef791",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 4, "balanced": 0, "pieces": 0, "queue": 0},
         "fetch_kib": 93, "fetch_factor": 2.0, "write_kib": 2, "write_factor": 1.0},
-    2: {"kernel_sources": "bcf777cd3beef791",
+    2: {"source": "profiles/pa_valu_kernel-gemma4_12b_local_bf16-hbm_counters.txt", "kernel_sources": "bcf777cd3beef791",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256, "balanced": 0, "pieces": 0, "queue": 0},
         "fetch_kib": 132873, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
-    3: {"kernel_sources": "be88d9a4f62d2ca4",
+    3: {"source": "profiles/pa_mfma_kernel-gemma4_12b_global_bf16-hbm_counters.txt", "kernel_sources": "be88d9a4f62d2ca4",
         "plan": {"kernel": 1, "rows": 16, "waves_per_group": 8, "splits": 57, "grid": 256, "balanced": 2, "pieces": 256, "queue": 0},
         "fetch_kib": 61350, "fetch_factor": 2.0, "write_kib": 4112, "write_factor": 1.0},
-    4: {"kernel_sources": "be88d9a4f62d2ca4",
+    4: {"source": "profiles/pa_mfma_kernel-gqa70b_int8kv-hbm_counters.txt", "kernel_sources": "be88d9a4f62d2ca4",
         "plan": {"kernel": 1, "rows": 8, "waves_per_group": 4, "splits": 4, "grid": 512, "balanced": 1, "pieces": 0, "queue": 0},
         "fetch_kib": 189527, "fetch_factor": 2.0, "write_kib": 3997, "write_factor": 1.0},
-    5: {"kernel_sources": "be88d9a4f62d2ca4",
+    5: {"source": "profiles/pa_mfma_kernel-verify5_bf16-hbm_counters.txt", "kernel_sources": "be88d9a4f62d2ca4",
         "plan": {"kernel": 1, "rows": 20, "waves_per_group": 4, "splits": 16, "grid": 512, "balanced": 2, "pieces": 4096, "queue": 1},
         "fetch_kib": 838486, "fetch_factor": 2.0, "write_kib": 35636, "write_factor": 1.0},
 }
@@ -107,12 +120,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="workload (2 = the Gemma4-12B local layer; others for their own measurements)")
+    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5],
+                    help="0 (default): every workload, the speculative-verify step (5, the largest) as the "
+                         "headline; 1-5: that workload alone")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated across steps (0: enough to exceed 4x the Infinity Cache)")
     ap.add_argument("--num-splits", type=int, default=0, help="force the context split count (0: library plan)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the headline's oracle baseline")
+    ap.add_argument("--cpu-seconds-others", type=float, default=3.0,
+                    help="budget for the oracle baseline of each other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the KV append timing")
     ap.add_argument("--ring", action="store_true",
@@ -120,9 +136,10 @@ def parse():
     ap.add_argument("--head-scales", action="store_true", help="int8 workload: one scale per KV head")
     ap.add_argument("--prefill", type=int, default=0, choices=[0, 1, 2, 3],
                     help="time a paged prefill workload instead of a decode step (1 local layer, 2 global, 3 int8)")
-    ap.add_argument("--event-every", type=int, default=8,
+    ap.add_argument("--event-every", type=int, default=0,
                     help="decode: stamp the attention kernel's dispatch with a HIP event pair on every Nth timed "
-                         "step (a pair on every step adds GPU and host time to each step)")
+                         "step (0: every max(1, steps // 16)-th, so at least 10 samples from 10 steps on; a pair "
+                         "on every step adds GPU and host time to each step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
     return ap.parse_args()
@@ -193,17 +210,37 @@ def event_pair(torch):
 
 
 def host_cpu() -> str:
-    """The host's CPU model and logical CPU count (for the CPU baseline's record)."""
-    model = "unknown CPU"
+    """The host's CPU as lscpu names it (model name, family/model/stepping, sockets,
+    cores, threads) and the logical CPUs this process may run on."""
+    fields = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
         pass
-    return f"{model}, {os.cpu_count()} logical CPUs"
+    if "Model name" not in fields:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        fields["Model name"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    desc = fields.get("Model name", "unknown CPU")
+    ids = [f"{k.lower()} {fields[k]}" for k in ("CPU family", "Model", "Stepping") if k in fields]
+    topo = [f"{fields[k]} {k.lower()}" for k in ("Socket(s)", "Core(s) per socket", "Thread(s) per core")
+            if k in fields]
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    parts = [desc] + ([", ".join(ids)] if ids else []) + ([", ".join(topo)] if topo else [])
+    return "; ".join(parts) + f"; {fields.get('CPU(s)', os.cpu_count())} logical CPUs, {usable} usable"
 
 
 def time_steps(torch, np, calls, steps: int, every: int):
@@ -398,18 +435,11 @@ def main_prefill(args) -> int:
     return 0
 
 
-def main() -> int:
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "decode attention shards by sequence or KV head with no exchange, so a multi-GPU figure "
-              "would be N independent copies of this one.", file=sys.stderr)
-        return 2
+CONFIG_ORDER = (5, 1, 2, 3, 4)   # the headline (largest single-GPU workload) first, then the others
 
-    if args.prefill:
-        return main_prefill(args)
 
+def run_decode(idx: int, args, *, cpu_seconds: float, one_core: bool, extras: bool) -> dict:
+    """Time the decode step of workload `idx` and return its record."""
     import numpy as np
     import torch
 
@@ -417,22 +447,16 @@ def main() -> int:
     from paged_kv_cache_94_amd import accounting
     from workloads import CONFIGS, make_config
 
-    if not os.path.exists(pa.library_path()):
-        from paged_kv_cache_94_amd import build
-        build.build()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    cfg = CONFIGS[args.config]
+    cfg = CONFIGS[idx]
     t0 = time.time()
-    x = make_config(args.config, ring=args.ring, head_scales=args.head_scales)
+    x = make_config(idx, ring=args.ring, head_scales=args.head_scales)
     acct = accounting.for_inputs(x)
-    log(f"workload {x.name}: B={x.batch} q_len={x.q_len} Hq={x.num_q_heads} Hkv={x.num_kv_heads} "
+    log(f"[{idx}] workload {x.name}: B={x.batch} q_len={x.q_len} Hq={x.num_q_heads} Hkv={x.num_kv_heads} "
         f"D={x.head_dim} window={x.window} kv={x.kv_dtype} pool={x.num_blocks} blocks "
         f"(generated in {time.time() - t0:.1f}s)")
-    log(f"algorithmic bytes/step {acct['alg_bytes'] / 1e6:.1f} MB, touched KV {acct['touched_kv_bytes'] / 1e6:.1f} MB, "
-        f"flops/step {acct['flops'] / 1e9:.2f} G")
+    log(f"[{idx}] algorithmic bytes/step {acct['alg_bytes'] / 1e6:.1f} MB, touched KV "
+        f"{acct['touched_kv_bytes'] / 1e6:.1f} MB, flops/step {acct['flops'] / 1e9:.2f} G")
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -445,7 +469,7 @@ def main() -> int:
     k0 = to_dev(x.k_pool)
     v0 = k0 if x.v_aliases_k else to_dev(x.v_pool)
     ks0 = None if x.k_scale is None else to_dev(x.k_scale)
-    vs0 = None if x.v_scale is None else to_dev(x.v_scale)
+    vs0 = None if x.v_scale is None else (ks0 if x.v_scale is x.k_scale else to_dev(x.v_scale))
     table0 = to_dev(x.block_table)
     entry = "verify" if x.q_len > 1 else ("decode_int8" if x.kv_dtype == "int8" else "decode")
     out = torch.empty_like(q)
@@ -457,19 +481,19 @@ def main() -> int:
             k = torch.empty_like(k0).copy_(k0)
             v = k if x.v_aliases_k else torch.empty_like(v0).copy_(v0)
             ks = None if ks0 is None else torch.empty_like(ks0).copy_(ks0)
-            vs = None if vs0 is None else torch.empty_like(vs0).copy_(vs0)
+            vs = None if vs0 is None else (ks if vs0 is ks0 else torch.empty_like(vs0).copy_(vs0))
             table = table0.clone()
         calls.append(pa.Prepared(entry, out, q, k, v, table, lens, window=x.window, scale=x.scale,
                                  max_seq_len=x.max_seq_len, k_scale=ks, v_scale=vs, num_splits=args.num_splits,
                                  ring_blocks=x.ring_blocks))
     plan = pa.plan(q, k0, v0, table0, lens, window=x.window, scale=x.scale, max_seq_len=x.max_seq_len,
                    k_scale=ks0, v_scale=vs0, num_splits=args.num_splits, ring_blocks=x.ring_blocks)
-    log(f"plan: {plan}; {copies} cache copies rotated")
+    log(f"[{idx}] plan: {plan}; {copies} cache copies rotated")
 
     # The timed steps run back to back; every `every`-th one also carries a
     # pair of HIP events stamped by the attention kernel's own dispatch
     # (hipExtLaunchKernel), whose mean is the kernel duration below.
-    every = max(1, args.event_every)
+    every = args.event_every or max(1, args.steps // 16)
     for i in range(args.warmup):
         calls[i % copies].launch()
     torch.cuda.synchronize()
@@ -477,36 +501,59 @@ def main() -> int:
     elapsed = step_s * args.steps
     srt = sorted(kern_ms)
     pct = {k: srt[min(len(srt) - 1, int(f * len(srt)))] * 1e3 for k, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
-    ms_per_step = elapsed / args.steps * 1e3
     queries = acct["queries"]
     value = queries * args.steps / elapsed
     achieved = acct["alg_bytes"] / kern_s / 1e9
-    step_gbs = acct["alg_bytes"] / (elapsed / args.steps) / 1e9
-    log(f"attention kernel: mean {kern_s * 1e6:.2f} us (p10 {pct['p10']:.2f}, median {pct['p50']:.2f}, "
-        f"p90 {pct['p90']:.2f}, min {min(kern_ms) * 1e3:.2f}, max {max(kern_ms) * 1e3:.2f}) "
-        f"-> {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS * 100:.1f}% of peak; "
-        f"whole step {ms_per_step * 1e3:.2f} us -> {step_gbs:.0f} GB/s, {value:.4g} queries/s")
+    step_gbs = acct["alg_bytes"] / step_s / 1e9
+    log(f"[{idx}] attention kernel: mean {kern_s * 1e6:.2f} us over {len(kern_ms)} stamped steps (p10 "
+        f"{pct['p10']:.2f}, median {pct['p50']:.2f}, p90 {pct['p90']:.2f}) -> {achieved:.0f} GB/s = "
+        f"{achieved / HBM_PEAK_GBS * 100:.1f}% of peak; whole step {step_s * 1e6:.2f} us -> {step_gbs:.0f} GB/s, "
+        f"{value:.4g} queries/s")
 
-    # Warm: every step re-reads the same cache copy, so the Infinity Cache
-    # (256 MB) can serve what of it fits. Reported beside the cold figures, never as them.
-    warm = None
-    if copies > 1:
-        wsteps = max(8, args.steps // 2)
-        w_step, w_kern, _ = time_steps(torch, np, calls[:1], wsteps, every)
-        warm = {"what": "every step re-reads one cache copy (the Infinity Cache may hold part of it)",
-                "steps": wsteps, "kernel_us": w_kern * 1e6, "ms_per_step": w_step * 1e3,
-                "queries_per_s": acct["queries"] / w_step, "kernel_GBps": acct["alg_bytes"] / w_kern / 1e9}
-        log(f"warm (one cache copy): attention kernel {w_kern * 1e6:.2f} us, step {w_step * 1e6:.2f} us")
+    traffic = None if (args.ring or args.head_scales or args.num_splits) else measured_traffic(idx, plan)
+    rec = {
+        "workload": f"{x.name}: B={x.batch}, q_len={x.q_len}, Hq={x.num_q_heads}, Hkv={x.num_kv_heads}, "
+                    f"D={x.head_dim}, block=16, window={x.window}, kv={x.kv_dtype}, lens {cfg['lens']} "
+                    f"(seed {idx})",
+        "batch": x.batch,
+        "q_len": x.q_len,
+        "dtype": {"f32": "f32", "bf16": "bf16", "int8": "int8 cache, bf16 q"}[x.kv_dtype],
+        "alg_bytes_per_step": acct["alg_bytes"],
+        "queries_per_step": queries,
+        "kernel": ("pa_valu_kernel" if plan["kernel"] == 0 else "pa_mfma_kernel"),
+        "kernel_us": {"mean": kern_s * 1e6, **pct},
+        "kernel_stamped_steps": len(kern_ms),
+        "achieved_GBps": achieved,
+        "frac": achieved / HBM_PEAK_GBS,
+        "step_us": step_s * 1e6,
+        "step_GBps": step_gbs,
+        "queries_per_s": value,
+        "ms_per_step": step_s * 1e3,
+        "plan": {k: plan[k] for k in ("kernel", "rows", "waves_per_group", "splits", "grid", "balanced", "pieces",
+                                      "queue")},
+        "cache_copies": copies,
+        "traffic": traffic,
+        "traffic_source": (MEASURED_TRAFFIC[idx]["source"] if traffic is not None else
+                           "null: no counter pass matches these kernel sources and this plan"),
+    }
 
-    alloc = measure_allocator(np, x, steps=200)
-    log(f"block allocator: {alloc['us_per_step']:.1f} us of host time per step for {x.batch} sequences")
-
-    app = None
-    if not args.no_append:
-        app = measure_append(pa, accounting, torch, np, x, k0, v0, ks0, vs0, reps=50)
-        for name, r in app.items():
-            log(f"kv append ({name}): {r['tokens']} tokens {r['src_dtype']} -> {x.kv_dtype}: "
-                f"{r['us_mean']:.2f} us -> {r['GBps']:.0f} GB/s")
+    if extras:
+        # Warm: every step re-reads the same cache copy, so the Infinity Cache
+        # (256 MB) can serve what of it fits. Reported beside the cold figures, never as them.
+        if copies > 1:
+            wsteps = max(8, args.steps // 2)
+            w_step, w_kern, _ = time_steps(torch, np, calls[:1], wsteps, every)
+            rec["warm"] = {"what": "every step re-reads one cache copy (the Infinity Cache may hold part of it)",
+                           "steps": wsteps, "kernel_us": w_kern * 1e6, "ms_per_step": w_step * 1e3,
+                           "queries_per_s": queries / w_step, "kernel_GBps": acct["alg_bytes"] / w_kern / 1e9}
+            log(f"[{idx}] warm (one cache copy): attention kernel {w_kern * 1e6:.2f} us, step {w_step * 1e6:.2f} us")
+        rec["block_allocator"] = measure_allocator(np, x, steps=200)
+        log(f"[{idx}] block allocator: {rec['block_allocator']['us_per_step']:.1f} us of host time per step")
+        if not args.no_append:
+            rec["kv_append"] = measure_append(pa, accounting, torch, np, x, k0, v0, ks0, vs0, reps=50)
+            for name, r in rec["kv_append"].items():
+                log(f"[{idx}] kv append ({name}): {r['tokens']} tokens {r['src_dtype']} -> {x.kv_dtype}: "
+                    f"{r['us_mean']:.2f} us -> {r['GBps']:.0f} GB/s")
 
     if args.calibrate_copy:
         n = 1 << 30
@@ -515,74 +562,119 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device-to-device copies done")
+        del src, dst
+        log(f"[{idx}] copy calibration: 3 x 1 GiB device-to-device copies done")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle   # the CPU baseline leg is the only part of the benchmark that uses the oracle
-        prob = oracle.Problem.from_inputs(x)
-        threads = oracle.default_threads()
-        reps, spent = 0, 0.0
-        while reps < 2 or spent < args.cpu_seconds:
+    del calls, out, q, lens, k0, v0, ks0, vs0, table0, k, v, ks, vs, table
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(np, x, queries, cpu_seconds=cpu_seconds, one_core=one_core)
+        log(f"[{idx}] cpu baseline: {rec['cpu_baseline']['value']:.4g} queries/s on "
+            f"{rec['cpu_baseline']['cores']} threads")
+    return rec
+
+
+def cpu_baseline(np, x, queries: int, *, cpu_seconds: float, one_core: bool) -> dict:
+    """The fp64 oracle on the host's cores over the same batch (a baseline, not the target)."""
+    import oracle   # the CPU baseline leg is the only part of the benchmark that uses the oracle
+    prob = oracle.Problem.from_inputs(x)
+    threads = oracle.default_threads()
+    reps, spent = 0, 0.0
+    while reps < 1 or spent < cpu_seconds:
+        c0 = time.perf_counter()
+        oracle.attention(prob, threads=threads)
+        spent += time.perf_counter() - c0
+        reps += 1
+        if reps >= 1000:
+            break
+    cpu = {"value": queries * reps / spent, "unit": "queries/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole {x.name} batch ({x.batch} sequences x {x.q_len} query token(s), all "
+                     f"{x.num_q_heads} heads), fp64, repeated {reps} times in {spent:.1f} s",
+           "host_cpu": host_cpu()}
+    if one_core and threads > 1:
+        # The same oracle on one core, over a bounded slice of the batch's rows.
+        rows_total = queries * x.num_q_heads
+        rng = np.random.default_rng(0)
+        n1, spent1, done1 = 64, 0.0, 0
+        while spent1 < cpu_seconds / 3 and done1 < rows_total:
+            rows = rng.integers(0, rows_total, n1).astype(np.int64)
             c0 = time.perf_counter()
-            oracle.attention(prob, threads=threads)
-            spent += time.perf_counter() - c0
-            reps += 1
-            if reps >= 1000:
-                break
-        cpu = {"value": queries * reps / spent, "unit": "queries/s", "cores": threads, "kind": "oracle",
-               "sample": f"the whole {x.name} batch ({x.batch} sequences x {x.q_len} query token(s), all "
-                         f"{x.num_q_heads} heads), fp64, repeated {reps} times in {spent:.1f} s",
-               "host_cpu": host_cpu()}
-        log(f"cpu baseline: {cpu['value']:.4g} queries/s on {threads} threads ({cpu['host_cpu']})")
-        if threads > 1:
-            # The same oracle on one core, over a bounded slice of the batch's rows.
-            rows_total = queries * x.num_q_heads
-            rng = np.random.default_rng(0)
-            n1, spent1, done1 = 64, 0.0, 0
-            while spent1 < args.cpu_seconds / 3 and done1 < rows_total:
-                rows = rng.integers(0, rows_total, n1).astype(np.int64)
-                c0 = time.perf_counter()
-                oracle.attention(prob, rows=rows, threads=1)
-                spent1 += time.perf_counter() - c0
-                done1 += n1
-            cpu["one_core"] = {"value": done1 / x.num_q_heads / spent1, "unit": "queries/s", "cores": 1,
-                               "sample": f"{done1} (query, head) rows drawn uniformly from the batch, fp64, "
-                                         f"{spent1:.1f} s; value = rows/s / Hq"}
-            log(f"cpu baseline, one core: {cpu['one_core']['value']:.4g} queries/s")
+            oracle.attention(prob, rows=rows, threads=1)
+            spent1 += time.perf_counter() - c0
+            done1 += n1
+        cpu["one_core"] = {"value": done1 / x.num_q_heads / spent1, "unit": "queries/s", "cores": 1,
+                           "sample": f"{done1} (query, head) rows drawn uniformly from the batch, fp64, "
+                                     f"{spent1:.1f} s; value = rows/s / Hq"}
+    return cpu
 
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "decode attention shards by sequence or KV head with no exchange, so a multi-GPU figure "
+              "would be N independent copies of this one.", file=sys.stderr)
+        return 2
+
+    if args.prefill:
+        return main_prefill(args)
+    if (args.ring or args.head_scales) and args.config == 0:
+        print("--ring and --head-scales apply to one workload: pass --config 2 (ring) or 4 (head scales)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_94_amd as pa
+
+    if not os.path.exists(pa.library_path()):
+        from paged_kv_cache_94_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(torch.device("cuda:0"))
+
+    order = CONFIG_ORDER if args.config == 0 else (args.config,)
+    head = order[0]
+    recs = {}
+    for idx in order:
+        cpu_s = 0.0 if args.no_cpu_baseline else (args.cpu_seconds if idx == head else args.cpu_seconds_others)
+        recs[idx] = run_decode(idx, args, cpu_seconds=cpu_s, one_core=idx == head, extras=idx == head)
+    h = recs[head]
+
+    roofline = {"bound": "hbm", "kernel": h["kernel"], "achieved": h["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": h["frac"], "traffic": h["traffic"], "traffic_source": h["traffic_source"]}
+    config = {"workload": h["workload"], "batch": h["batch"], "q_len": h["q_len"],
+              "alg_bytes_per_step": h["alg_bytes_per_step"], "kernel_us": h["kernel_us"],
+              "kernel_stamped_steps": h["kernel_stamped_steps"], "step_GBps": h["step_GBps"],
+              "cache_copies": h["cache_copies"], "plan": h["plan"]}
+    if len(order) > 1:
+        # Every workload of the set, timed in this same run (the headline's own entry included).
+        keep = ("workload", "dtype", "alg_bytes_per_step", "kernel", "kernel_us", "kernel_stamped_steps",
+                "achieved_GBps", "frac", "step_us", "step_GBps", "queries_per_s", "plan", "cache_copies", "traffic",
+                "traffic_source", "cpu_baseline")
+        config["configs"] = {f"C{i}": {k: recs[i][k] for k in keep if k in recs[i]} for i in sorted(recs)}
     rec = {
         "metric": METRIC,
-        "value": value,
+        "value": h["queries_per_s"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "int8": "int8 cache, bf16 q"}[x.kv_dtype],
+        "dtype": h["dtype"],
         "data": "synthetic",
-        "config": {
-            "workload": f"{x.name}: B={x.batch}, q_len={x.q_len}, Hq={x.num_q_heads}, Hkv={x.num_kv_heads}, "
-                        f"D={x.head_dim}, block=16, window={x.window}, lens {cfg['lens']} (seed {args.config})",
-            "batch": x.batch,
-            "q_len": x.q_len,
-            "alg_bytes_per_step": acct["alg_bytes"],
-            "kernel_us": {"mean": kern_s * 1e6, **pct},
-            "kernel_stamped_steps": len(kern_ms),
-            "step_GBps": step_gbs,
-            "cache_copies": copies,
-            "splits": plan["splits"],
-        },
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if (args.ring or args.head_scales) else measured_traffic(args.config, plan)},
-        "cpu_baseline": cpu,
-        "warm": warm,
-        "kv_append": app,
-        "block_allocator": alloc,
+        "config": config,
+        "roofline": roofline,
+        "cpu_baseline": h.get("cpu_baseline"),
+        "warm": h.get("warm"),
+        "kv_append": h.get("kv_append"),
+        "block_allocator": h.get("block_allocator"),
     }
     print(json.dumps(rec), flush=True)
     return 0
