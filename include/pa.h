@@ -206,6 +206,23 @@ int pa_decode_int8(const pa_args* args, pa_stream_t stream);
 int pa_verify(const pa_args* args, pa_stream_t stream);
 
 /*
+ * pa_verify without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc. Same arguments, kernels and results as pa_verify,
+ * except that args->workspace must be NULL and workspace_bytes 0: the split
+ * partials, prefix sums and piece queue go to a static device array of the
+ * library, 64 MiB per GPU, held from the first use on a GPU until the
+ * process ends. A call whose plan needs more (pa_workspace_size() >
+ * 67108864) returns PA_ERR_WORKSPACE and enqueues nothing. Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other host
+ * threads, other streams) race and must be ordered by the caller. The queue
+ * counters are cleared by a small kernel on `stream` before a call that
+ * uses them. The call itself allocates nothing; its first call on a device
+ * looks up the array's address there (hipGetSymbolAddress).
+ */
+int pa_verify_noalloc(const pa_args* args, pa_stream_t stream);
+
+/*
  * Debug: copy the raw cache rows that the attention kernels would load
  * (which = 0: keys, 1: values) into dst, [B][dst_tokens][Hkv][D] elements of
  * kv_dtype. Entry w of sequence b holds key first(b)+w, first(b) being the

@@ -33,7 +33,7 @@ from typing import Optional
 from . import _lib
 from ._lib import PaError  # noqa: F401
 
-__all__ = ["decode", "decode_int8", "verify", "prefill", "cache_write", "debug_gather", "validate", "plan",
+__all__ = ["decode", "decode_int8", "verify", "verify_noalloc", "prefill", "cache_write", "debug_gather", "validate", "plan",
            "workspace_size", "PaError", "library_path"]
 
 # Status bits of validate() (include/pa.h).
@@ -208,6 +208,25 @@ def decode_int8(out, q, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale,
 def verify(out, q, k_pool, v_pool, block_table, seq_lens, **kw):
     """q_len >= 1 query tokens per sequence, causal among themselves."""
     return _run("pa_verify", out, q, k_pool, v_pool, block_table, seq_lens, **kw)
+
+
+def verify_noalloc(out, q, k_pool, v_pool, block_table, seq_lens, *, window=0, scale=None, max_seq_len=None,
+                   k_scale=None, v_scale=None, num_splits=0, debug_visits=None, stream=None, timing=None,
+                   ring_blocks=0, tuning=None):
+    """pa_verify with the library's static scratch array as the workspace (pa_verify_noalloc).
+
+    Nothing is allocated on this path, here or in the library; calls that
+    overlap on one GPU share its scratch array and race.
+    """
+    lib = _lib.load()
+    a = _build_args(out, q, k_pool, v_pool, block_table, seq_lens, window=window, scale=scale,
+                    max_seq_len=max_seq_len, k_scale=k_scale, v_scale=v_scale, num_splits=num_splits,
+                    debug_visits=debug_visits, ring_blocks=ring_blocks, tuning=tuning)
+    if timing is not None:
+        a.timing_start = ctypes.c_void_p(getattr(timing[0], "cuda_event", timing[0]))
+        a.timing_stop = ctypes.c_void_p(getattr(timing[1], "cuda_event", timing[1]))
+    _lib.check(lib.pa_verify_noalloc(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+    return out
 
 
 def cache_write(k_new, v_new, slot_ids, k_pool, v_pool, k_scale=None, v_scale=None, *, stream=None,

@@ -19,7 +19,8 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_
 PA_PART_AUTO, PA_PART_ALIGNED, PA_PART_LIST, PA_PART_PIECES, PA_PART_QUEUE = 0, 1, 2, 3, 4
 
 EXPORTED = ("pa_workspace_size", "pa_plan", "pa_decode", "pa_decode_int8", "pa_verify", "pa_cache_write", "pa_prefill",
-            "pa_debug_gather", "pa_validate", "pa_strerror", "pa_last_error", "pa_version", "pa_build_id",
+            "pa_verify_noalloc", "pa_debug_gather", "pa_validate", "pa_strerror", "pa_last_error", "pa_version",
+            "pa_build_id",
             "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_add", "pa_alloc_add_ring", "pa_alloc_append",
             "pa_alloc_append_batch",
             "pa_alloc_release", "pa_alloc_num_free", "pa_alloc_block_table", "pa_alloc_stats",
@@ -185,7 +186,7 @@ def load(path: str = LIB_PATH):
         lib.pa_workspace_size.restype = ctypes.c_size_t
         lib.pa_plan.argtypes = [P, ctypes.POINTER(PaPlanInfo)]
         lib.pa_plan.restype = ctypes.c_int
-        for name in ("pa_decode", "pa_decode_int8", "pa_verify"):
+        for name in ("pa_decode", "pa_decode_int8", "pa_verify", "pa_verify_noalloc"):
             fn = getattr(lib, name)
             fn.argtypes = [P, ctypes.c_void_p]
             fn.restype = ctypes.c_int

@@ -309,14 +309,9 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   return p;
 }
 
-int run(const pa_args* a, pa_stream_t stream, Entry entry) {
-  pa::clear_error();
-  int rc = validate(a, entry);
-  if (rc) return rc;
-  Plan P;
-  rc = make_plan(a, &P);
-  if (rc) return rc;
-  if (a->num_seqs == 0) return PA_OK;
+// Enqueue the attention kernel (and the combine kernel when the plan splits)
+// for arguments already validated and planned; the workspace is checked.
+int launch_plan(const pa_args* a, const Plan& P, pa_stream_t stream) {
   if (P.ws_bytes) {
     if (!a->workspace || a->workspace_bytes < P.ws_bytes)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", P.ws_bytes,
@@ -346,6 +341,52 @@ int run(const pa_args* a, pa_stream_t stream, Entry entry) {
   return PA_OK;
 }
 
+int run(const pa_args* a, pa_stream_t stream, Entry entry) {
+  pa::clear_error();
+  int rc = validate(a, entry);
+  if (rc) return rc;
+  Plan P;
+  rc = make_plan(a, &P);
+  if (rc) return rc;
+  if (a->num_seqs == 0) return PA_OK;
+  return launch_plan(a, P, stream);
+}
+
+}  // namespace
+
+// ---- pa_verify_noalloc: the workspace in a static device array ----------------
+//
+// For callers that cannot allocate device memory (HIP graph capture, serving
+// loops that forbid it). The split partials, prefix sums and piece queue live
+// in `scratch`, one copy per GPU, zero when the library's code object is
+// loaded and kept until the process ends. On the host this name only stands
+// for the symbol: host code never hands it to a kernel or a copy, and uses
+// instead the device address hipGetSymbolAddress returns for the current
+// device (looked up once per device, then cached).
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d is past the library's table", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -382,6 +423,38 @@ int pa_plan(const pa_args* a, pa_plan_info* info) {
 int pa_decode(const pa_args* a, pa_stream_t stream) { return run(a, stream, kDecode); }
 int pa_decode_int8(const pa_args* a, pa_stream_t stream) { return run(a, stream, kDecodeInt8); }
 int pa_verify(const pa_args* a, pa_stream_t stream) { return run(a, stream, kVerify); }
+
+int pa_verify_noalloc(const pa_args* a, pa_stream_t stream) {
+  pa::clear_error();
+  int rc = validate(a, kVerify);
+  if (rc) return rc;
+  if (a->workspace || a->workspace_bytes)
+    return fail(PA_ERR_INVALID_ARG, "pa_verify_noalloc uses the library's scratch array: pass no workspace");
+  Plan P;
+  rc = make_plan(a, &P);
+  if (rc) return rc;
+  if (a->num_seqs == 0) return PA_OK;
+  if (P.ws_bytes > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the library's array holds %zu "
+                "(use pa_verify with a workspace)", P.ws_bytes, kScratchBytes);
+  pa_args b = *a;
+  if (P.ws_bytes) {
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    b.workspace = ws;
+    b.workspace_bytes = kScratchBytes;
+    if (P.queue) {
+      // The piece queue's counters must start at zero; a previous call on
+      // this GPU leaves them so, but they are cleared here by a small kernel
+      // on the call's own stream (no memset node if the call is captured).
+      const hipError_t e = pa::launch_zero_words(reinterpret_cast<int32_t*>(ws), (int32_t)(kWsHeader / 4),
+                                                 reinterpret_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return fail(PA_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+    }
+  }
+  return launch_plan(&b, P, stream);
+}
 
 int pa_debug_gather(const pa_args* a, int32_t which, void* dst, int64_t dst_tokens, pa_stream_t stream) {
   pa::clear_error();

@@ -293,6 +293,16 @@ hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(256) pa_zero_words_kernel(int32_t* p, int32_t n) {
+  for (int32_t i = threadIdx.x; i < n; i += 256) p[i] = 0;
+}
+
+hipError_t launch_zero_words(int32_t* p, int32_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pa_zero_words_kernel, dim3(1), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const Params& p, int kv_dtype, int D, int which, void* dst, int64_t dst_tokens,
                          hipStream_t st) {
   const int32_t eb = kv_dtype == 0 ? 4 : (kv_dtype == 1 ? 2 : 1);

@@ -112,4 +112,6 @@ hipError_t launch_validate(const Params& p, int32_t num_blocks, int32_t max_seq_
                            const int32_t* queue_header, int32_t* status, hipStream_t st);
 hipError_t launch_gather(const Params& p, int kv_dtype, int D, int which, void* dst, int64_t dst_tokens,
                          hipStream_t st);
+// Zero n int32 words at p with a small kernel (one workgroup; vector stores).
+hipError_t launch_zero_words(int32_t* p, int32_t n, hipStream_t st);
 }  // namespace pa

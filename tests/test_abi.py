@@ -375,3 +375,20 @@ def test_build_id_matches_sources_and_stale_copies_are_refused(lib, tmp_path):
         f.write("\n// edited\n")
     with pytest.raises(RuntimeError, match="built from other sources"):
         _lib.check_build_id(lib, root=str(tmp_path))
+
+
+def test_noalloc_entry_rules(lib):
+    # pa_verify_noalloc takes no workspace, and refuses plans larger than its 64 MiB scratch
+    # array before touching the device.
+    many = dict(num_seqs=300, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128, window=0, max_seq_len=3000,
+                max_blocks_per_seq=188)
+    a = _args(**many, workspace=64, workspace_bytes=1 << 20)
+    assert lib.pa_verify_noalloc(ctypes.byref(a), None) == _lib.PA_ERR_INVALID_ARG
+    b = _tuned(_args(**many), partition=_lib.PA_PART_QUEUE, pieces_per_wg=64)
+    assert lib.pa_workspace_size(ctypes.byref(b)) > 64 << 20
+    assert lib.pa_verify_noalloc(ctypes.byref(b), None) == _lib.PA_ERR_WORKSPACE
+    assert b"67108864" in lib.pa_last_error()
+    c = _args(**dict(many, q_len=0))
+    assert lib.pa_verify_noalloc(ctypes.byref(c), None) == _lib.PA_ERR_INVALID_ARG
+    d = _args(**dict(many, num_seqs=0), out=0, q=0, k_pool=0, v_pool=0, block_table=0, seq_lens=0)
+    assert lib.pa_verify_noalloc(ctypes.byref(d), None) == _lib.PA_OK
