@@ -126,6 +126,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated across steps (0: enough to exceed 4x the Infinity Cache)")
     ap.add_argument("--num-splits", type=int, default=0, help="force the context split count (0: library plan)")
+    ap.add_argument("--tuning", default="",
+                    help="launch-plan overrides (pa_tuning fields), e.g. partition=queue,pieces_per_wg=8; the record "
+                         "notes them (experiments only: the library's own plan is the default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the headline's oracle baseline")
     ap.add_argument("--cpu-seconds-others", type=float, default=3.0,
                     help="budget for the oracle baseline of each other workload")
@@ -140,6 +143,13 @@ def parse():
                     help="decode: stamp the attention kernel's dispatch with a HIP event pair on every Nth timed "
                          "step (0: every max(1, steps // 16)-th, so at least 10 samples from 10 steps on; a pair "
                          "on every step adds GPU and host time to each step)")
+    ap.add_argument("--stamps", action="store_true",
+                    help="load libpa_stamps.so (the same sources built with PA_STAMPS) and, after the timed steps, "
+                         "record one launch's per-workgroup phase timestamps for each matrix-core workload")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="after each workload's timed steps, stream its cache tiles with the load-only probe "
+                         "(libpa_probe.so) on the same cache copies: the read rate this part gives that access "
+                         "pattern, the kernel's practical ceiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy 3x (a known-size kernel for counter scaling)")
     return ap.parse_args()
@@ -485,9 +495,10 @@ def run_decode(idx: int, args, *, cpu_seconds: float, one_core: bool, extras: bo
             table = table0.clone()
         calls.append(pa.Prepared(entry, out, q, k, v, table, lens, window=x.window, scale=x.scale,
                                  max_seq_len=x.max_seq_len, k_scale=ks, v_scale=vs, num_splits=args.num_splits,
-                                 ring_blocks=x.ring_blocks))
+                                 ring_blocks=x.ring_blocks, tuning=tuning_of(args, x)))
     plan = pa.plan(q, k0, v0, table0, lens, window=x.window, scale=x.scale, max_seq_len=x.max_seq_len,
-                   k_scale=ks0, v_scale=vs0, num_splits=args.num_splits, ring_blocks=x.ring_blocks)
+                   k_scale=ks0, v_scale=vs0, num_splits=args.num_splits, ring_blocks=x.ring_blocks,
+                   tuning=tuning_of(args, x))
     log(f"[{idx}] plan: {plan}; {copies} cache copies rotated")
 
     # The timed steps run back to back; every `every`-th one also carries a
@@ -510,7 +521,10 @@ def run_decode(idx: int, args, *, cpu_seconds: float, one_core: bool, extras: bo
         f"{achieved / HBM_PEAK_GBS * 100:.1f}% of peak; whole step {step_s * 1e6:.2f} us -> {step_gbs:.0f} GB/s, "
         f"{value:.4g} queries/s")
 
-    traffic = None if (args.ring or args.head_scales or args.num_splits) else measured_traffic(idx, plan)
+    traffic = None if (args.ring or args.head_scales or args.num_splits or args.stamps) else \
+        measured_traffic(idx, plan)
+    stamps = phase_stamps(torch, calls[0], plan, kern_s, acct["alg_bytes"]) if args.stamps and plan["kernel"] == 1 \
+        else None
     rec = {
         "workload": f"{x.name}: B={x.batch}, q_len={x.q_len}, Hq={x.num_q_heads}, Hkv={x.num_kv_heads}, "
                     f"D={x.head_dim}, block=16, window={x.window}, kv={x.kv_dtype}, lens {cfg['lens']} "
@@ -531,11 +545,22 @@ def run_decode(idx: int, args, *, cpu_seconds: float, one_core: bool, extras: bo
         "ms_per_step": step_s * 1e3,
         "plan": {k: plan[k] for k in ("kernel", "rows", "waves_per_group", "splits", "grid", "balanced", "pieces",
                                       "queue")},
+        "tuning": tuning_of(args, x),
         "cache_copies": copies,
         "traffic": traffic,
         "traffic_source": (MEASURED_TRAFFIC[idx]["source"] if traffic is not None else
                            "null: no counter pass matches these kernel sources and this plan"),
     }
+    if stamps is not None:
+        rec["stamps"] = stamps
+        log_stamps(idx, stamps)
+    if args.ceiling:
+        rec["ceiling"] = read_ceiling(torch, np, x, calls, args.steps, kern_s)
+        c = rec["ceiling"]
+        log(f"[{idx}] read ceiling: {c['kv_bytes'] / 1e6:.1f} MB of cache tiles; " +
+            "; ".join(f"{r['workgroups']}x{r['waves']}w depth {r['depth']}: {r['us']:.2f} us = {r['TBps']:.2f} TB/s"
+                      for r in c["runs"]) +
+            f"; the attention kernel reads them at {c['kernel_TBps']:.2f} TB/s = {c['kernel_share']:.1%} of the best")
 
     if extras:
         # Warm: every step re-reads the same cache copy, so the Infinity Cache
@@ -574,6 +599,168 @@ def run_decode(idx: int, args, *, cpu_seconds: float, one_core: bool, extras: bo
         log(f"[{idx}] cpu baseline: {rec['cpu_baseline']['value']:.4g} queries/s on "
             f"{rec['cpu_baseline']['cores']} threads")
     return rec
+
+
+STAMP_TICKS_PER_US = 100.0   # s_memrealtime counts at 100 MHz on MI300-class parts (checked against events below)
+
+
+def phase_stamps(torch, call, plan: dict, kern_s: float, alg_bytes: int) -> dict:
+    """One launch with the phase stamps of libpa_stamps.so on; per-workgroup phase statistics in us.
+
+    Slots per workgroup (include/pa.h, pa_args.debug_stamps): 0 entry, 1 partition known, 2 exit,
+    3 segment count, then per segment s at 4 + 5s: start, first block consumed, block loop done,
+    result written, block count. Times are from the earliest workgroup entry. stream_TBps: the
+    algorithmic bytes spread over each segment's [start, block loop done] in proportion to its
+    blocks, summed over workgroups in 5 us bins -- the rate at which the kernel pulls its data.
+    """
+    import numpy as np
+    slots = 64
+    buf = torch.zeros(plan["grid"] * slots, dtype=torch.int64, device="cuda")
+    call.args.debug_stamps = buf.data_ptr()
+    ev = event_pair(torch)
+    for a in ev:
+        a.record()
+    for _ in range(2):
+        buf.zero_()
+        call.launch(timing=ev)
+    torch.cuda.synchronize()
+    call.args.debug_stamps = None
+    st = buf.view(plan["grid"], slots).cpu().numpy().astype(np.int64)
+    kern_us = ev[0].elapsed_time(ev[1]) * 1e3
+    t0 = st[:, 0].min()
+    us = (st - t0) / STAMP_TICKS_PER_US
+    per_seg = 5
+    nseg = np.minimum(st[:, 3], (slots - 4) // per_seg)
+    starts, streams, merges, gaps, firsts, spans = [], [], [], [], [], []
+    for w in range(st.shape[0]):
+        n = int(nseg[w])
+        raw = st[w, 4:4 + per_seg * n].reshape(n, per_seg) if n else np.zeros((0, per_seg), dtype=np.int64)
+        seg = us[w, 4:4 + per_seg * n].reshape(n, per_seg) if n else np.zeros((0, per_seg))
+        for k in range(n):
+            spans.append((seg[k, 0], seg[k, 2], int(raw[k, 4])))
+        starts.append(float((seg[:, 1] - seg[:, 0]).sum()))
+        streams.append(float((seg[:, 2] - seg[:, 1]).sum()))
+        merges.append(float((seg[:, 3] - seg[:, 2]).sum()))
+        gaps.append(float((seg[1:, 0] - seg[:-1, 3]).sum()) if n > 1 else 0.0)
+        if n:
+            firsts.append(float(seg[0, 1]))
+
+    def q(v):
+        v = np.sort(np.asarray(v, dtype=np.float64))
+        if v.size == 0:
+            return None
+        return {"p10": float(v[int(0.1 * (v.size - 1))]), "p50": float(v[int(0.5 * (v.size - 1))]),
+                "p90": float(v[int(0.9 * (v.size - 1))]), "max": float(v[-1])}
+
+    span_us = float(us[:, 2].max())
+    # Streaming rate over time: each segment's share of the bytes, spread over [start, loop done].
+    total_blocks = sum(b for _, _, b in spans) or 1
+    bin_us = 5.0
+    bins = np.zeros(int(span_us // bin_us) + 2)
+    for t0s, t1s, blocks in spans:
+        nbytes = alg_bytes * blocks / total_blocks
+        a, b = max(0.0, t0s), max(t0s + 1e-3, t1s)
+        i0, i1 = int(a // bin_us), int(b // bin_us)
+        for i in range(i0, i1 + 1):
+            lo, hi = max(a, i * bin_us), min(b, (i + 1) * bin_us)
+            if hi > lo:
+                bins[i] += nbytes * (hi - lo) / (b - a)
+    rate = [round(float(x) / (bin_us * 1e-6) / 1e12, 2) for x in bins]
+    return {
+        "what": "one launch of libpa_stamps.so (same sources, PA_STAMPS); us from the first workgroup entry",
+        "kernel_us_events": kern_us, "span_us_stamps": span_us,
+        "stamp_rate_check": span_us / kern_us if kern_us > 0 else None,
+        "workgroups": int(st.shape[0]), "segments_per_wg": q(nseg),
+        "entry": q(us[:, 0]), "partition_known": q(us[:, 1]), "first_block_consumed": q(firsts), "exit": q(us[:, 2]),
+        "sum_segment_starts": q(starts), "sum_streaming": q(streams), "sum_merges_and_writes": q(merges),
+        "sum_between_segments": q(gaps),
+        "stream_TBps_per_5us": rate,
+    }
+
+
+def log_stamps(idx: int, s: dict) -> None:
+    log(f"[{idx}] phase stamps ({s['workgroups']} workgroups; kernel {s['kernel_us_events']:.1f} us by events, "
+        f"{s['span_us_stamps']:.1f} us by stamps), us from the first entry: p10 / p50 / p90 / max")
+    for key in ("segments_per_wg", "entry", "partition_known", "first_block_consumed", "exit", "sum_segment_starts",
+                "sum_streaming", "sum_merges_and_writes", "sum_between_segments"):
+        v = s[key]
+        if v is not None:
+            log(f"[{idx}]   {key:24s} {v['p10']:8.2f} {v['p50']:8.2f} {v['p90']:8.2f} {v['max']:8.2f}")
+    log(f"[{idx}]   streaming TB/s per 5 us: {' '.join(f'{x:.1f}' for x in s['stream_TBps_per_5us'])}")
+
+
+def tuning_of(args, x):
+    """The --tuning overrides as a dict (None without any); they apply to the matrix-core workloads only."""
+    if not args.tuning:
+        return None
+    mfma = x.kv_dtype == "int8" or (x.kv_dtype == "bf16" and x.num_q_heads // x.num_kv_heads * x.q_len > 512 // x.head_dim)
+    if not mfma:
+        return None
+    out = {}
+    for item in args.tuning.split(","):
+        k, v = item.split("=")
+        out[k.strip()] = v.strip() if k.strip() == "partition" else int(v)
+    return out
+
+
+def tile_list(np, x):
+    """The (block, KV head) tiles one step reads, as ids phys * Hkv + g, in (sequence, KV head, block) order."""
+    ids = []
+    R = x.ring_blocks
+    for b in range(x.batch):
+        L = int(x.seq_lens[b])
+        lo = max(0, L - x.q_len - x.window + 1) if x.window > 0 else 0
+        blocks = np.arange(lo // 16, (L - 1) // 16 + 1)
+        phys = x.block_table[b, (blocks % R) if R else blocks].astype(np.int64)
+        for g in range(x.num_kv_heads):
+            ids.append(phys * x.num_kv_heads + g)
+    return np.concatenate(ids).astype(np.int32) if ids else np.zeros(0, dtype=np.int32)
+
+
+def read_ceiling(torch, np, x, calls, steps: int, kern_s: float) -> dict:
+    """Stream the step's cache tiles with the load-only probe (libpa_probe.so), rotating over the cache copies."""
+    import ctypes
+    from paged_kv_cache_94_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build(variants=("probe",))
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    V, I32 = ctypes.c_void_p, ctypes.c_int32
+    lib.pa_probe_read.argtypes = [V, V, V, I32, I32, I32, I32, I32, I32, V, V, V, V]
+    lib.pa_probe_read.restype = ctypes.c_int
+    tiles_h = tile_list(np, x)
+    tiles = torch.from_numpy(tiles_h).to("cuda")
+    elem = {"f32": 4, "bf16": 2, "int8": 1}[x.kv_dtype]
+    row_bytes = x.head_dim * elem
+    two = not x.v_aliases_k
+    kv_bytes = int(tiles_h.size) * 16 * row_bytes * (2 if two else 1)
+    pools = [(c._keep[2], c._keep[3]) for c in calls]
+    runs = []
+    for wgs, waves, depth in ((512, 4, 2), (256, 8, 2), (512, 4, 3)):
+        sink = torch.empty(wgs * waves * 64, dtype=torch.int32, device="cuda")
+        n = max(8, min(steps, 40))
+        evs = [event_pair(torch) for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream().cuda_stream
+        for i in range(-2, n):   # two untimed warm-up launches
+            k, v = pools[i % len(pools)]
+            ev = evs[i] if i >= 0 else (None, None)
+            rc = lib.pa_probe_read(k.data_ptr(), v.data_ptr() if two else None, tiles.data_ptr(), int(tiles_h.size),
+                                   row_bytes, x.num_kv_heads, wgs, waves, depth, sink.data_ptr(),
+                                   ev[0].cuda_event if ev[0] else None, ev[1].cuda_event if ev[1] else None, stream)
+            if rc != 0:
+                raise RuntimeError(f"pa_probe_read failed ({rc})")
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+        runs.append({"workgroups": wgs, "waves": waves, "depth": depth, "us": us, "TBps": kv_bytes / us / 1e6})
+    best = max(r["TBps"] for r in runs)
+    kernel_tbps = kv_bytes / kern_s / 1e12
+    return {"what": "load-only probe over the same cache tiles and copies: each cached row read front to back in "
+                    "16-byte non-temporal pieces, as the matrix-core kernel loads them; KV bytes only",
+            "kv_bytes": kv_bytes, "tiles": int(tiles_h.size), "runs": runs, "best_TBps": best,
+            "kernel_TBps": kernel_tbps, "kernel_share": kernel_tbps / best}
 
 
 def cpu_baseline(np, x, queries: int, *, cpu_seconds: float, one_core: bool) -> dict:
@@ -629,9 +816,14 @@ def main() -> int:
     import torch
 
     import paged_kv_cache_94_amd as pa
+    from paged_kv_cache_94_amd import _lib, build
 
-    if not os.path.exists(pa.library_path()):
-        from paged_kv_cache_94_amd import build
+    if args.stamps:
+        if not os.path.exists(build.STAMPS_LIB):
+            build.build(variants=("stamps",))
+        _lib.load(build.STAMPS_LIB)   # every call of this process goes to the stamps build
+        log(f"loaded {build.STAMPS_LIB}")
+    elif not os.path.exists(pa.library_path()):
         build.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(torch.device("cuda:0"))
@@ -676,6 +868,11 @@ def main() -> int:
         "kv_append": h.get("kv_append"),
         "block_allocator": h.get("block_allocator"),
     }
+    if args.ceiling:
+        rec["ceiling"] = {f"C{i}": recs[i]["ceiling"] for i in sorted(recs) if "ceiling" in recs[i]}
+    if args.stamps:
+        rec["stamps"] = {f"C{i}": recs[i]["stamps"] for i in sorted(recs) if "stamps" in recs[i]}
+        rec["library"] = "libpa_stamps.so (diagnostic build with phase stamps)"
     print(json.dumps(rec), flush=True)
     return 0
 

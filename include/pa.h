@@ -149,6 +149,12 @@ typedef struct {
                                  notes, "Quantization": per_head granularity, a smaller scale table) */
   const pa_tuning* tuning;    /* NULL: the library's launch plan; else explicit overrides (host memory,
                                  read during the call only) */
+  void* debug_stamps;         /* NULL, or (a library built with -DPA_STAMPS, libpa_stamps.so) a device
+                                 buffer of grid x 64 uint64 that the matrix-core kernel fills with the
+                                 real-time counter at each workgroup's phases (slot 0 entry, 1 partition
+                                 known, 2 exit, 3 segment count, then per segment s at 4 + 4s: start,
+                                 first block consumed, block loop done, result written). The release
+                                 library never writes it. */
 } pa_args;
 
 /* Plan the library would use for these arguments (informational). */

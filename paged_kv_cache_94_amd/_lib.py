@@ -69,6 +69,7 @@ class PaArgs(ctypes.Structure):
         ("ring_blocks", ctypes.c_int32),
         ("scale_per_head", ctypes.c_int32),
         ("tuning", ctypes.c_void_p),
+        ("debug_stamps", ctypes.c_void_p),
     ]
 
 

@@ -57,8 +57,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpa.so)")
 
 
-def _compile(src: str, extra: list) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+# Libraries: the release library; a diagnostic copy of the same sources
+# compiled with PA_STAMPS, whose matrix-core kernel records per-workgroup
+# phase timestamps into pa_args.debug_stamps (bench.py --stamps); and the
+# read-ceiling probe, a load-only kernel over a workload's cache tiles
+# (bench.py --ceiling).
+VARIANTS = {
+    "release": {"lib": LIB, "objdir": BUILD, "flags": [], "sources": SOURCES},
+    "stamps": {"lib": os.path.join(PKG, "libpa_stamps.so"), "objdir": os.path.join(PKG, "_build_stamps"),
+               "flags": ["-DPA_STAMPS"], "sources": SOURCES},
+    "probe": {"lib": os.path.join(PKG, "libpa_probe.so"), "objdir": os.path.join(PKG, "_build_probe"),
+              "flags": [], "sources": ["pa_probe.hip"]},
+}
+STAMPS_LIB = VARIANTS["stamps"]["lib"]
+PROBE_LIB = VARIANTS["probe"]["lib"]
+ALL_VARIANTS = ("release", "stamps", "probe")
+
+
+def _compile(src: str, extra: list, objdir: str) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [hipcc()] + COMMON + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,23 +84,33 @@ def _compile(src: str, extra: list) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags: list | None = None) -> str:
-    """Compile every source and link libpa.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags: list | None = None, variants=("release",)) -> str:
+    """Compile every source and link each requested variant; returns the release library's path."""
     extra = list(extra_flags or []) + [f'-DPA_BUILD_ID="{source_hash()}"']
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"linking libpa.so failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    jobs = [(v, src) for v in variants for src in VARIANTS[v]["sources"]]
+    for v in variants:
+        os.makedirs(VARIANTS[v]["objdir"], exist_ok=True)
+    workers = min(len(jobs), max(1, min(16, os.cpu_count() or 1)))
+    # The matrix-core kernels take longest: start them first.
+    jobs.sort(key=lambda j: j[1] != "pa_mfma.hip")
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda j: (j[0], _compile(j[1], extra + VARIANTS[j[0]]["flags"], VARIANTS[j[0]]["objdir"])),
+                           jobs))
+    for v in variants:
+        target = VARIANTS[v]["lib"]
+        tmp = target + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for vv, o in objs if vv == v]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"linking {os.path.basename(target)} failed:\n{res.stdout}\n{res.stderr}")
+        os.replace(tmp, target)
+        if verbose:
+            print(f"built {target}")
     return LIB
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra_flags=sys.argv[1:])
+    # python -m paged_kv_cache_94_amd.build [--all] [extra hipcc flags...]
+    argv = sys.argv[1:]
+    variants = ALL_VARIANTS if "--all" in argv else ("release",)
+    build(verbose=True, extra_flags=[a for a in argv if a != "--all"], variants=variants)

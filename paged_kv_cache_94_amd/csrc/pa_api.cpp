@@ -205,7 +205,7 @@ int make_plan(const pa_args* a, Plan* pl) {
     // 4 waves and leaves half the partials to merge (16 sequences of 4K-32K
     // tokens on one KV head: kernel 29.4 vs 29.2 us, step 34.9 vs 37.0 us).
     if (!nw_forced && 2 * units <= (int64_t)cu_count()) P.nw = 8;
-    P.nwg = cu_count() * (8 / P.nw);
+    P.nwg = cu_count() * (8 / P.nw);   // as many workgroups as are resident at once (2 wavefronts per SIMD)
     if (tu.oversub > 0) P.nwg *= tu.oversub;
     // Measured on MI355X: one piece per workgroup is best for few units
     // (<= nwg/2: 16 long contexts on one KV head), the flattened list for
@@ -293,6 +293,7 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   p.balanced = P.balanced;
   p.nwg = P.nwg;
   p.visits = a->debug_visits;
+  p.stamps = reinterpret_cast<uint64_t*>(a->debug_stamps);
   p.B = a->num_seqs;
   p.q_len = a->q_len;
   p.Hq = a->num_q_heads;

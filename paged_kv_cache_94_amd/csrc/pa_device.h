@@ -44,7 +44,43 @@ struct Params {
   int32_t* ws_queue;    // mode 2, non-null: hand pieces out through this [2] counter pair (zero between calls)
   int32_t ring;         // > 0: each table row is a ring of this many entries (logical block i -> i mod ring)
   int32_t head_scales;  // int8: 1 -> k_scale / v_scale hold one scale per KV head
+  uint64_t* stamps;     // builds with PA_STAMPS only: [grid][kStampSlots] phase timestamps, or null
 };
+
+// ---- phase stamps (a diagnostic build compiled with -DPA_STAMPS) ------------
+//
+// Thread 0 of a workgroup records the constant-rate real-time counter
+// (s_memrealtime) at the phases of its work: slot 0 entry, 1 partition
+// known, 2 exit, 3 the number of segments, then five per segment s (from
+// slot 4 + 5s): segment start, first block consumed, block loop done,
+// output or partial written, and the segment's block count (a count, not a
+// time). The release build compiles all of it away.
+constexpr int kStampSlots = 64;
+constexpr int kStampPerSeg = 5;
+constexpr int kStampSegments = (kStampSlots - 4) / kStampPerSeg;
+enum { kStampEntry = 0, kStampPartition = 1, kStampExit = 2, kStampCount = 3, kStampSeg0 = 4 };
+
+template <typename P>
+__device__ __forceinline__ void stamp(const P& p, int slot) {
+#ifdef PA_STAMPS
+  if (p.stamps && threadIdx.x == 0 && slot < kStampSlots)
+    p.stamps[(size_t)blockIdx.x * kStampSlots + slot] = __builtin_amdgcn_s_memrealtime();
+#else
+  (void)p;
+  (void)slot;
+#endif
+}
+
+template <typename P>
+__device__ __forceinline__ void stamp_value(const P& p, int slot, uint64_t v) {
+#ifdef PA_STAMPS
+  if (p.stamps && threadIdx.x == 0 && slot < kStampSlots) p.stamps[(size_t)blockIdx.x * kStampSlots + slot] = v;
+#else
+  (void)p;
+  (void)slot;
+  (void)v;
+#endif
+}
 
 // Table entry that holds logical block i (Lab 5 handout, "Ring KV Cache": in
 // a ring of R blocks position t lives in slot t mod 16R, i.e. block i mod R).

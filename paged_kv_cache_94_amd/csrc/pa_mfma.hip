@@ -97,7 +97,10 @@ __device__ __forceinline__ int32_t chunk_table(const Params& p, int32_t b, int32
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
 __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t first,
                                              int32_t last, int64_t slot, int32_t tbl0, int32_t& pf,
-                                             int32_t& pf_claim, int32_t* claim_lds) {
+                                             int32_t& pf_claim, int32_t* claim_lds, int32_t& seg) {
+  const int stamp_base = kStampSeg0 + kStampPerSeg * (seg < kStampSegments ? seg : kStampSegments);
+  stamp(p, stamp_base);
+  stamp_value(p, stamp_base + 4, (uint64_t)(last - first + 1));
   using Lds = MfmaLds<D, MT, NW, ALIAS>;
   constexpr int ROWS = Lds::ROWS;
   constexpr int C = D / 32;                           // contraction chunks of 32 dims
@@ -244,12 +247,13 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     }
   };
 
-  auto consume = [&](int32_t k, const Fetched& f) __attribute__((always_inline)) {
+  // Stage block k of this wavefront in LDS as bf16 (waits for its loads). A
+  // V row nobody may see can hold anything and is written as zeros (only
+  // edge blocks have such rows); a K row's score is masked by select, so its
+  // contents do not matter. The registers that held the block are free
+  // afterwards.
+  auto stage_block = [&](int32_t k, const Fetched& f) __attribute__((always_inline)) {
     const int32_t i = cfirst + wave + NW * k;   // logical block
-
-    // Stage the block in LDS as bf16. A V row nobody may see can hold
-    // anything and is written as zeros (only edge blocks have such rows); a K
-    // row's score is masked by select, so its contents do not matter.
     const bool edge = i * kBlock < kr.lo0 || i * kBlock + kBlock > L;
     __builtin_amdgcn_wave_barrier();   // the previous block's reads stay before these writes
 #pragma unroll
@@ -271,6 +275,11 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       if (lane < 32) sst[lane] = lane < 16 ? f.ks : f.vs;
     }
     __builtin_amdgcn_wave_barrier();   // these writes stay before this block's reads
+  };
+
+  // Attention over staged block k: scores, online softmax, P.V.
+  auto compute = [&](int32_t k) __attribute__((always_inline)) {
+    const int32_t i = cfirst + wave + NW * k;   // logical block
 
     // K operand chunks: token n, dims 32c + 8*q4 .. +7.
     bf16x8 kop[C];
@@ -350,10 +359,12 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   };
 
   // Software pipeline: DEPTH blocks in flight per wavefront; block k+DEPTH-1
-  // is requested before block k is consumed. The fetches are unconditional
-  // (past the end they load zero bytes), so every path into the loop head
-  // has the same loads outstanding and the compiler waits only for the
-  // block it consumes.
+  // is requested before block k is staged and computed. The fetches are
+  // unconditional (past the end they load zero bytes), so every path into
+  // the loop head has the same loads outstanding and the compiler waits only
+  // for the block it consumes. (Staging block k first and refilling its
+  // buffer with block k+DEPTH before the computation measured slower on the
+  // global layer and no faster elsewhere.)
   constexpr int FETCH_WORDS = NLOAD * 4 * (ALIAS ? 1 : 2) + (INT8 ? 2 : 0);
   constexpr int DEPTH = mfma_depth(FETCH_WORDS);
   // Blocks come in chunks of at most 64 per wavefront (one table entry per
@@ -389,7 +400,11 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
           fetch(k + d + DEPTH - 1, f[(d + DEPTH - 1) % DEPTH]);
-          consume(k + d, f[d]);
+          stage_block(k + d, f[d]);
+          compute(k + d);
+#ifdef PA_STAMPS
+          if (k + d == 0 && cfirst == first) stamp(p, stamp_base + 1);
+#endif
           if (k + d + 1 >= nmine) goto drained;
           __builtin_amdgcn_sched_barrier(0);   // refill a buffer only once it is consumed
         }
@@ -405,6 +420,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 #pragma unroll
     for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
   }
+  stamp(p, stamp_base + 2);
   pf = settle(pf);
   pf_claim = settle(pf_claim);
   if (claim_lds && threadIdx.x == 0) *claim_lds = pf_claim;   // read by all after the merge's barriers
@@ -502,6 +518,8 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       }
     }
   }
+  stamp(p, stamp_base + 3);
+  ++seg;
 }
 
 
@@ -512,6 +530,12 @@ template <bool INT8, bool ALIAS, int D, int MT, int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 pa_mfma_kernel(const Params p) {
   __shared__ __attribute__((aligned(16))) char smem[MfmaLds<D, MT, NW, ALIAS>::BYTES];
+  int32_t seg = 0;   // segments this workgroup has run (phase stamps only)
+  stamp(p, kStampEntry);
+  auto done = [&]() __attribute__((always_inline)) {
+    stamp_value(p, kStampCount, (uint64_t)seg);
+    stamp(p, kStampExit);
+  };
   if constexpr (MODE == 0) {
     // Aligned splits: workgroup (split, b, g) takes blocks [blk_lo + split*bps, ...] of sequence b.
     const int32_t g = blockIdx.x % p.Hkv;
@@ -519,16 +543,17 @@ pa_mfma_kernel(const Params p) {
     const int32_t b = bsplit % p.B;
     const int32_t split = bsplit / p.B;
     const int32_t L = p.seq_lens[b];
-    if (!len_ok(L, p)) return;   // broken precondition: touch nothing outside the arrays
+    if (!len_ok(L, p)) return done();   // broken precondition: touch nothing outside the arrays
     const KeyRange kr = key_range(L, p.q_len, p.window);
     const int32_t first = kr.blk_lo + split * p.bps;
-    if (first > kr.blk_hi) return;
+    if (first > kr.blk_hi) return done();
     const int32_t last = min(kr.blk_hi, first + p.bps - 1);
     const int64_t slot = p.splits > 1 ? (int64_t)(b * p.Hkv + g) * p.splits + split : -1;
+    stamp(p, kStampPartition);
     int32_t none = 0, none_c = 0;
     mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, first, last, slot, chunk_table<NW>(p, b, first, last), none,
-                                         none_c, nullptr);
-    return;
+                                         none_c, nullptr, seg);
+    return done();
   }
   __shared__ int32_t pre[balanced_seq_limit(NW) + 1];
   if constexpr (MODE == 2) {
@@ -548,6 +573,7 @@ pa_mfma_kernel(const Params p) {
       claims[1] = atomicAdd(qnext, 1);
     }
     __syncthreads();
+    stamp(p, kStampPartition);
     if (blockIdx.x == 0 && p.ws_prefix)
       for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
     const int32_t npieces = pre[p.B];
@@ -568,12 +594,12 @@ pa_mfma_kernel(const Params p) {
     if (!p.ws_queue) {
       // Static: workgroup w owns piece w.
       const int32_t w = blockIdx.x;
-      if (w >= npieces) return;
+      if (w >= npieces) return done();
       const Run r = run_of(w);
       int32_t none = 0, none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot,
-                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr);
-      return;
+                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr, seg);
+      return done();
     }
     // Queue: claims only grow, so a workgroup's pieces come in increasing
     // order. While piece w streams, the next piece's table entries load and
@@ -599,7 +625,7 @@ pa_mfma_kernel(const Params p) {
       }
       if (threadIdx.x == 0) claim = atomicAdd(qnext, 1);
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot, tbl0, tbln, claim,
-                                           &claims[0]);
+                                           &claims[0], seg);
       w = w1;
       w1 = piece_of_claim(claims[0]);
       tbl0 = tbln;
@@ -611,7 +637,7 @@ pa_mfma_kernel(const Params p) {
       atomicExch(qnext, 0);
       atomicExch(qdone, 0);
     }
-    return;
+    return done();
   }
   if constexpr (MODE == 1) {
     // Flattened-list partition: this workgroup's slice of the flattened (unit, block)
@@ -625,12 +651,13 @@ pa_mfma_kernel(const Params p) {
     __shared__ int32_t blo[balanced_seq_limit(NW)];
     block_prefix(p, pre, blo);
     __syncthreads();
+    stamp(p, kStampPartition);
     if (blockIdx.x == 0 && p.ws_prefix)
       for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
     const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
     const int64_t x0 = (int64_t)blockIdx.x * bal.per;
     const int64_t hi = min(bal.total, x0 + bal.per);
-    if (x0 >= hi) return;
+    if (x0 >= hi) return done();
     // The segment starting at item x: unit (b, g), its first item `off`, and
     // the logical blocks [first, last] it covers.
     struct Seg {
@@ -664,12 +691,13 @@ pa_mfma_kernel(const Params p) {
       const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
       int32_t none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln, none_c,
-                                           nullptr);
+                                           nullptr, seg);
       if (!more) break;
       x = cur.end;
       cur = segment_at(x);
       tbl0 = tbln;
     }
+    return done();
   }
 }
 
