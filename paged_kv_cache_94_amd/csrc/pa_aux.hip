@@ -38,7 +38,169 @@ __host__ __device__ inline int combine_row_groups(const Params& p) {
 // lane. The first partial rows of a chunk are requested together with its
 // (m, l), so a row costs one memory round trip once its unit's bounds are
 // known.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Two consecutive floats through a buffer descriptor (zeros past its end).
+// The words are copied out of the vector before the bit casts: a bit cast
+// of a vector element read element 0 whatever the index with this compiler.
+__device__ __forceinline__ float2 buffer_load_f32x2(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  const uint32_t a = t[0], c = t[1];
+  return make_float2(__builtin_bit_cast(float, a), __builtin_bit_cast(float, c));
+}
+
+// Merge the rows r0, r0 + step, ... of one unit when a wavefront has several
+// of them (many units, few workgroups per unit). A partial row is D floats,
+// D/4 lanes x 16 bytes, so one load instruction of the wavefront fetches the
+// rows of SPI = 256/D splits at once, and a batch of KF = 8 splits takes
+// 8/SPI instructions. The next row's (m, l) pairs and first batch are
+// requested before the current row is merged, so the rows' memory round
+// trips overlap. Loads go through buffer descriptors that end after the
+// chunk's last split: past it they return zeros without touching memory, so
+// every path issues the same loads and the compiler waits for the current
+// row's alone. Splits past the first batch (units of more than KF pieces)
+// are loaded as the merge reaches them.
+constexpr int kCombineMaxRowsPerWave = 8;   // rows a wavefront of the pipelined merge can take
+
 template <typename OutT, int D>
+__device__ __forceinline__ void combine_rows_pipelined(const Params& p, int32_t b, int32_t g, int64_t slot_first,
+                                                       int32_t ns, int r0, int step) {
+  constexpr int LPS = D / 4;      // lanes per partial row
+  constexpr int SPI = 64 / LPS;   // splits per load instruction
+  constexpr int KF = 8;           // splits per batch
+  constexpr int NI = KF / SPI;    // load instructions per batch
+  const int lane = __lane_id();
+  const int sl = lane / LPS;                  // this lane's split within an instruction
+  const int32_t loff = (lane % LPS) * 16;     // this lane's 16 bytes of a partial row
+  const int32_t S = p.rows * D * 4;           // bytes from one split's partial row to the next split's
+  struct Batch {
+    float m, l;          // lane s: split c0 + s of the chunk
+    float v[NI][4];      // instruction i: split j0 + i*SPI + sl, dims loff/4 .. +3
+  };
+  auto load_ml = [&](int32_t r, int32_t c0, int32_t cnt, Batch& x) __attribute__((always_inline)) {
+    const auto rm = buffer_rsrc(p.ws_ml + ((size_t)(slot_first + c0) * p.rows + r) * 2, cnt * p.rows * 8);
+    const float2 ml = buffer_load_f32x2(rm, lane * p.rows * 8);
+    x.m = lane < cnt ? ml.x : -INFINITY;
+    x.l = lane < cnt ? ml.y : 0.f;
+  };
+  auto load_rows = [&](int32_t r, int32_t c0, int32_t j0, int32_t cnt, Batch& x) __attribute__((always_inline)) {
+    const auto rs = buffer_rsrc(p.ws_acc + ((size_t)(slot_first + c0) * p.rows + r) * D, cnt * S);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint4 t = buffer_load16<0>(rs, (j0 + i * SPI + sl) * S + loff);
+      x.v[i][0] = __builtin_bit_cast(float, t.x);
+      x.v[i][1] = __builtin_bit_cast(float, t.y);
+      x.v[i][2] = __builtin_bit_cast(float, t.z);
+      x.v[i][3] = __builtin_bit_cast(float, t.w);
+    }
+  };
+  // Fold a chunk's (m, l) into the running max M and denominator den,
+  // rescaling o; returns this lane's weight 2^(m_s - M) (0 past the chunk).
+  auto fold = [&](const Batch& x, int32_t cnt, float& M, float& den, float (&o)[4]) __attribute__((always_inline)) {
+    float cm = x.m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor(cm, off));
+    const float Mn = fmaxf(M, cm);
+    const float Ms = Mn == -INFINITY ? 0.f : Mn;
+    const float resc = fast_exp2(M - Ms);   // 0 on the first chunk (M = -inf)
+    den *= resc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= resc;
+    M = Mn;
+    const float w = lane < cnt ? fast_exp2(x.m - Ms) : 0.f;
+    float dl = w * x.l;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dl += shfl_xor(dl, off);
+    den += dl;
+    return w;
+  };
+  // o += weight(split j0 + i*SPI + sl) * its partial row, over the batch.
+  auto accumulate = [&](const Batch& x, float w, int32_t j0, float (&o)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float ws;
+      if constexpr (SPI == 1) {
+        ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + i));
+      } else {
+        ws = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((j0 + i * SPI + sl) << 2, __builtin_bit_cast(int, w)));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += ws * x.v[i][e];
+    }
+  };
+  auto prefetch = [&](int32_t r, Batch& x) __attribute__((always_inline)) {
+    const bool live = r < p.rows;   // a row past the unit's last loads nothing
+    const int32_t cnt = live ? min(64, ns) : 0;
+    const int32_t rr = live ? r : 0;
+    load_ml(rr, 0, cnt, x);
+    load_rows(rr, 0, 0, cnt, x);
+  };
+  auto merge = [&](int32_t r, Batch& x) __attribute__((always_inline)) {
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    float M = -INFINITY, den = 0.f;
+    const int32_t cnt0 = min(64, ns);
+    const float w0 = fold(x, cnt0, M, den, o);
+    accumulate(x, w0, 0, o);
+    if (ns > KF) {
+      for (int32_t j0 = KF; j0 < cnt0; j0 += KF) {
+        load_rows(r, 0, j0, cnt0, x);
+        accumulate(x, w0, j0, o);
+      }
+      for (int32_t c0 = 64; c0 < ns; c0 += 64) {
+        const int32_t cnt = min(64, ns - c0);
+        load_ml(r, c0, cnt, x);
+        load_rows(r, c0, 0, cnt, x);
+        const float w = fold(x, cnt, M, den, o);
+        accumulate(x, w, 0, o);
+        for (int32_t j0 = KF; j0 < cnt; j0 += KF) {
+          load_rows(r, c0, j0, cnt, x);
+          accumulate(x, w, j0, o);
+        }
+      }
+    }
+    // Sum the SPI lane groups (each holds other splits' share of the same dims).
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (SPI == 4) o[e] += shfl_xor(o[e], 16);
+      if constexpr (SPI >= 2) o[e] += shfl_xor(o[e], 32);
+    }
+    if (sl == 0) {
+      const float inv = 1.f / den;
+      const int t = r / p.G;
+      const int h = g * p.G + r % p.G;
+      OutT* out = reinterpret_cast<OutT*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + loff / 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(OutT) == 4) {
+          out[e] = o[e] * inv;
+        } else {
+          out[e] = (__bf16)(o[e] * inv);
+        }
+      }
+    }
+  };
+  // Fully unrolled, so the two batches stay in fixed registers (a copy from
+  // one to the other would wait for its loads).
+  // The scheduling barriers keep the requests in row order (the compiler
+  // otherwise issues the second row's first, and the first merge then waits
+  // for both).
+  Batch bt[2];
+  prefetch(r0, bt[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  prefetch(r0 + step, bt[1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kCombineMaxRowsPerWave; ++i) {
+    const int r = r0 + i * step;
+    if (r >= p.rows) break;
+    merge(r, bt[i & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch(r + 2 * step, bt[i & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <typename OutT, int D, bool PIPE>
 __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Params p) {
   constexpr int PER = D / 64;   // dims per lane
   const int rgs = combine_row_groups(p);
@@ -95,6 +257,14 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
     }
   }
 
+  if constexpr (PIPE) {
+    // Wave-uniform values in scalar registers (the buffer descriptors need them there).
+    const int64_t sf = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(slot_first >> 32)) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)slot_first));
+    combine_rows_pipelined<OutT, D>(p, b, g, sf, __builtin_amdgcn_readfirstlane(ns),
+                                    __builtin_amdgcn_readfirstlane(rg * kCombineWaves + wave), rgs * kCombineWaves);
+    return;
+  }
   for (int r = rg * kCombineWaves + wave; r < p.rows; r += rgs * kCombineWaves) {
     const size_t slot0 = (size_t)slot_first * p.rows + r;   // partial s of this row: slot0 + s*rows
     const float* ml = p.ws_ml + slot0 * 2;
@@ -195,6 +365,17 @@ __global__ void __launch_bounds__(256) pa_gather_kernel(const Params p, const ch
   }
 }
 
+template <typename OutT, int D>
+void launch_combine_as(const Params& p, dim3 grid, dim3 block, hipStream_t st) {
+  // The pipelined instance when a wavefront merges more than one row (and
+  // at most kCombineMaxRowsPerWave of them: 32 query rows at most).
+  const int step = combine_row_groups(p) * kCombineWaves;
+  if (p.rows > step && p.rows <= kCombineMaxRowsPerWave * step)
+    hipLaunchKernelGGL((pa_combine_kernel<OutT, D, true>), grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL((pa_combine_kernel<OutT, D, false>), grid, block, 0, st, p);
+}
+
 hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
   const int64_t groups = combine_groups(p) * combine_row_groups(p);
   if (groups == 0) return hipSuccess;
@@ -203,16 +384,16 @@ hipError_t launch_combine(const Params& p, int q_dtype, int D, hipStream_t st) {
   const bool bf16 = q_dtype == 1;
   switch (D) {
     case 64:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 64>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 64>), grid, block, 0, st, p);
+      if (bf16) launch_combine_as<__bf16, 64>(p, grid, block, st);
+      else launch_combine_as<float, 64>(p, grid, block, st);
       break;
     case 128:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 128>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 128>), grid, block, 0, st, p);
+      if (bf16) launch_combine_as<__bf16, 128>(p, grid, block, st);
+      else launch_combine_as<float, 128>(p, grid, block, st);
       break;
     case 256:
-      if (bf16) hipLaunchKernelGGL((pa_combine_kernel<__bf16, 256>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((pa_combine_kernel<float, 256>), grid, block, 0, st, p);
+      if (bf16) launch_combine_as<__bf16, 256>(p, grid, block, st);
+      else launch_combine_as<float, 256>(p, grid, block, st);
       break;
     default:
       return hipErrorInvalidValue;
