@@ -16,13 +16,17 @@
 // Per step of 32 keys (two cache blocks): every thread loads 16-byte pieces
 // of the K and V rows along the cached rows and writes them to LDS as bf16
 // (int8 codes widen exactly); the next step's loads are in flight while the
-// current step is computed from the other LDS buffer. The MFMA operand
-// layouts are those of the decode kernel: S^T = K Q^T with
-// v_mfma_f32_16x16x32_bf16 (Q^T in registers), the softmax lane-local per row
-// with a 4-lane max, and O^T += V^T [P_hi; P_lo] with V^T read transposed by
-// ds_read_b64_tr_b16. Keys outside the tile's range are staged as zeros and
-// every score outside a row's [first visible key, own position] is removed
-// by select; steps whose keys every row of the tile sees skip the masks.
+// current step is computed from the other LDS buffer. S^T = K Q^T uses the
+// decode kernel's operand layout with v_mfma_f32_16x16x32_bf16 (Q^T in
+// registers), the softmax is lane-local per row with a 4-lane max, and
+// O^T += V^T P^T takes all 32 keys of a step in one instruction per output
+// tile: V^T read transposed by ds_read_b64_tr_b16 from both 16-key halves,
+// against one bf16 weight per key (rounded to nearest: each weight within a
+// relative 2^-9, so O within 2^-9 max|V| of its exact value; the row sum l
+// adds the same rounded weights, so O stays a convex combination of V rows).
+// Keys outside the tile's range are staged as zeros and every score outside
+// a row's [first visible key, own position] is removed by select; steps
+// whose keys every row of the tile sees skip the masks.
 //
 // int8 caches: K codes widen to bf16 (the query's type, so S^T keeps the bf16
 // MFMA) and V codes to f16, both exactly (|code| <= 127). The key scale, times
@@ -30,11 +34,9 @@
 // multiplies each weight (dequantize after the gather, tiniestgpt notes, KV
 // cache quantization). The weights then go to the matrix cores as one f16
 // value each (11 significant bits, rounded to nearest), against the f16 V^T
-// of both 16-key halves in one v_mfma_f32_16x16x32_f16 per output tile: half
-// the P.V instructions of the bf16 path's [P_hi; P_lo] split, which a bf16
-// cache needs because its V cannot be widened to f16 exactly. A weight times
-// its value scale must stay within f16 range: value scales below 255, i.e.
-// dequantized values below ~32500 in magnitude.
+// of both 16-key halves in one v_mfma_f32_16x16x32_f16 per output tile. A
+// weight times its value scale must stay within f16 range: value scales
+// below 255, i.e. dequantized values below ~32500 in magnitude.
 //
 // The running max is moved lazily: a row's reference max only changes when
 // its block max exceeds it by more than kRescaleSlack (log2 units), so the
@@ -382,7 +384,7 @@ pa_prefill_kernel(const PrefillParams p) {
     // Online softmax per row over the step's 32 keys; P leaves as hi/lo bf16
     // parts (bf16 caches) or as one f16 value per key times its value scale
     // (int8 caches; weight e of the lane is key 16*(e/4) + 4*q4 + e%4).
-    bf16x8 pbv[MT][2];
+    bf16x8 pbv[MT];
     f16x8 pbh[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -410,28 +412,26 @@ pa_prefill_kernel(const PrefillParams p) {
       const float msafe = m[mt] == -INFINITY ? 0.f : m[mt];
       float pe[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = fast_exp2(sc[e] - msafe);
-        l[mt] += pe[e];
-      }
+      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sc[e] - msafe);
       if constexpr (INT8) {
         // A masked key's weight is exactly 0 (2^-inf), and its value scale is
         // finite (0 outside [klo, khi]).
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pbh[mt][e] = (_Float16)(pe[e] * vsc[e]);
+        for (int e = 0; e < 8; ++e) {
+          l[mt] += pe[e];
+          pbh[mt][e] = (_Float16)(pe[e] * vsc[e]);
+        }
         continue;
       }
+      // One bf16 weight per key; the row sum takes the same rounded weights,
+      // so O stays a convex combination of the V rows.
+      const uint4 pw = make_uint4(pack_bf16(pe[0], pe[1]), pack_bf16(pe[2], pe[3]), pack_bf16(pe[4], pe[5]),
+                                  pack_bf16(pe[6], pe[7]));
+      const uint32_t pwv[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hi[e] = pe[4 * half + e];
-          lo[e] = hi[e] - __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)hi[e]) << 16);
-        }
-        pbv[mt][half] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]),
-                                                              pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])));
-      }
+      for (int i = 0; i < 4; ++i)
+        l[mt] += __builtin_bit_cast(float, pwv[i] << 16) + __builtin_bit_cast(float, pwv[i] & 0xFFFF0000u);
+      pbv[mt] = __builtin_bit_cast(bf16x8, pw);
     }
     if constexpr (INT8) {
       // O^T += V^T P^T over all 32 keys: A holds the transposed f16 V reads of
@@ -452,21 +452,24 @@ pa_prefill_kernel(const PrefillParams p) {
       }
       return;
     }
-    // O^T += V^T [P_hi; P_lo] for each half, V^T read transposed from LDS.
+    // O^T += V^T P^T over all 32 keys: A holds the transposed V reads of both
+    // halves (lane: keys 4*q4 .. +3, then 16 + 4*q4 .. +3, one dim), the order
+    // of the lane's weights in pbv.
+    const int vrow0 = 4 * q4 + (n >> 2);
+    const char* vread0 = vst + vrow0 * RS + 8 * (n & 1);
+    const char* vread1 = vread0 + 16 * RS;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int vrow = 16 * half + 4 * q4 + (n >> 2);
-      const char* vread = vst + vrow * RS + 8 * (n & 1);
+    for (int j = 0; j < TJ; ++j) {
+      // dims 16j + 4*(n&3) .. +3: 16-byte chunk 2j + ((n&3) >> 1), half (n & 1); rows vrow0 and
+      // vrow0 + 16 share a swizzle
+      const int chunk = 2 * j + ((n & 3) >> 1);
+      const int sw = S::DIRECT ? (chunk ^ lds_swz<D>(vrow0)) : chunk;
+      const uint2 a0 = lds_read_tr16(vread0 + 16 * sw);
+      const uint2 a1 = lds_read_tr16(vread1 + 16 * sw);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        // dims 16j + 4*(n&3) .. +3: 16-byte chunk 2j + ((n&3) >> 1), half (n & 1)
-        const int chunk = 2 * j + ((n & 3) >> 1);
-        const uint2 a = lds_read_tr16(vread + 16 * (S::DIRECT ? (chunk ^ lds_swz<D>(vrow)) : chunk));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, a.x, a.y));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv[mt][half], o[mt][j], 0, 0, 0);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv[mt], o[mt][j], 0, 0, 0);
     }
   };
 
