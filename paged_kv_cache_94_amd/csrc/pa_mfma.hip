@@ -85,6 +85,17 @@ __device__ __forceinline__ int32_t chunk_table(const Params& p, int32_t b, int32
   return p.block_table[(size_t)b * p.maxb + table_entry(p, idx)];
 }
 
+// Barrier that orders LDS only. The merge exchanges data through LDS alone;
+// a full __syncthreads() would also wait for every load in flight, among them
+// the next segment's touch loads below.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+constexpr int kTouch = 2;   // touch loads per lane for the next segment's first blocks
+
 // Attention of query rows (b, g) over logical blocks [first, last] of sequence
 // b. slot < 0: write the normalised output; else write (m, l, o) to
 // workspace slot `slot`. tbl0 = chunk_table(b, first, last), which the caller
@@ -92,12 +103,18 @@ __device__ __forceinline__ int32_t chunk_table(const Params& p, int32_t b, int32
 // later segment: they are waited for right after this segment's block loop,
 // when nothing else is in flight, so they reach the caller as settled values.
 // pf_claim is thread 0's claim on the piece queue; it is handed to every
-// wavefront through *claim_lds (read after this call returns). Called
-// uniformly by every wavefront of the workgroup.
+// wavefront through *claim_lds (read after this call returns). When pf holds
+// the next segment's table entries (next_g >= 0, its KV head), the wavefront
+// ends by touching that segment's first block, one dword per 128-byte line,
+// so it is on its way to L2 while the next segment starts and is found there
+// when that segment loads it; the touch loads land in `touch`,
+// which the next call consumes after its first barrier (which waits for every
+// load anyway). Called uniformly by every wavefront of the workgroup.
 template <bool INT8, bool ALIAS, int D, int MT, int NW>
 __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t first,
                                              int32_t last, int64_t slot, int32_t tbl0, int32_t& pf,
-                                             int32_t& pf_claim, int32_t* claim_lds, int32_t& seg) {
+                                             int32_t& pf_claim, int32_t* claim_lds, int32_t& seg,
+                                             int32_t next_g, uint32_t (&touch)[kTouch]) {
   const int stamp_base = kStampSeg0 + kStampPerSeg * (seg < kStampSegments ? seg : kStampSegments);
   stamp(p, stamp_base);
   stamp_value(p, stamp_base + 4, (uint64_t)(last - first + 1));
@@ -381,6 +398,10 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 #pragma unroll
   for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
   __syncthreads();
+  // The previous segment's touch loads have landed (the barrier waited for
+  // every load); their values are dead from here on.
+#pragma unroll
+  for (int t = 0; t < kTouch; ++t) keep_loaded(__builtin_bit_cast(float, touch[t]));
   // Per-row visibility: row r (query t) sees keys [first_key(t), p0 + t].
   kr = key_range(L, p.q_len, p.window);
 #pragma unroll
@@ -437,7 +458,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   // Lane l holds the same (row, dims) in every wave: the fold is per lane.
   float4* lds_o = reinterpret_cast<float4*>(smem);
   float2* lds_ml = reinterpret_cast<float2*>(smem + Lds::O_BYTES);
-  __syncthreads();   // every wavefront is done with its staging tile
+  lds_barrier();   // every wavefront is done with its staging tile
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
     lds_ml[(wave * MT + tile) * 64 + lane] = make_float2(m[tile], l[tile]);
@@ -450,7 +471,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       lds_o[((tile * TJ + j) * (NW - 1) + s) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) {
     float2 ml[NW];
@@ -518,6 +539,25 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       }
     }
   }
+  if (next_g >= 0) {
+    constexpr int LR = (ROW_BYTES + 127) / 128;         // 128-byte lines per cached row
+    constexpr int LB = kBlock * LR * (ALIAS ? 1 : 2);   // lines per block (K, and V unless aliased)
+    constexpr int TL = (LB + 63) / 64;                  // touch loads per lane (the first block only)
+    static_assert(TL <= kTouch, "touch loads");
+    const int32_t phys = __builtin_amdgcn_readfirstlane(pf);   // lane 0: the next segment's first block
+    const size_t tile = tile_offset_bytes(phys, next_g, p.Hkv, ROW_BYTES);
+#pragma unroll
+    for (int t = 0; t < TL; ++t) {
+      // The lane's line is the same for every segment; pinned here (an empty
+      // asm), so the compiler does not hoist what derives from it out of the
+      // segment loop and keep it live through the block loops.
+      int w = min(lane + 64 * t, LB - 1);
+      asm volatile("" : "+v"(w));
+      const char* base = ((w >= kBlock * LR) ? vpool : kpool) + tile + ((w / LR) % kBlock) * tok_stride +
+                         128 * (w % LR);
+      touch[t] = *reinterpret_cast<const uint32_t*>(base);
+    }
+  }
   stamp(p, stamp_base + 3);
   ++seg;
 }
@@ -531,6 +571,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
 pa_mfma_kernel(const Params p) {
   __shared__ __attribute__((aligned(16))) char smem[MfmaLds<D, MT, NW, ALIAS>::BYTES];
   int32_t seg = 0;   // segments this workgroup has run (phase stamps only)
+  uint32_t touch[kTouch] = {};   // the next segment's touch loads (consumed by the call after)
   stamp(p, kStampEntry);
   auto done = [&]() __attribute__((always_inline)) {
     stamp_value(p, kStampCount, (uint64_t)seg);
@@ -552,7 +593,7 @@ pa_mfma_kernel(const Params p) {
     stamp(p, kStampPartition);
     int32_t none = 0, none_c = 0;
     mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, first, last, slot, chunk_table<NW>(p, b, first, last), none,
-                                         none_c, nullptr, seg);
+                                         none_c, nullptr, seg, -1, touch);
     return done();
   }
   __shared__ int32_t pre[balanced_seq_limit(NW) + 1];
@@ -598,7 +639,8 @@ pa_mfma_kernel(const Params p) {
       const Run r = run_of(w);
       int32_t none = 0, none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot,
-                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr, seg);
+                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr, seg, -1,
+                                           touch);
       return done();
     }
     // Queue: claims only grow, so a workgroup's pieces come in increasing
@@ -618,14 +660,15 @@ pa_mfma_kernel(const Params p) {
     }
     while (w >= 0 && w < npieces) {
       const Run r = run_of(w);
-      int32_t tbln = 0, claim = 0;
+      int32_t tbln = 0, claim = 0, next_g = -1;
       if (w1 >= 0 && w1 < npieces) {
         const Run rn = run_of(w1);
         tbln = chunk_table<NW>(p, rn.b, rn.first, rn.last);
+        next_g = rn.g;
       }
       if (threadIdx.x == 0) claim = atomicAdd(qnext, 1);
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot, tbl0, tbln, claim,
-                                           &claims[0], seg);
+                                           &claims[0], seg, next_g, touch);
       w = w1;
       w1 = piece_of_claim(claims[0]);
       tbl0 = tbln;
@@ -682,16 +725,17 @@ pa_mfma_kernel(const Params p) {
     while (true) {
       // The next segment's first table chunk loads while this one streams.
       const bool more = cur.end < hi;
-      int32_t tbln = 0;
+      int32_t tbln = 0, next_g = -1;
       if (more) {
         const Seg nx = segment_at(cur.end);
         tbln = chunk_table<NW>(p, nx.b, nx.first, nx.last);
+        next_g = nx.g;
       }
       const bool whole = x == cur.off && cur.end == cur.off + (pre[cur.b + 1] - pre[cur.b]);
       const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
       int32_t none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln, none_c,
-                                           nullptr, seg);
+                                           nullptr, seg, next_g, touch);
       if (!more) break;
       x = cur.end;
       cur = segment_at(x);
