@@ -94,27 +94,37 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-constexpr int kTouch = 2;   // touch loads per lane for the next segment's first blocks
+constexpr int kTouch = 2;   // touch loads per lane for the next segment's first block
+
+// What a segment's caller finds out about the segment after it: its first
+// table chunk (a load in flight), thread 0's queue claim (an atomic in
+// flight) and its KV head (-1: no next segment).
+struct NextSeg {
+  int32_t tbl = 0, claim = 0, g = -1;
+};
 
 // Attention of query rows (b, g) over logical blocks [first, last] of sequence
 // b. slot < 0: write the normalised output; else write (m, l, o) to
 // workspace slot `slot`. tbl0 = chunk_table(b, first, last), which the caller
-// may have loaded ahead. pf and pf_claim are loads the caller issued for a
-// later segment: they are waited for right after this segment's block loop,
-// when nothing else is in flight, so they reach the caller as settled values.
+// may have loaded ahead. next_fn() finds the segment after this one (a search
+// in LDS, a table load and a queue claim); it runs once this segment's first
+// loads are issued, so its latency hides under theirs, and its loads come back
+// in pf and pf_claim: they are waited for right after this segment's block
+// loop, when nothing else is in flight, so they reach the caller as settled
+// values.
 // pf_claim is thread 0's claim on the piece queue; it is handed to every
 // wavefront through *claim_lds (read after this call returns). When pf holds
-// the next segment's table entries (next_g >= 0, its KV head), the wavefront
+// the next segment's table entries (next_fn's g >= 0, its KV head), the wavefront
 // ends by touching that segment's first block, one dword per 128-byte line,
 // so it is on its way to L2 while the next segment starts and is found there
 // when that segment loads it; the touch loads land in `touch`,
 // which the next call consumes after its first barrier (which waits for every
 // load anyway). Called uniformly by every wavefront of the workgroup.
-template <bool INT8, bool ALIAS, int D, int MT, int NW>
+template <bool INT8, bool ALIAS, int D, int MT, int NW, typename NextFn>
 __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_t b, int32_t g, int32_t first,
                                              int32_t last, int64_t slot, int32_t tbl0, int32_t& pf,
                                              int32_t& pf_claim, int32_t* claim_lds, int32_t& seg,
-                                             int32_t next_g, uint32_t (&touch)[kTouch]) {
+                                             uint32_t (&touch)[kTouch], NextFn&& next_fn) {
   const int stamp_base = kStampSeg0 + kStampPerSeg * (seg < kStampSegments ? seg : kStampSegments);
   stamp(p, stamp_base);
   stamp_value(p, stamp_base + 4, (uint64_t)(last - first + 1));
@@ -397,6 +407,10 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   tbl = tbl_first;
 #pragma unroll
   for (int d = 0; d + 1 < DEPTH; ++d) fetch(d, f[d]);
+  const NextSeg next = next_fn();
+  pf = next.tbl;
+  pf_claim = next.claim;
+  const int32_t next_g = next.g;
   __syncthreads();
   // The previous segment's touch loads have landed (the barrier waited for
   // every load); their values are dead from here on.
@@ -593,7 +607,7 @@ pa_mfma_kernel(const Params p) {
     stamp(p, kStampPartition);
     int32_t none = 0, none_c = 0;
     mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, b, g, first, last, slot, chunk_table<NW>(p, b, first, last), none,
-                                         none_c, nullptr, seg, -1, touch);
+                                         none_c, nullptr, seg, touch, [] { return NextSeg{}; });
     return done();
   }
   __shared__ int32_t pre[balanced_seq_limit(NW) + 1];
@@ -639,8 +653,8 @@ pa_mfma_kernel(const Params p) {
       const Run r = run_of(w);
       int32_t none = 0, none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot,
-                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr, seg, -1,
-                                           touch);
+                                           chunk_table<NW>(p, r.b, r.first, r.last), none, none_c, nullptr, seg,
+                                           touch, [] { return NextSeg{}; });
       return done();
     }
     // Queue: claims only grow, so a workgroup's pieces come in increasing
@@ -654,24 +668,33 @@ pa_mfma_kernel(const Params p) {
     int32_t tbl0 = 0;
     // A negative claim can only come from a header that was not zero-filled;
     // it ends the workgroup rather than naming a piece.
+    Run r{};
     if (w >= 0 && w < npieces) {
-      const Run r = run_of(w);
+      r = run_of(w);
       tbl0 = settle(chunk_table<NW>(p, r.b, r.first, r.last));
     }
     while (w >= 0 && w < npieces) {
-      const Run r = run_of(w);
-      int32_t tbln = 0, claim = 0, next_g = -1;
-      if (w1 >= 0 && w1 < npieces) {
-        const Run rn = run_of(w1);
-        tbln = chunk_table<NW>(p, rn.b, rn.first, rn.last);
-        next_g = rn.g;
-      }
-      if (threadIdx.x == 0) claim = atomicAdd(qnext, 1);
+      // The next piece's run is found once, inside the segment (under its
+      // first loads), and carried into the next iteration (the search is
+      // eight dependent LDS reads and three divisions).
+      Run rn{};
+      int32_t tbln = 0, claim = 0;
+      auto next = [&]() __attribute__((always_inline)) {
+        NextSeg nx;
+        if (w1 >= 0 && w1 < npieces) {
+          rn = run_of(w1);
+          nx.tbl = chunk_table<NW>(p, rn.b, rn.first, rn.last);
+          nx.g = rn.g;
+        }
+        if (threadIdx.x == 0) nx.claim = atomicAdd(qnext, 1);
+        return nx;
+      };
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, r.b, r.g, r.first, r.last, r.slot, tbl0, tbln, claim,
-                                           &claims[0], seg, next_g, touch);
+                                           &claims[0], seg, touch, next);
       w = w1;
       w1 = piece_of_claim(claims[0]);
       tbl0 = tbln;
+      r = rn;
     }
     // The last workgroup of a shard out returns its counters to zero for the
     // next call (every claim on that shard has completed by then).
@@ -725,17 +748,21 @@ pa_mfma_kernel(const Params p) {
     while (true) {
       // The next segment's first table chunk loads while this one streams.
       const bool more = cur.end < hi;
-      int32_t tbln = 0, next_g = -1;
-      if (more) {
-        const Seg nx = segment_at(cur.end);
-        tbln = chunk_table<NW>(p, nx.b, nx.first, nx.last);
-        next_g = nx.g;
-      }
+      int32_t tbln = 0;
+      auto next = [&]() __attribute__((always_inline)) {
+        NextSeg nx;
+        if (more) {
+          const Seg sg = segment_at(cur.end);
+          nx.tbl = chunk_table<NW>(p, sg.b, sg.first, sg.last);
+          nx.g = sg.g;
+        }
+        return nx;
+      };
       const bool whole = x == cur.off && cur.end == cur.off + (pre[cur.b + 1] - pre[cur.b]);
       const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
       int32_t none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln, none_c,
-                                           nullptr, seg, next_g, touch);
+                                           nullptr, seg, touch, next);
       if (!more) break;
       x = cur.end;
       cur = segment_at(x);
