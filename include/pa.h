@@ -90,7 +90,9 @@ typedef struct {
   int32_t waves;              /* wavefronts per workgroup: 4 or 8 (also 2 for the matrix-core kernel); 0 auto */
   int32_t blocks_per_wave;    /* aligned splits without num_splits: blocks per wavefront per split; 0 auto */
   int32_t partition;          /* PA_PART_* */
-  int32_t pieces_per_wg;      /* PA_PART_QUEUE: pieces per workgroup the queue aims for, 1..64; 0 auto */
+  int32_t pieces_per_wg;      /* PA_PART_QUEUE: pieces per workgroup the queue aims for, 1..64; 0 auto
+                                 (the plan then keeps at least two pieces per unit; an explicit count
+                                 at least one) */
   int32_t oversub;            /* list / piece partitions: workgroups per resident slot, 1..64; 0 auto */
 } pa_tuning;
 

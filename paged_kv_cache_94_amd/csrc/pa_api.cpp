@@ -247,7 +247,10 @@ int make_plan(const pa_args* a, Plan* pl) {
       P.queue = queue;
       const int64_t per_wg = tu.pieces_per_wg > 0 ? tu.pieces_per_wg : 4;
       P.pieces = queue ? per_wg * P.nwg : P.nwg;
-      if (P.pieces < 2 * units) P.pieces = 2 * units;   // the device's search for the piece size needs this
+      // The device's search for the piece size needs at least one piece per
+      // unit; the plan's own choice keeps twice that, an explicit request
+      // (tuning.pieces_per_wg) only the minimum.
+      if (P.pieces < 2 * units) P.pieces = tu.pieces_per_wg > 0 ? std::max<int64_t>(P.pieces, units) : 2 * units;
       P.slots = P.pieces;
     } else {
       P.queue = false;

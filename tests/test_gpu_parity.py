@@ -161,6 +161,26 @@ def test_mfma_partitions(case, mode):
     np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
 
 
+@pytest.mark.parametrize("per_wg", [1, 3])
+def test_queue_pieces_down_to_one_per_unit(per_wg):
+    """An explicit pieces-per-workgroup request may go below the plan's two
+    pieces per unit, down to one: with 1280 units and 512 workgroups, 1 asks
+    for 512 pieces and gets one per unit (no partials), 3 asks for 1536."""
+    rng = np.random.default_rng(zlib.crc32(b"pieces-per-wg") + per_wg)
+    lens = rng.integers(16, 1500, 160).tolist()
+    x = make_inputs(lens, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16",
+                    poison=True, seed=per_wg)
+    dev = Dev(x)
+    tuning = {"partition": "queue", "pieces_per_wg": per_wg}
+    plan = dev.plan(tuning=tuning)
+    units = x.batch * x.num_kv_heads
+    _log(f"queue pieces_per_wg={per_wg}: plan {plan}")
+    assert plan["queue"] == 1 and plan["pieces"] == max(per_wg * plan["grid"], units) < 2 * units
+    got = dev.run_f64(tuning=tuning)
+    assert not np.isnan(got).any()
+    assert max_err(got, _oracle(x)) <= TOL["bf16"]
+
+
 # --- invariants on the GPU path -------------------------------------------------------------------
 
 def test_block_permutation_is_bit_identical():
