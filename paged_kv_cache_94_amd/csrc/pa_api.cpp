@@ -264,7 +264,7 @@ int make_plan(const pa_args* a, Plan* pl) {
   // prefix sums.
   if (P.slots > 0) {
     P.ws_bytes = kWsHeader + (size_t)P.slots * P.rows * (size_t)(D + 2) * sizeof(float);
-    if (P.balanced) P.ws_bytes += (size_t)(a->num_seqs + 1) * sizeof(int32_t);
+    if (P.balanced) P.ws_bytes += (size_t)(2 * a->num_seqs + 1) * sizeof(int32_t);
   } else {
     P.ws_bytes = 0;
   }
@@ -283,7 +283,9 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   p.block_table = a->block_table;
   p.seq_lens = a->seq_lens;
   // Workspace: the header (queue words), acc [slots][rows][D] f32, then
-  // (m, l) [slots][rows][2] f32, then (balanced mode) the prefix sums [B+1] int32.
+  // (m, l) [slots][rows][2] f32, then (balanced modes) a sequence table of
+  // 2B+1 int32: block prefix sums [B+1] (list partition), or first piece
+  // numbers [B] and piece counts [B] (piece partition).
   const size_t acc_bytes = (size_t)P.slots * P.rows * a->head_dim * sizeof(float);
   const size_t ml_bytes = (size_t)P.slots * P.rows * 2 * sizeof(float);
   char* ws = reinterpret_cast<char*>(a->workspace);

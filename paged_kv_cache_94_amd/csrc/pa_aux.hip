@@ -238,14 +238,15 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
     const int32_t L = p.seq_lens[b];
     if (p.balanced == 2) {
       // Piece partition: unit (b, g) was cut into k pieces, numbered
-      // kp[b] + g*k .. + k-1, each of which left its partial in the slot of
-      // its own number; a unit of one piece was written out directly. The
-      // prefix entries are requested with the length (both are in bounds
-      // whatever the length holds).
+      // first + g*k .. + k-1 (sequence b's first piece number and its Hkv*k
+      // pieces are in the workspace table), each of which left its partial
+      // in the slot of its own number; a unit of one piece was written out
+      // directly. The table entries are requested with the length (both are
+      // in bounds whatever the length holds).
       const int32_t kp0 = p.ws_prefix[b];
-      const int32_t kp1 = p.ws_prefix[b + 1];
+      const int32_t cnt = p.ws_prefix[p.B + b];
       if (!len_ok(L, p)) return;
-      const int32_t k = (kp1 - kp0) / p.Hkv;
+      const int32_t k = cnt / p.Hkv;
       if (k <= 1) return;
       slot_first = kp0 + (int64_t)g * k;
       ns = k;

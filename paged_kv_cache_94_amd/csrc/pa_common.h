@@ -75,7 +75,6 @@ constexpr int kMaxBalancedSeqs = 2048;   // flattened-list partition: block pref
 // Workgroups of one or two wavefronts run four to eight to a compute unit, so
 // their LDS share is smaller: their prefix table holds fewer sequences.
 constexpr int balanced_seq_limit(int nw) { return nw >= 4 ? kMaxBalancedSeqs : 1024; }
-constexpr int kMaxPieceSeqs = 512;       // piece partition: blocks per sequence
 // Piece queue in the workspace header: kQueueShards "next" counters, then as
 // many "done" counters, each on its own 64-byte line (int32 index stride 16).
 constexpr int kQueueShards = 8;

@@ -39,7 +39,7 @@ struct Params {
   int32_t splits, bps;  // aligned mode: splits per sequence and logical blocks per split
   int32_t balanced;     // 0: aligned splits; 1: flattened-list partition; 2: piece partition
   int32_t nwg;          // modes 1 and 2: workgroups of the launch
-  int32_t* ws_prefix;   // mode 1: [B+1] block prefix sums; mode 2: [B+1] piece prefix sums (workgroup 0 writes)
+  int32_t* ws_prefix;   // mode 1: [B+1] block prefix sums; mode 2: [B] first piece numbers, [B] piece counts (workgroup 0 writes)
   int32_t pieces;       // mode 2: pieces the partition aims for (nwg, or more when they are handed out)
   int32_t* ws_queue;    // mode 2, non-null: hand pieces out through this [2] counter pair (zero between calls)
   int32_t ring;         // > 0: each table row is a ring of this many entries (logical block i -> i mod ring)
@@ -225,19 +225,33 @@ __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre, int32_t* 
 
 // Piece partition. Unit (b, g) with n_b blocks is cut into
 // k_b = ceil(n_b / per) pieces of ceil(n_b / k_b) blocks; `per` is the
-// smallest count for which all pieces number at most p.pieces. Pieces are
-// ordered by (b, g, piece). With p.pieces == nwg each workgroup owns the
-// piece of its own index (few units: long contexts on one or two KV heads);
-// with more, workgroups take pieces from a queue until none are left, which
-// evens out the time workgroups take for the same number of blocks.
+// smallest count for which all pieces number at most p.pieces. With
+// p.pieces == nwg each workgroup owns the piece of its own index (few units:
+// long contexts on one or two KV heads); with more, workgroups take pieces
+// from a queue until none are left, which evens out the time workgroups take
+// for the same number of blocks.
+//
+// With by_size, pieces are numbered largest first, so that the last ones a
+// queue hands out are the shortest and workgroups run out of work at nearly
+// the same time. Sequences fall into kPieceClasses classes by the size c_b of
+// their pieces, class floor(kPieceClasses * (per - c_b) / per) (class 0 the
+// largest); the order is by class, then by b, then by (g, piece), so a unit's
+// pieces stay consecutive. Without it (one piece per workgroup, where the
+// order changes nothing) the order is by (b, g, piece). A sequence with no
+// blocks has no pieces: its rank r has kp[r] == kp[r + 1] wherever it falls.
 //
 // Wave 0 fills nbs[b] = n_b, blo[b] = the first logical block sequence b
-// loads, and kp[0..B] = Hkv * (k_0 + ... + k_{b-1}); the caller synchronises
-// the workgroup before reading them. `per` is at least min_per (enough
-// blocks for every wavefront of the workgroup). Needs p.pieces >= 2 * B * Hkv
-// (checked on the host), which bounds the search below.
+// loads, ord[r] = the sequence at rank r, and kp[0..B] = Hkv * (k_ord[0] + ...
+// + k_ord[r-1]), the number of the first piece of rank r; the caller
+// synchronises the workgroup before reading them. `per` is at least min_per
+// (enough blocks for every wavefront of the workgroup). Needs p.pieces >=
+// B * Hkv (checked on the host), which bounds the search below.
+constexpr int kMaxPieceSeqs = 512;   // batch limit of the piece partition (its per-sequence tables live in LDS)
+constexpr int kPieceClasses = 8;
+
 template <typename P>
-__device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* blo, int32_t* kp, int32_t min_per) {
+__device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* blo, int32_t* ord, int32_t* kp,
+                                             int32_t min_per, bool by_size) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   int64_t total = 0;
@@ -266,20 +280,113 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
   int64_t hi = spare > 0 ? (total + spare - 1) / spare : total;
   if (lo < min_per) lo = min_per;
   if (hi < lo) hi = lo;   // pieces() only falls as per grows
+  // Bisection for the smallest fitting count in [lo, hi]. Its first two probes
+  // sit where the answer usually is: at the count that fits if every unit's
+  // last piece is half full (total / (target - units / 2)), then next to it on
+  // the side that is still open. Most searches end there instead of after
+  // log2(hi - lo) probes; the result is the same.
+  auto probe = [&](int64_t x) {
+    const bool fits = pieces((int32_t)x) <= target;
+    if (fits) hi = x;
+    else lo = x + 1;
+    return fits;
+  };
+  if (lo < hi) {
+    const int64_t half = target - ((int64_t)p.B * p.Hkv) / 2;
+    int64_t guess = (total + half - 1) / half;
+    guess = guess < lo ? lo : (guess > hi - 1 ? hi - 1 : guess);
+    const bool fits = probe(guess);
+    if (lo < hi) probe(fits ? hi - 1 : lo);
+  }
   while (lo < hi) {
     const int64_t mid = (lo + hi) >> 1;
-    if (pieces((int32_t)mid) <= target) hi = mid;
-    else lo = mid + 1;
+    probe(mid);
   }
   const int32_t per = (int32_t)lo;
-  if (lane == 0) kp[0] = 0;
+  if (!by_size) {
+    if (lane == 0) kp[0] = 0;
+    int32_t carry = 0;
+    for (int32_t base = 0; base < p.B; base += 64) {
+      const int32_t b = base + lane;
+      const int32_t v = wave_scan_incl(b < p.B ? (nbs[b] + per - 1) / per * p.Hkv : 0);
+      if (b < p.B) {
+        ord[b] = b;
+        kp[b + 1] = carry + v;
+      }
+      carry += __builtin_amdgcn_readlane(v, 63);
+    }
+    return;
+  }
+  // Class and piece count of each of this lane's sequences (per and c_b are
+  // below 2^27, so 8 * per fits). Class >= j exactly when 8c <= (8 - j) per.
+  static_assert(kPieceClasses == 8, "classes are counted in 8-bit fields of two words");
+  constexpr int kChunks = kMaxPieceSeqs / 64;
+  int32_t cls[kChunks], kk[kChunks];
+  uint32_t tot_lo = 0, tot_hi = 0;   // sequences per class: 4 fields of 8 bits in each word per chunk
+  int32_t tot[kPieceClasses] = {};
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (i * 64 >= p.B) break;
+    const int32_t b = i * 64 + lane;
+    const int32_t nb = b < p.B ? nbs[b] : 0;
+    const int32_t k = (nb + per - 1) / per;
+    const int32_t c = k > 0 ? (nb + k - 1) / k : 0;
+    int32_t q = 0;
+#pragma unroll
+    for (int j = 1; j < kPieceClasses; ++j) q += 8 * c <= (8 - j) * per ? 1 : 0;
+    cls[i] = q;
+    kk[i] = k * p.Hkv;
+    const uint32_t one = b < p.B ? 1u << (8 * (q & 3)) : 0u;
+    tot_lo = (uint32_t)wave_sum((int32_t)(q < 4 ? one : 0u));
+    tot_hi = (uint32_t)wave_sum((int32_t)(q < 4 ? 0u : one));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tot[j] += (tot_lo >> (8 * j)) & 0xFF;
+      tot[4 + j] += (tot_hi >> (8 * j)) & 0xFF;
+    }
+  }
+  // Rank of each sequence: its class's start, the sequences of its class in
+  // earlier chunks, and those on lower lanes of its own chunk.
+  int32_t off[kPieceClasses];
+  off[0] = 0;
+#pragma unroll
+  for (int j = 1; j < kPieceClasses; ++j) off[j] = off[j - 1] + tot[j - 1];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (i * 64 >= p.B) break;
+    const int32_t b = i * 64 + lane;
+    const int32_t q = cls[i];
+    const uint32_t one = b < p.B ? 1u << (8 * (q & 3)) : 0u;
+    const uint32_t in_lo = (uint32_t)wave_scan_incl((int32_t)(q < 4 ? one : 0u));
+    const uint32_t in_hi = (uint32_t)wave_scan_incl((int32_t)(q < 4 ? 0u : one));
+    const int32_t before = (int32_t)(((q < 4 ? in_lo : in_hi) >> (8 * (q & 3))) & 0xFF) - 1;
+    int32_t start = off[0];
+#pragma unroll
+    for (int j = 1; j < kPieceClasses; ++j) start = q == j ? off[j] : start;
+    if (b < p.B) {
+      ord[start + before] = b;
+      kp[start + before + 1] = kk[i];   // piece counts by rank, summed in place below
+    }
+    const uint32_t ch_lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)in_lo, 63);
+    const uint32_t ch_hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)in_hi, 63);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      off[j] += (ch_lo >> (8 * j)) & 0xFF;
+      off[4 + j] += (ch_hi >> (8 * j)) & 0xFF;
+    }
+  }
+  // The counts were written by other lanes of this wavefront.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int32_t carry = 0;
   for (int32_t base = 0; base < p.B; base += 64) {
-    const int32_t b = base + lane;
-    const int32_t v = wave_scan_incl(b < p.B ? (nbs[b] + per - 1) / per * p.Hkv : 0);
-    if (b < p.B) kp[b + 1] = carry + v;
+    const int32_t r = base + lane;
+    const int32_t v = wave_scan_incl(r < p.B ? kp[r + 1] : 0);   // each lane rewrites only what it read
+    if (r < p.B) kp[r + 1] = carry + v;
     carry += __builtin_amdgcn_readlane(v, 63);
   }
+  if (lane == 0) kp[0] = 0;
 }
 
 // The piece of work a workgroup owns in the piece partition.
@@ -290,9 +397,11 @@ struct Piece {
   int32_t count;   // blocks it streams (>= 1)
 };
 
-// Piece w (< kp[B]) of the list: the largest b with kp[b] <= w owns it.
-__device__ __forceinline__ Piece piece_of(const int32_t* nbs, const int32_t* kp, int32_t B, int32_t Hkv,
-                                          int32_t w) {
+// Piece w (< kp[B]) of the list: the sequence of the largest rank r with
+// kp[r] <= w owns it (ranks without pieces have kp[r] == kp[r + 1] and are
+// passed over).
+__device__ __forceinline__ Piece piece_of(const int32_t* nbs, const int32_t* ord, const int32_t* kp, int32_t B,
+                                          int32_t Hkv, int32_t w) {
   int32_t lo = 0, hi = B - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
@@ -300,12 +409,12 @@ __device__ __forceinline__ Piece piece_of(const int32_t* nbs, const int32_t* kp,
     else hi = mid - 1;
   }
   Piece pc;
-  pc.b = lo;
+  pc.b = ord[lo];
   pc.k = (kp[lo + 1] - kp[lo]) / Hkv;
   const int32_t r = w - kp[lo];
   pc.g = r / pc.k;
   const int32_t i = r % pc.k;
-  const int32_t nb = nbs[lo];
+  const int32_t nb = nbs[pc.b];
   const int32_t len = (nb + pc.k - 1) / pc.k;   // (k-1)*len < nb: every piece is non-empty
   pc.first = i * len;
   pc.count = min(nb, pc.first + len) - pc.first;

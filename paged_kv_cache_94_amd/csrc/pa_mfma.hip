@@ -616,28 +616,37 @@ pa_mfma_kernel(const Params p) {
     // partial is the piece's own index.
     __shared__ int32_t nbs[kMaxPieceSeqs];
     __shared__ int32_t blo[kMaxPieceSeqs];
+    __shared__ int32_t ord[kMaxPieceSeqs];
     __shared__ int32_t claims[2];
     // Queue shard of this workgroup: shard s hands out pieces s, s + kQueueShards, ...
     // (one counter per shard: claims on a single counter serialize at ~11 ns each).
     const int32_t shard = blockIdx.x % kQueueShards;
     int32_t* const qnext = p.ws_queue ? p.ws_queue + shard * kQueueStride : nullptr;
     int32_t* const qdone = qnext ? qnext + kQueueShards * kQueueStride : nullptr;
-    piece_prefix(p, nbs, blo, pre, 2 * NW);
-    if (qnext && threadIdx.x == 0) {
-      claims[0] = atomicAdd(qnext, 1);   // this workgroup's first two claims
+    // This workgroup's first two claims, from the second wavefront while the
+    // first one searches the partition.
+    static_assert(NW >= 2, "claims and partition search run on different wavefronts");
+    if (qnext && threadIdx.x == 64) {
+      claims[0] = atomicAdd(qnext, 1);
       claims[1] = atomicAdd(qnext, 1);
     }
+    piece_prefix(p, nbs, blo, ord, pre, 2 * NW, qnext != nullptr);
     __syncthreads();
     stamp(p, kStampPartition);
+    // For the combine: the number of sequence b's first piece, and its piece count.
     if (blockIdx.x == 0 && p.ws_prefix)
-      for (int32_t b = threadIdx.x; b <= p.B; b += NW * 64) p.ws_prefix[b] = pre[b];
+      for (int32_t r = threadIdx.x; r < p.B; r += NW * 64) {
+        const int32_t b = ord[r];
+        p.ws_prefix[b] = pre[r];
+        p.ws_prefix[p.B + b] = pre[r + 1] - pre[r];
+      }
     const int32_t npieces = pre[p.B];
     struct Run {
       int32_t b, g, first, last;
       int64_t slot;
     };
     auto run_of = [&](int32_t w) __attribute__((always_inline)) {
-      const Piece pc = piece_of(nbs, pre, p.B, p.Hkv, w);
+      const Piece pc = piece_of(nbs, ord, pre, p.B, p.Hkv, w);
       Run r;
       r.b = pc.b;
       r.g = pc.g;

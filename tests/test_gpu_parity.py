@@ -181,6 +181,39 @@ def test_queue_pieces_down_to_one_per_unit(per_wg):
     assert max_err(got, _oracle(x)) <= TOL["bf16"]
 
 
+def test_queue_size_order_with_empty_sequences():
+    """The queue hands pieces out largest first: sequences are ranked by the
+    size of their pieces in eight classes, here across all eight 64-sequence
+    chunks of the ranking (500 sequences, lengths spanning every class), with
+    a dozen sequences that have no blocks (a length below the step's query
+    count) ranked among them. Every other sequence must match the oracle and
+    visit each of its blocks exactly once; the empty ones visit none."""
+    rng = np.random.default_rng(zlib.crc32(b"queue-size-order"))
+    lens = np.clip(np.rint(rng.lognormal(np.log(120.0), 1.0, 500)), 5, 2000).astype(np.int64)
+    x = make_inputs(lens.tolist(), q_len=5, num_q_heads=16, num_kv_heads=4, head_dim=64, q_dtype="bf16",
+                    kv_dtype="bf16", poison=True, seed=11)
+    empty = rng.choice(x.batch, 12, replace=False)
+    dev = Dev(x)
+    dev_lens = x.seq_lens.astype(np.int32).copy()
+    dev_lens[empty] = 2
+    dev.lens = torch.from_numpy(dev_lens).cuda()
+    tuning = {"partition": "queue"}
+    plan = dev.plan(tuning=tuning)
+    _log(f"queue size order: plan {plan}")
+    assert plan["kernel"] == 1 and plan["queue"] == 1 and plan["pieces"] >= 2 * x.batch * x.num_kv_heads
+    got = dev.run_f64(tuning=tuning)
+    keep = np.ones(x.batch, dtype=bool)
+    keep[empty] = False
+    ref = _oracle(x)
+    assert not np.isnan(got[keep]).any()
+    assert max_err(got[keep], ref[keep]) <= TOL["bf16"]
+    visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
+    dev.run(debug_visits=visits, tuning=tuning)
+    expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
+    expect[empty] = 0
+    np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
+
+
 # --- invariants on the GPU path -------------------------------------------------------------------
 
 def test_block_permutation_is_bit_identical():
