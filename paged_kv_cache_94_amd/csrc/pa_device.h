@@ -201,6 +201,69 @@ __device__ __forceinline__ int64_t wave_sum_wide(int32_t x) {
   return lo + (hi << 16);
 }
 
+// Maximum over the wavefront of non-negative values (the same DPP steps as
+// the scan; a lane whose source falls outside its row takes 0).
+__device__ __forceinline__ int32_t wave_max_nonneg(int32_t x) {
+  x = max(x, dpp_i32<0x111>(x));
+  x = max(x, dpp_i32<0x112>(x));
+  x = max(x, dpp_i32<0x114>(x));
+  x = max(x, dpp_i32<0x118>(x));
+  x = max(x, dpp_i32<0x142, 0xA>(x));
+  x = max(x, dpp_i32<0x143, 0xC>(x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Inclusive scans (wave_scans) or sums (wave_sums, the same value in every
+// lane) of N values at once: each DPP step is applied to all N before the
+// next, so no step waits on the result of the one before it.
+template <int N>
+__device__ __forceinline__ void wave_scans(int32_t (&x)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_i32<0x111>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_i32<0x112>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_i32<0x114>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_i32<0x118>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_i32<0x142, 0xA>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_i32<0x143, 0xC>(x[j]);
+}
+template <int N>
+__device__ __forceinline__ void wave_sums(int32_t (&x)[N]) {
+  wave_scans(x);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] = __builtin_amdgcn_readlane(x[j], 63);
+}
+
+// 1/d to within a few ulps: the hardware estimate and two Newton steps.
+// (The IEEE division sequence reads and writes VCC, which serializes
+// neighbouring divisions; these chains overlap.)
+__device__ __forceinline__ double recip(double d) {
+  double r = __builtin_amdgcn_rcp(d);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  return __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+}
+
+// ceil(n / d) for 0 <= n < 2^31 and 1 <= d < 2^31 by one double fma: the
+// quotient (n + d - 1/2) / d lies at least 1/(2d) from every integer, and
+// the error of the fma with an inverse good to a few ulps stays below
+// (n/d + 1) * 2^-48, far smaller, so truncating it gives
+// floor((n + d - 1) / d) exactly. The divisor's two constants are computed
+// once for many numerators.
+struct CeilDiv {
+  double inv, bias;
+};
+__device__ __forceinline__ CeilDiv ceil_div_by(int32_t d) {
+  const double inv = recip((double)d);
+  return {inv, ((double)d - 0.5) * inv};
+}
+__device__ __forceinline__ int32_t ceil_div(double n, const CeilDiv& c) {
+  return (int32_t)__builtin_fma(n, c.inv, c.bias);
+}
+
 // pre[0..B] = prefix sums of seq_blocks over the batch and blo[0..B) = the
 // first logical block each sequence loads, computed by wave 0 of the
 // workgroup (64 sequences per step, DPP scan); the caller synchronises the
@@ -254,61 +317,99 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
                                              int32_t min_per, bool by_size) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  int64_t total = 0;
-  for (int32_t base = 0; base < p.B; base += 64) {
-    const int32_t b = base + lane;
-    const int32_t L = b < p.B ? p.seq_lens[b] : 0;
-    const int32_t nb = b < p.B ? seq_blocks(L, p) : 0;
-    if (b < p.B) {
-      nbs[b] = nb;
-      blo[b] = key_range(L, p.q_len, p.window).blk_lo;
-    }
-    total += wave_sum_wide(nb);
+  // Lane l holds sequences l, l + 64, ... in registers: chunk i is b = 64 i + l.
+  // Every length is requested at once (one memory round trip); lanes past the
+  // batch count no blocks.
+  constexpr int kChunks = kMaxPieceSeqs / 64;
+  const int32_t nch = (p.B + 63) >> 6;
+  int32_t L[kChunks], nb[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int32_t b = i * 64 + lane;
+    L[i] = i < nch && b < p.B ? p.seq_lens[b] : 0;
   }
-  total *= p.Hkv;
-  // Pieces needed with at most `per` blocks each: sum over units of ceil(n / per).
-  // B <= kMaxPieceSeqs keeps the count far below 2^31.
-  auto pieces = [&](int32_t per) {
-    int32_t c = 0;
-    for (int32_t b = lane; b < p.B; b += 64) c += (nbs[b] + per - 1) / per;
-    return (int64_t)wave_sum(c) * p.Hkv;
-  };
-  // pieces(per) <= total / per + B*Hkv, so per_hi = ceil(total / (target - B*Hkv)) always fits.
+  int32_t lane_blocks = 0;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    nb[i] = 0;
+    if (i >= nch) continue;
+    const int32_t b = i * 64 + lane;
+    if (b < p.B) {
+      nb[i] = seq_blocks(L[i], p);
+      nbs[b] = nb[i];
+      blo[b] = key_range(L[i], p.q_len, p.window).blk_lo;
+    }
+    lane_blocks += nb[i];   // at most 8 sequences of < 2^27 blocks
+  }
+  const int64_t total = wave_sum_wide(lane_blocks) * p.Hkv;
+  double nbd[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) nbd[i] = (double)nb[i];
+  // Bounds of the smallest fitting count: it is at least total / target, and
+  // ceil(total / (target - units)) fits (pieces(per) <= total / per + units),
+  // as does the longest unit (one piece each). The quotients are taken in
+  // double (relative error far below 2^-40 for quotients below 2^31):
+  // truncated, the first is at most its ceiling; the second is widened by
+  // two, which keeps both bounds valid.
   const int64_t target = p.pieces;
-  const int64_t spare = target - (int64_t)p.B * p.Hkv;
-  int64_t lo = (total + target - 1) / target;
-  int64_t hi = spare > 0 ? (total + spare - 1) / spare : total;
+  const int64_t units = (int64_t)p.B * p.Hkv;
+  const int64_t spare = target - units;
+  const double totd = (double)total;
+  int32_t lo = (int32_t)fmin(totd * recip((double)target), 1073741824.0);
+  int32_t hi;
+  if (spare > 0) {
+    hi = (int32_t)fmin(totd * recip((double)spare) + 2.0, 1073741824.0);
+  } else {
+    int32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) m = nb[i] > m ? nb[i] : m;
+    hi = wave_max_nonneg(m);
+  }
   if (lo < min_per) lo = min_per;
   if (hi < lo) hi = lo;   // pieces() only falls as per grows
-  // Bisection for the smallest fitting count in [lo, hi]. Its first two probes
-  // sit where the answer usually is: at the count that fits if every unit's
-  // last piece is half full (total / (target - units / 2)), then next to it on
-  // the side that is still open. Most searches end there instead of after
-  // log2(hi - lo) probes; the result is the same.
-  auto probe = [&](int64_t x) {
-    const bool fits = pieces((int32_t)x) <= target;
-    if (fits) hi = x;
-    else lo = x + 1;
-    return fits;
-  };
-  if (lo < hi) {
-    const int64_t half = target - ((int64_t)p.B * p.Hkv) / 2;
-    int64_t guess = (total + half - 1) / half;
-    guess = guess < lo ? lo : (guess > hi - 1 ? hi - 1 : guess);
-    const bool fits = probe(guess);
-    if (lo < hi) probe(fits ? hi - 1 : lo);
+  // Search for the smallest fitting count in [lo, hi]. Each pass counts the
+  // pieces (sum over units of ceil(n / x)) for kCand candidates x at once,
+  // their divisions and wavefront sums side by side. pieces() only falls as
+  // x grows, so each candidate moves lo or hi. The first pass tries the
+  // counts around the one that fits if every unit's last piece is half full
+  // (total / (target - units / 2)), which usually holds the answer; later
+  // ones spread the candidates evenly over [lo, hi). B <= kMaxPieceSeqs
+  // keeps every count far below 2^31.
+  constexpr int kCand = 8;
+  const int32_t guess = (int32_t)fmin(totd * recip((double)(target - units / 2)) + 1.0, 1073741824.0);
+  for (bool first = true; lo < hi; first = false) {
+    int32_t xs[kCand], cnt[kCand];
+    CeilDiv dv[kCand];
+#pragma unroll
+    for (int c = 0; c < kCand; ++c) {
+      const int32_t x = first ? guess - kCand / 2 + c : lo + (int32_t)((int64_t)(hi - lo) * (c + 1) / (kCand + 1));
+      xs[c] = x < lo ? lo : (x > hi - 1 ? hi - 1 : x);
+      dv[c] = ceil_div_by(xs[c]);
+      cnt[c] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      if (i < nch) {
+#pragma unroll
+        for (int c = 0; c < kCand; ++c) cnt[c] += ceil_div(nbd[i], dv[c]);
+      }
+    wave_sums(cnt);
+#pragma unroll
+    for (int c = 0; c < kCand; ++c) {
+      if ((int64_t)cnt[c] * p.Hkv <= target) hi = xs[c] < hi ? xs[c] : hi;
+      else lo = xs[c] + 1 > lo ? xs[c] + 1 : lo;
+    }
   }
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    probe(mid);
-  }
-  const int32_t per = (int32_t)lo;
+  const int32_t per = lo;
+  const CeilDiv by_per = ceil_div_by(per);
   if (!by_size) {
     if (lane == 0) kp[0] = 0;
     int32_t carry = 0;
-    for (int32_t base = 0; base < p.B; base += 64) {
-      const int32_t b = base + lane;
-      const int32_t v = wave_scan_incl(b < p.B ? (nbs[b] + per - 1) / per * p.Hkv : 0);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      if (i >= nch) break;
+      const int32_t b = i * 64 + lane;
+      const int32_t v = wave_scan_incl(ceil_div(nbd[i], by_per) * p.Hkv);
       if (b < p.B) {
         ord[b] = b;
         kp[b + 1] = carry + v;
@@ -317,58 +418,62 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
     }
     return;
   }
-  // Class and piece count of each of this lane's sequences (per and c_b are
-  // below 2^27, so 8 * per fits). Class >= j exactly when 8c <= (8 - j) per.
+  // Class of each sequence (per and c_b are below 2^27, so 8 * per fits):
+  // class >= j exactly when 8c <= (8 - j) per. Its rank inside its class is
+  // the sequences of that class in earlier chunks plus those on lower lanes
+  // of its own chunk, counted in 8-bit fields (at most 64 per chunk), four
+  // classes to a word; the scans of all chunks run side by side.
   static_assert(kPieceClasses == 8, "classes are counted in 8-bit fields of two words");
-  constexpr int kChunks = kMaxPieceSeqs / 64;
-  int32_t cls[kChunks], kk[kChunks];
-  uint32_t tot_lo = 0, tot_hi = 0;   // sequences per class: 4 fields of 8 bits in each word per chunk
-  int32_t tot[kPieceClasses] = {};
+  int32_t cls[kChunks], kk[kChunks], in[2 * kChunks];
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
-    if (i * 64 >= p.B) break;
-    const int32_t b = i * 64 + lane;
-    const int32_t nb = b < p.B ? nbs[b] : 0;
-    const int32_t k = (nb + per - 1) / per;
-    const int32_t c = k > 0 ? (nb + k - 1) / k : 0;
+    cls[i] = kk[i] = in[2 * i] = in[2 * i + 1] = 0;
+    if (i >= nch) continue;
+    const int32_t k = ceil_div(nbd[i], by_per);
+    const int32_t c = k > 0 ? (nb[i] + k - 1) / k : 0;
     int32_t q = 0;
 #pragma unroll
     for (int j = 1; j < kPieceClasses; ++j) q += 8 * c <= (8 - j) * per ? 1 : 0;
+    const uint32_t one = i * 64 + lane < p.B ? 1u << (8 * (q & 3)) : 0u;
     cls[i] = q;
     kk[i] = k * p.Hkv;
-    const uint32_t one = b < p.B ? 1u << (8 * (q & 3)) : 0u;
-    tot_lo = (uint32_t)wave_sum((int32_t)(q < 4 ? one : 0u));
-    tot_hi = (uint32_t)wave_sum((int32_t)(q < 4 ? 0u : one));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tot[j] += (tot_lo >> (8 * j)) & 0xFF;
-      tot[4 + j] += (tot_hi >> (8 * j)) & 0xFF;
-    }
+    in[2 * i] = (int32_t)(q < 4 ? one : 0u);
+    in[2 * i + 1] = (int32_t)(q < 4 ? 0u : one);
   }
-  // Rank of each sequence: its class's start, the sequences of its class in
-  // earlier chunks, and those on lower lanes of its own chunk.
-  int32_t off[kPieceClasses];
-  off[0] = 0;
-#pragma unroll
-  for (int j = 1; j < kPieceClasses; ++j) off[j] = off[j - 1] + tot[j - 1];
+  wave_scans(in);
+  // Class starts (sequences per class: the fields of every chunk's last lane).
+  int32_t off[kPieceClasses] = {};
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
-    if (i * 64 >= p.B) break;
+    if (i >= nch) break;
+    const uint32_t ch_lo = (uint32_t)__builtin_amdgcn_readlane(in[2 * i], 63);
+    const uint32_t ch_hi = (uint32_t)__builtin_amdgcn_readlane(in[2 * i + 1], 63);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      off[j + 1] += (ch_lo >> (8 * j)) & 0xFF;
+      if (j < 3) off[j + 5] += (ch_hi >> (8 * j)) & 0xFF;
+    }
+  }
+#pragma unroll
+  for (int j = 1; j < kPieceClasses; ++j) off[j] += off[j - 1];
+  // Each sequence to its rank, its piece count beside it (summed in place
+  // below); off[] advances past each chunk's members of every class.
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (i >= nch) break;
     const int32_t b = i * 64 + lane;
     const int32_t q = cls[i];
-    const uint32_t one = b < p.B ? 1u << (8 * (q & 3)) : 0u;
-    const uint32_t in_lo = (uint32_t)wave_scan_incl((int32_t)(q < 4 ? one : 0u));
-    const uint32_t in_hi = (uint32_t)wave_scan_incl((int32_t)(q < 4 ? 0u : one));
-    const int32_t before = (int32_t)(((q < 4 ? in_lo : in_hi) >> (8 * (q & 3))) & 0xFF) - 1;
     int32_t start = off[0];
 #pragma unroll
     for (int j = 1; j < kPieceClasses; ++j) start = q == j ? off[j] : start;
+    const uint32_t w = (uint32_t)(q < 4 ? in[2 * i] : in[2 * i + 1]);
+    const int32_t r = start + (int32_t)((w >> (8 * (q & 3))) & 0xFF) - 1;
     if (b < p.B) {
-      ord[start + before] = b;
-      kp[start + before + 1] = kk[i];   // piece counts by rank, summed in place below
+      ord[r] = b;
+      kp[r + 1] = kk[i];
     }
-    const uint32_t ch_lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)in_lo, 63);
-    const uint32_t ch_hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)in_hi, 63);
+    const uint32_t ch_lo = (uint32_t)__builtin_amdgcn_readlane(in[2 * i], 63);
+    const uint32_t ch_hi = (uint32_t)__builtin_amdgcn_readlane(in[2 * i + 1], 63);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       off[j] += (ch_lo >> (8 * j)) & 0xFF;
@@ -379,12 +484,17 @@ __device__ __forceinline__ void piece_prefix(const P& p, int32_t* nbs, int32_t* 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int32_t v[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) v[i] = i < nch && i * 64 + lane < p.B ? kp[i * 64 + lane + 1] : 0;
+  wave_scans(v);
   int32_t carry = 0;
-  for (int32_t base = 0; base < p.B; base += 64) {
-    const int32_t r = base + lane;
-    const int32_t v = wave_scan_incl(r < p.B ? kp[r + 1] : 0);   // each lane rewrites only what it read
-    if (r < p.B) kp[r + 1] = carry + v;
-    carry += __builtin_amdgcn_readlane(v, 63);
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    if (i >= nch) break;
+    const int32_t r = i * 64 + lane;
+    if (r < p.B) kp[r + 1] = carry + v[i];   // each lane rewrites only what it read
+    carry += __builtin_amdgcn_readlane(v[i], 63);
   }
   if (lane == 0) kp[0] = 0;
 }
