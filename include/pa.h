@@ -94,6 +94,10 @@ typedef struct {
                                  (the plan then keeps at least two pieces per unit; an explicit count
                                  at least one) */
   int32_t oversub;            /* list / piece partitions: workgroups per resident slot, 1..64; 0 auto */
+  int32_t segment_blocks;     /* list partition: what one more segment (a unit a workgroup's share
+                                 starts in or crosses into) costs, in blocks of streaming: each
+                                 unit counts as its blocks plus this many; 1..4096, -1 none (equal
+                                 blocks per workgroup), 0 auto */
 } pa_tuning;
 
 typedef struct {
@@ -174,6 +178,7 @@ typedef struct {
                                  or (queue != 0) handed out to the workgroups in turn */
   int32_t pieces;             /* partition 2: most pieces the partition can produce */
   int32_t queue;              /* partition 2: 1 if pieces go out through the workspace queue */
+  int32_t segment_blocks;     /* partition 1: blocks each unit is charged beyond its own (0: none) */
   size_t workspace_bytes;     /* == pa_workspace_size() */
 } pa_plan_info;
 

@@ -8,7 +8,7 @@ stream the kernels are launched on, so its zero-fill is ordered before them
 and the block is not handed out again before they finish.
 
 ``tuning`` (decode / verify / plan): a dict of pa_tuning fields (waves,
-blocks_per_wave, partition, pieces_per_wg, oversub) overriding the launch
+blocks_per_wave, partition, pieces_per_wg, oversub, segment_blocks) overriding the launch
 plan for tests and experiments; ``partition`` takes "aligned", "list",
 "pieces" or "queue".
 

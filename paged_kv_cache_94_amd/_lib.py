@@ -34,6 +34,7 @@ class PaTuning(ctypes.Structure):
         ("partition", ctypes.c_int32),
         ("pieces_per_wg", ctypes.c_int32),
         ("oversub", ctypes.c_int32),
+        ("segment_blocks", ctypes.c_int32),
     ]
 
 
@@ -84,6 +85,7 @@ class PaPlanInfo(ctypes.Structure):
         ("balanced", ctypes.c_int32),
         ("pieces", ctypes.c_int32),
         ("queue", ctypes.c_int32),
+        ("segment_blocks", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

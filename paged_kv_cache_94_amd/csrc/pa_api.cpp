@@ -48,6 +48,7 @@ struct Plan {
   int nwg = 0;
   int64_t pieces = 0;   // piece partition: pieces aimed for
   bool queue = false;   // piece partition: pieces handed out through the workspace queue
+  int seg_blocks = 0;   // list partition: blocks each unit is charged beyond its own
   int64_t slots = 0;    // workspace partial slots
   int64_t grid = 0;
   size_t ws_bytes = 0;
@@ -111,7 +112,7 @@ int validate(const pa_args* a, Entry entry) {
 int make_plan(const pa_args* a, Plan* pl) {
   const int G = a->num_q_heads / a->num_kv_heads;
   const int D = a->head_dim;
-  static const pa_tuning kNoTuning = {0, 0, PA_PART_AUTO, 0, 0};
+  static const pa_tuning kNoTuning = {0, 0, PA_PART_AUTO, 0, 0, 0};
   const pa_tuning& tu = a->tuning ? *a->tuning : kNoTuning;
   Plan P;
   P.rows = G * a->q_len;
@@ -147,6 +148,8 @@ int make_plan(const pa_args* a, Plan* pl) {
     return fail(PA_ERR_INVALID_ARG, "num_splits asks for aligned splits; tuning.partition asks otherwise");
   if (tu.pieces_per_wg < 0 || tu.pieces_per_wg > 64 || tu.oversub < 0 || tu.oversub > 64)
     return fail(PA_ERR_INVALID_ARG, "tuning.pieces_per_wg and tuning.oversub must be 0..64");
+  if (tu.segment_blocks < -1 || tu.segment_blocks > 4096)
+    return fail(PA_ERR_INVALID_ARG, "tuning.segment_blocks must be -1..4096 (got %d)", tu.segment_blocks);
   const bool nw_forced = tu.waves != 0;
   if (nw_forced) P.nw = tu.waves;
 
@@ -256,6 +259,21 @@ int make_plan(const pa_args* a, Plan* pl) {
       P.queue = false;
       P.pieces = 0;
       P.slots = P.nwg + units;
+      // Equal blocks per workgroup leave the workgroups whose share crosses
+      // more unit boundaries behind: each segment costs a start and a merge,
+      // measured at ~3.5 + 1.2 us on MI355X (int8 GQA layer, 512 workgroups).
+      // Each unit is therefore charged, besides its blocks, the blocks a
+      // workgroup streams in that time at its share of ~6 TB/s.
+      if (tu.segment_blocks > 0) {
+        P.seg_blocks = tu.segment_blocks;
+      } else if (tu.segment_blocks == 0) {
+        const bool int8 = a->kv_dtype == PA_INT8;
+        const double row_bytes = (double)D * (int8 ? 1 : a->kv_dtype == PA_BF16 ? 2 : 4);
+        const double block_bytes = pa::kBlock * row_bytes * (a->v_pool == a->k_pool ? 1 : 2) +
+                                   (int8 ? 2.0 * pa::kBlock * sizeof(float) : 0.0);
+        const long c = std::lround(4.7e-6 * 6.0e12 / P.nwg / block_bytes);
+        P.seg_blocks = (int)std::min<long>(std::max<long>(c, 1), 4096);
+      }
     }
   }
   if (P.grid > 0x7FFFFFFF || P.pieces > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "launch too large");
@@ -297,6 +315,7 @@ pa::Params make_params(const pa_args* a, const Plan& P) {
   p.pieces = (int32_t)P.pieces;
   p.balanced = P.balanced;
   p.nwg = P.nwg;
+  p.seg_items = P.balanced == 1 ? P.seg_blocks : 0;
   p.visits = a->debug_visits;
   p.stamps = reinterpret_cast<uint64_t*>(a->debug_stamps);
   p.B = a->num_seqs;
@@ -422,6 +441,7 @@ int pa_plan(const pa_args* a, pa_plan_info* info) {
   info->balanced = P.balanced;
   info->pieces = (int32_t)P.pieces;
   info->queue = P.queue ? 1 : 0;
+  info->segment_blocks = P.balanced == 1 ? P.seg_blocks : 0;
   info->workspace_bytes = P.ws_bytes;
   return PA_OK;
 }

@@ -213,9 +213,10 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
   int32_t ns;
   if (p.balanced == 1) {
     // Boundary grp lies between workgroups grp and grp+1, at item x of the
-    // flattened list. The unit holding x is merged here if it starts inside
-    // workgroup grp (it is then cut by this boundary first); workgroups
-    // w0..w1 left its partials in slots w + unit. The block prefix sums are
+    // flattened list (a unit's p.seg_items leading items, then its blocks).
+    // The unit holding x is merged here if x cuts its blocks and they start
+    // inside workgroup grp (this boundary then cuts them first); workgroups
+    // grp..w1 left its partials in slots w + unit. The item prefix sums are
     // staged in LDS so the search below costs no memory round trips.
     __shared__ int32_t pre[kMaxBalancedSeqs + 1];
     for (int32_t i = threadIdx.x; i <= p.B; i += 64 * kCombineWaves) pre[i] = p.ws_prefix[i];
@@ -224,12 +225,12 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
     const int64_t x = (int64_t)(grp + 1) * bal.per;
     if (x >= bal.total) return;
     b = balanced_seq(pre, p.B, p.Hkv, x);
-    const int32_t nb = pre[b + 1] - pre[b];
+    const int32_t items = pre[b + 1] - pre[b];
     const int64_t base = (int64_t)p.Hkv * pre[b];
-    g = (int32_t)((x - base) / nb);
-    const int64_t off = base + (int64_t)g * nb;
-    if (off >= x || off < (int64_t)grp * bal.per) return;
-    const int64_t w1 = (off + nb - 1) / bal.per;
+    g = (int32_t)((x - base) / items);
+    const int64_t blk0 = base + (int64_t)g * items + p.seg_items;   // the unit's first block item
+    if (blk0 >= x || blk0 < (int64_t)grp * bal.per) return;
+    const int64_t w1 = (blk0 + (items - p.seg_items) - 1) / bal.per;   // the last workgroup with its blocks
     slot_first = grp + (int64_t)b * p.Hkv + g;
     ns = (int32_t)(w1 - grp + 1);
   } else {

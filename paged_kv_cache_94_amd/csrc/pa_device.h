@@ -39,6 +39,7 @@ struct Params {
   int32_t splits, bps;  // aligned mode: splits per sequence and logical blocks per split
   int32_t balanced;     // 0: aligned splits; 1: flattened-list partition; 2: piece partition
   int32_t nwg;          // modes 1 and 2: workgroups of the launch
+  int32_t seg_items;    // mode 1: items each non-empty unit counts beyond its blocks
   int32_t* ws_prefix;   // mode 1: [B+1] block prefix sums; mode 2: [B] first piece numbers, [B] piece counts (workgroup 0 writes)
   int32_t pieces;       // mode 2: pieces the partition aims for (nwg, or more when they are handed out)
   int32_t* ws_queue;    // mode 2, non-null: hand pieces out through this [2] counter pair (zero between calls)
@@ -264,10 +265,12 @@ __device__ __forceinline__ int32_t ceil_div(double n, const CeilDiv& c) {
   return (int32_t)__builtin_fma(n, c.inv, c.bias);
 }
 
-// pre[0..B] = prefix sums of seq_blocks over the batch and blo[0..B) = the
-// first logical block each sequence loads, computed by wave 0 of the
-// workgroup (64 sequences per step, DPP scan); the caller synchronises the
-// workgroup before reading them.
+// pre[0..B] = prefix sums of the list items per unit over the batch, and
+// blo[0..B) = the first logical block each sequence loads, computed by wave 0
+// of the workgroup (64 sequences per step, DPP scan); the caller synchronises
+// the workgroup before reading them. A unit of sequence b counts its n_b
+// blocks plus p.seg_items items ahead of them (none for a unit without
+// blocks): the cost of one more segment in a workgroup's share.
 template <typename P>
 __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre, int32_t* blo) {
   if (threadIdx.x >= 64) return;
@@ -277,7 +280,8 @@ __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre, int32_t* 
   for (int32_t base = 0; base < p.B; base += 64) {
     const int32_t b = base + lane;
     const int32_t L = b < p.B ? p.seq_lens[b] : 0;
-    const int32_t v = wave_scan_incl(b < p.B ? seq_blocks(L, p) : 0);
+    const int32_t nb = b < p.B ? seq_blocks(L, p) : 0;
+    const int32_t v = wave_scan_incl(nb > 0 ? nb + p.seg_items : 0);
     if (b < p.B) {
       pre[b + 1] = carry + v;
       blo[b] = key_range(L, p.q_len, p.window).blk_lo;

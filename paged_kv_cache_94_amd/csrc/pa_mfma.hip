@@ -715,9 +715,13 @@ pa_mfma_kernel(const Params p) {
     return done();
   }
   if constexpr (MODE == 1) {
-    // Flattened-list partition: this workgroup's slice of the flattened (unit, block)
-    // list, cut at unit boundaries into segments. A segment holding a whole
-    // unit writes the output directly; the others leave a partial in slot
+    // Flattened-list partition: this workgroup's slice of the flattened
+    // (unit, item) list, cut at unit boundaries into segments. A unit's items
+    // are p.seg_items leading ones, which stand for the cost of a segment
+    // start and merge and load nothing, then its blocks; equal slices then
+    // balance blocks plus segments. A slice's part of a unit that holds none
+    // of its blocks is no segment. A segment holding all of a unit's blocks
+    // writes the output directly; the others leave a partial in slot
     // (workgroup + unit), which is unique because both indices only grow
     // along the list. Each sequence's first loaded block sits in LDS next to
     // the prefix sums, so the next segment's table entries are loaded while a
@@ -733,48 +737,57 @@ pa_mfma_kernel(const Params p) {
     const int64_t x0 = (int64_t)blockIdx.x * bal.per;
     const int64_t hi = min(bal.total, x0 + bal.per);
     if (x0 >= hi) return done();
-    // The segment starting at item x: unit (b, g), its first item `off`, and
-    // the logical blocks [first, last] it covers.
+    // The slice's part of the unit holding item x (from x on): unit (b, g),
+    // the logical blocks [first, last] it covers (last < first: none), the
+    // item after it, and whether it holds all of the unit's blocks.
     struct Seg {
       int32_t b, g, first, last;
-      int64_t off, end;
+      int64_t end;
+      bool whole;
     };
     auto segment_at = [&](int64_t x) __attribute__((always_inline)) {
       Seg sg;
       sg.b = balanced_seq(pre, p.B, p.Hkv, x);
-      const int32_t nb = pre[sg.b + 1] - pre[sg.b];
+      const int32_t items = pre[sg.b + 1] - pre[sg.b];   // >= 1: x lies in this sequence's units
       const int64_t base = (int64_t)p.Hkv * pre[sg.b];
-      sg.g = (int32_t)((x - base) / nb);
-      sg.off = base + (int64_t)sg.g * nb;
-      sg.end = min(hi, sg.off + nb);
-      sg.first = blo[sg.b] + (int32_t)(x - sg.off);
-      sg.last = blo[sg.b] + (int32_t)(sg.end - sg.off) - 1;
+      sg.g = (int32_t)((x - base) / items);
+      const int64_t off = base + (int64_t)sg.g * items;
+      sg.end = min(hi, off + items);
+      const int32_t b0 = max((int32_t)(x - off) - p.seg_items, 0);
+      const int32_t b1 = (int32_t)(sg.end - off) - p.seg_items;   // past the last block (<= b0: none)
+      sg.first = blo[sg.b] + b0;
+      sg.last = blo[sg.b] + b1 - 1;
+      sg.whole = b0 == 0 && b1 == items - p.seg_items;
       return sg;
     };
-    int64_t x = x0;
-    Seg cur = segment_at(x);
+    // Only a slice that lies within a unit's leading items can begin without
+    // blocks, and then it holds none at all.
+    Seg cur = segment_at(x0);
+    if (cur.last < cur.first) return done();
     int32_t tbl0 = settle(chunk_table<NW>(p, cur.b, cur.first, cur.last));
     while (true) {
       // The next segment's first table chunk loads while this one streams.
+      // Only the slice's last part of a unit can hold no blocks.
       const bool more = cur.end < hi;
+      Seg nxs{};
       int32_t tbln = 0;
       auto next = [&]() __attribute__((always_inline)) {
         NextSeg nx;
         if (more) {
-          const Seg sg = segment_at(cur.end);
-          nx.tbl = chunk_table<NW>(p, sg.b, sg.first, sg.last);
-          nx.g = sg.g;
+          nxs = segment_at(cur.end);
+          if (nxs.last >= nxs.first) {
+            nx.tbl = chunk_table<NW>(p, nxs.b, nxs.first, nxs.last);
+            nx.g = nxs.g;
+          }
         }
         return nx;
       };
-      const bool whole = x == cur.off && cur.end == cur.off + (pre[cur.b + 1] - pre[cur.b]);
-      const int64_t slot = whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
+      const int64_t slot = cur.whole ? -1 : (int64_t)blockIdx.x + (int64_t)cur.b * p.Hkv + cur.g;
       int32_t none_c = 0;
       mfma_segment<INT8, ALIAS, D, MT, NW>(p, smem, cur.b, cur.g, cur.first, cur.last, slot, tbl0, tbln, none_c,
                                            nullptr, seg, touch, next);
-      if (!more) break;
-      x = cur.end;
-      cur = segment_at(x);
+      if (!more || nxs.last < nxs.first) break;
+      cur = nxs;
       tbl0 = tbln;
     }
     return done();

@@ -325,6 +325,8 @@ def test_tuning_waves_and_rejections(lib):
         (dict(pieces_per_wg=65), _lib.PA_ERR_INVALID_ARG),
         (dict(oversub=-1), _lib.PA_ERR_INVALID_ARG),
         (dict(blocks_per_wave=-2), _lib.PA_ERR_INVALID_ARG),
+        (dict(segment_blocks=-2), _lib.PA_ERR_INVALID_ARG),
+        (dict(segment_blocks=4097), _lib.PA_ERR_INVALID_ARG),
     ]:
         assert lib.pa_plan(ctypes.byref(_tuned(_args(**C3_LIKE), **fields)), ctypes.byref(info)) == code, fields
     # The vector kernel (2 rows per KV head) has only aligned splits, and only 4 or 8 waves.
@@ -375,6 +377,26 @@ def test_build_id_matches_sources_and_stale_copies_are_refused(lib, tmp_path):
         f.write("\n// edited\n")
     with pytest.raises(RuntimeError, match="built from other sources"):
         _lib.check_build_id(lib, root=str(tmp_path))
+
+
+def test_list_partition_charges_each_segment(lib):
+    """The flattened list charges every unit, besides its blocks, the blocks a
+    segment start and merge cost: by default ~4.7 us of a workgroup's share of
+    ~6 TB/s in blocks of this cache (13 for 128-dim int8 rows at 512
+    workgroups, 7 for 128-dim bf16 K and V), the tuning's count, or nothing
+    (-1). The other partitions charge nothing."""
+    int8 = dict(num_seqs=64, num_q_heads=64, num_kv_heads=8, head_dim=128, kv_dtype=_lib.PA_INT8, window=0,
+                max_seq_len=4096, max_blocks_per_seq=256, v_pool=16, k_scale=8, v_scale=24)
+    bf16 = dict(int8, kv_dtype=_lib.PA_BF16, k_scale=0, v_scale=0)
+    info = _lib.PaPlanInfo()
+    for args, tuning, want in [
+        (int8, {}, 13), (bf16, {}, 7), (int8, dict(segment_blocks=-1), 0), (int8, dict(segment_blocks=40), 40),
+    ]:
+        a = _tuned(_args(**args), partition=_lib.PA_PART_LIST, **tuning)
+        assert lib.pa_plan(ctypes.byref(a), ctypes.byref(info)) == 0, lib.pa_last_error()
+        assert info.balanced == 1 and info.grid == 512 and info.segment_blocks == want, (args, tuning)
+    a = _tuned(_args(**int8), partition=_lib.PA_PART_QUEUE, segment_blocks=40)
+    assert lib.pa_plan(ctypes.byref(a), ctypes.byref(info)) == 0 and info.segment_blocks == 0
 
 
 def test_noalloc_entry_rules(lib):

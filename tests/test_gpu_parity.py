@@ -214,6 +214,42 @@ def test_queue_size_order_with_empty_sequences():
     np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
 
 
+@pytest.mark.parametrize("seg", [-1, 1, 13, 200])
+def test_list_partition_segment_charges(seg):
+    """The flattened list charges each unit seg blocks beyond its own (-1:
+    none). 40 sequences on 8 KV heads are 320 units for 512 workgroups, so
+    a slice is about 0.6 units: at 13 and 200 many slices lie within a
+    unit's leading items and hold no blocks, and others end in the next
+    unit's leading items. Lengths of 1-15 blocks; four sequences get a
+    length below q_len on the device (units with no blocks, charged
+    nothing). int8 and bf16 caches. Every block is visited once and the
+    outputs match the oracle."""
+    rng = np.random.default_rng(zlib.crc32(b"list-segments") + seg)
+    lens = rng.integers(3, 240, 40)
+    empty = rng.choice(40, 4, replace=False)
+    for kvd in ("int8", "bf16"):
+        x = make_inputs(lens.tolist(), q_len=3, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                        kv_dtype=kvd, poison=True, seed=seg + 7)
+        dev = Dev(x)
+        dev_lens = x.seq_lens.astype(np.int32).copy()
+        dev_lens[empty] = 2
+        dev.lens = torch.from_numpy(dev_lens).cuda()
+        tuning = {"partition": "list", "segment_blocks": seg}
+        plan = dev.plan(tuning=tuning)
+        _log(f"list segment_blocks={seg} {kvd}: plan {plan}")
+        assert plan["kernel"] == 1 and plan["balanced"] == 1 and plan["segment_blocks"] == max(seg, 0)
+        got = dev.run_f64(tuning=tuning)
+        keep = np.ones(x.batch, dtype=bool)
+        keep[empty] = False
+        assert not np.isnan(got[keep]).any()
+        assert max_err(got[keep], _oracle(x)[keep]) <= TOL[kvd]
+        visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
+        dev.run(debug_visits=visits, tuning=tuning)
+        expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
+        expect[empty] = 0
+        np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
+
+
 # --- invariants on the GPU path -------------------------------------------------------------------
 
 def test_block_permutation_is_bit_identical():
