@@ -109,7 +109,10 @@ typedef struct {
                                  KV head), a block's 16 scales of one head contiguous; or [Hkv],
                                  one per KV head, when scale_per_head is 1; else NULL */
   const float* v_scale;       /* int8 cache only: same shape; else NULL. When v_pool == k_pool the
-                                 values are the keys, so v_scale must equal k_scale */
+                                 values are the keys, so v_scale must equal k_scale. With separate
+                                 pools every V scale a step reads must be below 255 in magnitude:
+                                 each weight (at most 2^8) times its value scale reaches the matrix
+                                 cores as one f16 value (pa_validate flags larger ones) */
   const int32_t* block_table; /* [B][max_blocks_per_seq] physical block ids; with ring_blocks > 0 each
                                  row's first ring_blocks entries form the sequence's ring */
   const int32_t* seq_lens;    /* [B] cached tokens per sequence, this step's q_len tokens included */
@@ -205,7 +208,8 @@ int pa_decode(const pa_args* args, pa_stream_t stream);
  * Single-token decode step (q_len must be 1) over an int8 cache with
  * per-token, per-KV-head fp32 scales (tiniestgpt notes, KV cache
  * quantization: gather the int8 codes, then dequantize). q_dtype must be
- * PA_BF16, kv_dtype PA_INT8, and k_scale / v_scale non-NULL.
+ * PA_BF16, kv_dtype PA_INT8, and k_scale / v_scale non-NULL; with separate
+ * K and V pools the value scales must stay below 255 (see v_scale).
  */
 int pa_decode_int8(const pa_args* args, pa_stream_t stream);
 
@@ -257,8 +261,9 @@ enum {
   PA_BAD_LEN_LONG = 2,  /* seq_len > max_seq_len, or (linear table) > max_blocks_per_seq * block_size */
   PA_BAD_BLOCK = 4,     /* a table entry the step would read is outside [0, num_blocks) */
   PA_BAD_SCALE = 8,     /* int8: a K or V scale of a key the step sees is NaN or infinite */
-  PA_BIG_V_SCALE = 16,  /* int8: a V scale of a key the step sees is 255 or more in magnitude; decode
-                           takes it, pa_prefill does not (see its v_scale) */
+  PA_BIG_V_SCALE = 16,  /* int8: a V scale of a key the step sees is 255 or more in magnitude; only
+                           decode over a shared K/V pool takes it (see pa_args.v_scale and
+                           pa_prefill's v_scale) */
   PA_BAD_WORKSPACE = 32 /* (entry 0 only) the call would hand pieces out through the workspace queue
                            and the queue's counters in the workspace header are not zero */
 };

@@ -16,6 +16,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -698,6 +699,25 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16(uint32_t w, int byte0) {
 __device__ __forceinline__ void i8x16_to_bf16(const uint4& w, uint4& lo, uint4& hi) {
   lo = make_uint4(i8pair_to_bf16(w.x, 0), i8pair_to_bf16(w.x, 2), i8pair_to_bf16(w.y, 0), i8pair_to_bf16(w.y, 2));
   hi = make_uint4(i8pair_to_bf16(w.z, 0), i8pair_to_bf16(w.z, 2), i8pair_to_bf16(w.w, 0), i8pair_to_bf16(w.w, 2));
+}
+
+// 16 int8 codes as 16 f16 values, exactly: with the sign bit flipped a code
+// c reads as the unsigned byte c + 128; placed under the high byte 0x64 (the
+// f16 pattern of 1024, whose spacing is 1) it reads as 1024 + c + 128, and a
+// packed f16 subtraction of 1152 leaves c (every value is an integer below
+// 2048, so nothing rounds). Five instructions per four codes.
+typedef _Float16 f16x2h __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t i8pair_to_f16(uint32_t flipped, uint32_t sel) {
+  const uint32_t bits = __builtin_amdgcn_perm(flipped, 0x64646464u, sel);
+  const f16x2h v = __builtin_bit_cast(f16x2h, bits) - f16x2h{(_Float16)1152.f, (_Float16)1152.f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void i8x16_to_f16_exact(const uint4& w, uint4& lo, uint4& hi) {
+  // v_perm_b32 selectors: bytes 4..7 are the codes, bytes 0..3 the constant 0x64.
+  constexpr uint32_t kLow = 0x00050004u, kHigh = 0x00070006u;
+  const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u, x2 = w.z ^ 0x80808080u, x3 = w.w ^ 0x80808080u;
+  lo = make_uint4(i8pair_to_f16(x0, kLow), i8pair_to_f16(x0, kHigh), i8pair_to_f16(x1, kLow), i8pair_to_f16(x1, kHigh));
+  hi = make_uint4(i8pair_to_f16(x2, kLow), i8pair_to_f16(x2, kHigh), i8pair_to_f16(x3, kLow), i8pair_to_f16(x3, kHigh));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));

@@ -139,6 +139,10 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   constexpr int LPR = ROW_BYTES / 16;
   constexpr int RPI = 64 / LPR;
   constexpr int NLOAD = kBlock / RPI;
+  // int8 caches with separate K and V stage the values as f16 and weigh them
+  // with one f16 weight per key (a shared K/V tile serves as bf16 K, so it
+  // keeps the bf16 weights of the other caches).
+  constexpr bool F16V = INT8 && !ALIAS;
   // Cache rows are read once per step: the non-temporal hint keeps them from
   // displacing anything in L2 (measured 5% faster on 128-byte int8 rows too).
   constexpr int CPOL = kCacheNonTemporal;
@@ -261,11 +265,13 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   };
 
   // Write one loaded piece (row r, 16 bytes at byte 16*ld_chunk of the cached
-  // row) into a staging tile as bf16; int8 codes widen to 32 bytes.
-  auto stage = [&](char* dst_tile, int r, const uint4& w) __attribute__((always_inline)) {
+  // row) into a staging tile as bf16; int8 codes widen to 32 bytes, as f16
+  // for a V tile of the f16-value path.
+  auto stage = [&](char* dst_tile, int r, const uint4& w, bool as_f16) __attribute__((always_inline)) {
     if constexpr (INT8) {
       uint4 lo, hi;
-      i8x16_to_bf16(w, lo, hi);
+      if (F16V && as_f16) i8x16_to_f16_exact(w, lo, hi);
+      else i8x16_to_bf16(w, lo, hi);
       char* dst = dst_tile + r * RS + 32 * ld_chunk;
       *reinterpret_cast<uint4*>(dst) = lo;
       *reinterpret_cast<uint4*>(dst + 16) = hi;
@@ -295,8 +301,8 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
         w.z = v_ok ? w.z : 0u;
         w.w = v_ok ? w.w : 0u;
       }
-      stage(vst, r, w);
-      if constexpr (!ALIAS) stage(kst, r, f.k[u]);
+      stage(vst, r, w, true);
+      if constexpr (!ALIAS) stage(kst, r, f.k[u], false);
     }
     if constexpr (INT8) {
       if (lane < 32) sst[lane] = lane < 16 ? f.ks : f.vs;
@@ -320,8 +326,13 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       vsc[0] = v.x; vsc[1] = v.y; vsc[2] = v.z; vsc[3] = v.w;
     }
 
-    // Scores and softmax for every row tile; P leaves as hi/lo bf16 parts.
+    // Scores and softmax for every row tile; P leaves as hi/lo bf16 parts, or
+    // (f16 values) as one f16 weight per key times its value scale, rounded
+    // to nearest: 11 significant bits, so O moves by at most 2^-12 of the
+    // weighted |V| sum; a weight stays below 2^kRescaleSlack, so with value
+    // scales below 255 it stays in f16 range.
     bf16x8 pbv[MT];
+    f16x4 pbh[MT];
 #pragma unroll
     for (int tile = 0; tile < MT; ++tile) {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -365,6 +376,10 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
           pe[e] *= vis ? vsc[e] : 0.f;
         }
       }
+      if constexpr (F16V) {
+        pbh[tile] = f16x4{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3]};
+        continue;
+      }
       // P as hi + lo bf16 parts for the 32-deep PV contraction.
       float lo[4];
 #pragma unroll
@@ -378,10 +393,19 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const uint2 a = lds_read_tr16(vread + 32 * j);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, a.x, a.y));
+      if constexpr (F16V) {
+        // One 16-deep product: lane l holds V^T for dim n, keys 4*q4 .. +3,
+        // against its own four weights.
+        const f16x4 av = __builtin_bit_cast(f16x4, a);
 #pragma unroll
-      for (int tile = 0; tile < MT; ++tile)
-        o[tile][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv[tile], o[tile][j], 0, 0, 0);
+        for (int tile = 0; tile < MT; ++tile)
+          o[tile][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pbh[tile], o[tile][j], 0, 0, 0);
+      } else {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, a.x, a.y));
+#pragma unroll
+        for (int tile = 0; tile < MT; ++tile)
+          o[tile][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv[tile], o[tile][j], 0, 0, 0);
+      }
     }
   };
 

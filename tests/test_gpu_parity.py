@@ -250,6 +250,28 @@ def test_list_partition_segment_charges(seg):
         np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
 
 
+@pytest.mark.parametrize("head_scales", [False, True])
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_int8_large_value_scales(head_scales, q_len):
+    """With separate K and V caches the int8 path hands each weight to the
+    matrix cores as one f16 product (weight <= 2^8) x (value scale). Value
+    scales up to 200 (dequantized values up to ~25400, products up to 51200)
+    stay inside f16 range; the bar scales with the values (plus the bf16
+    output's own rounding)."""
+    rng = np.random.default_rng(zlib.crc32(b"int8-big-v") + 2 * q_len + head_scales)
+    lens = rng.integers(q_len, 700, 24).tolist()
+    x = make_inputs(lens, q_len=q_len, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                    kv_dtype="int8", head_scales=head_scales, poison=True, seed=91 + q_len)
+    f = 200.0 / float(np.nanmax(np.abs(np.where(np.isfinite(x.v_scale), x.v_scale, 0.0))))
+    x.v_scale[...] = x.v_scale * np.float32(f)
+    _log(f"int8 value scales x{f:.0f}, q_len={q_len}, head_scales={head_scales}")
+    got = Dev(x).run_f64()
+    ref = _oracle(x)
+    assert np.isfinite(got).all()
+    bar = TOL["int8"] * f + np.abs(ref) * 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= bar), float(np.max(np.abs(got - ref) - bar))
+
+
 # --- invariants on the GPU path -------------------------------------------------------------------
 
 def test_block_permutation_is_bit_identical():
