@@ -189,12 +189,12 @@ int make_plan(const pa_args* a, Plan* pl) {
 
   // The matrix-core kernel defaults to a work-balanced partition over as
   // many workgroups as are resident at once (two per compute unit at 4
-  // waves, one at 8). With few units (sequence, KV head) -- long contexts on
-  // one or two KV heads -- units are cut on the device into near-equal
-  // pieces, one per workgroup. With many, pieces are handed out to the
-  // workgroups through a sharded queue in the workspace. In between, and for
-  // batches beyond the piece partition's LDS tables, each workgroup takes an
-  // equal share of the flattened (unit, block) list. Forced splits and the
+  // waves, one at 8). With many units (sequence, KV head), units are cut on
+  // the device into near-equal pieces handed out to the workgroups through a
+  // sharded queue in the workspace. Otherwise, and for batches beyond the
+  // piece partition's LDS tables, each workgroup takes an equal share of the
+  // flattened (unit, block) list, each unit charged a segment's cost. One
+  // piece per workgroup is available on request. Forced splits and the
   // vector kernel keep the aligned splits.
   const int part = tu.partition;
   const bool balanced = P.kernel == 1 && a->num_splits == 0 && part != PA_PART_ALIGNED;
@@ -203,18 +203,20 @@ int make_plan(const pa_args* a, Plan* pl) {
       return fail(PA_ERR_UNSUPPORTED, "the balanced partitions take at most %d sequences at %d waves",
                   pa::balanced_seq_limit(P.nw), P.nw);
   } else if (balanced) {
-    // Few units (at most one per two CUs) are cut into one piece per
-    // workgroup: one 8-wave workgroup per CU streams them as fast as two of
-    // 4 waves and leaves half the partials to merge (16 sequences of 4K-32K
-    // tokens on one KV head: kernel 29.4 vs 29.2 us, step 34.9 vs 37.0 us).
+    // Few units (at most one per two CUs): one 8-wave workgroup per CU
+    // streams them as fast as two of 4 waves and leaves half the partials to
+    // merge (16 sequences of 4K-32K tokens on one KV head: kernel 29.4 vs
+    // 29.2 us, step 34.9 vs 37.0 us).
     if (!nw_forced && 2 * units <= (int64_t)cu_count()) P.nw = 8;
     P.nwg = cu_count() * (8 / P.nw);   // as many workgroups as are resident at once (2 wavefronts per SIMD)
     if (tu.oversub > 0) P.nwg *= tu.oversub;
-    // Measured on MI355X: one piece per workgroup is best for few units
-    // (<= nwg/2: 16 long contexts on one KV head), the flattened list for
-    // about as many units as workgroups (512 units of 1-4K tokens: 90 us vs
-    // 102 us through the queue), the queue for many (2048 units of lognormal
-    // length: 333 us vs 347 us for the flattened list).
+    // Measured on MI355X: the flattened list with segment charges for few
+    // units (16 long contexts on one KV head: kernel 27.3 vs 28.2 us for one
+    // piece per workgroup, step 33.3 vs 34.2 us; equal items per workgroup
+    // where pieces of different units differ in size) and for about as many
+    // units as workgroups (512 units of 1-4K tokens: 81 us vs 89-98 us
+    // through the queue), the queue for many (2048 units of lognormal
+    // length: 306 us vs 310 us for the flattened list).
     const bool few = 2 * units <= P.nwg;
     const bool many = units >= 2 * (int64_t)P.nwg;
     const bool pieces_ok = a->num_seqs <= pa::kMaxPieceSeqs && P.nw >= 4;
@@ -239,9 +241,8 @@ int make_plan(const pa_args* a, Plan* pl) {
         pieces = queue = true;
         break;
       default:
-        pieces = pieces_ok && (few || many);
-        queue = !few && queue_ok;
-        if (pieces && !few && !queue) pieces = false;   // (a device too small for the queue)
+        pieces = pieces_ok && many && queue_ok;
+        queue = pieces;
         break;
     }
     P.balanced = pieces ? 2 : 1;

@@ -165,9 +165,10 @@ def test_plan_choices(lib):
     # Global layer: 16 query heads on one KV head go to the matrix cores.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=16, num_kv_heads=1, window=0, max_seq_len=32768,
                                           max_blocks_per_seq=2048)), ctypes.byref(info)) == 0
-    # Few long units: each workgroup owns one piece of one unit (no queue), one 8-wave workgroup per CU.
-    assert info.kernel == 1 and info.rows == 16 and info.balanced == 2 and info.waves_per_group == 8
-    assert info.queue == 0 and info.pieces == info.grid
+    # Few long units: the flattened list, each unit charged 13 blocks for a segment (8 KiB blocks
+    # of a shared K/V pool), one 8-wave workgroup per CU.
+    assert info.kernel == 1 and info.rows == 16 and info.balanced == 1 and info.waves_per_group == 8
+    assert info.queue == 0 and info.pieces == 0 and info.segment_blocks == 13
     # Verify step: 4 heads x 5 tokens = 20 rows.
     assert lib.pa_plan(ctypes.byref(_args(num_seqs=256, q_len=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
                                           window=0, max_seq_len=16384, max_blocks_per_seq=1024)),

@@ -56,10 +56,11 @@ def test_noalloc_matches_verify_on_consecutive_calls():
     o = oracle.attention(oracle.Problem.from_inputs(big), rows=rows)
     assert max_err(got.reshape(-1, big.head_dim)[rows], o.reshape(-1, big.head_dim)) <= TOL["bf16"]
 
-    # Call 2, right after on the same scratch: a smaller global-layer problem cut into one piece per workgroup.
+    # Call 2, right after on the same scratch: a smaller global-layer problem cut into one piece per
+    # workgroup (asked for through the tuning).
     small = make_inputs([3000, 700, 4100], q_len=1, num_q_heads=16, num_kv_heads=1, head_dim=256, q_dtype="bf16",
                         kv_dtype="bf16", alias_v=True, poison=True, seed=zlib.crc32(b"noalloc-small"))
-    plan2, got2, ref2 = _both(small)
+    plan2, got2, ref2 = _both(small, tuning={"partition": "pieces"})
     _log(f"call 2: plan {plan2}")
     assert plan2["balanced"] == 2 and plan2["queue"] == 0 and 0 < plan2["workspace_bytes"] < plan["workspace_bytes"]
     np.testing.assert_array_equal(got2, ref2)
