@@ -53,22 +53,6 @@ namespace pa {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));
 
-// 16 int8 codes widened to 16 f16 values (exact: |code| <= 128 fits f16's 11
-// significant bits, so the truncating pack loses nothing), in order.
-__device__ __forceinline__ void i8x16_to_f16(const uint4& w, uint4& lo, uint4& hi) {
-  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-  uint32_t r[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = (float)(int32_t)(int8_t)(x[i]), b = (float)(int32_t)(int8_t)(x[i] >> 8);
-    const float c = (float)(int32_t)(int8_t)(x[i] >> 16), d = (float)(int32_t)(int8_t)(x[i] >> 24);
-    r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-    r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(c, d));
-  }
-  lo = make_uint4(r[0], r[1], r[2], r[3]);
-  hi = make_uint4(r[4], r[5], r[6], r[7]);
-}
-
 template <bool INT8, int D>
 struct PrefillShape {
   static constexpr int NW = 4;
@@ -320,7 +304,7 @@ pa_prefill_kernel(const PrefillParams p) {
       char* dst = buf + (isv ? S::TILE : 0) + row * RS;
       if constexpr (INT8) {
         uint4 lo, hi;
-        if (isv) i8x16_to_f16(w, lo, hi);
+        if (isv) i8x16_to_f16_exact(w, lo, hi);
         else i8x16_to_bf16(w, lo, hi);
         *reinterpret_cast<uint4*>(dst + 32 * chunk) = lo;
         *reinterpret_cast<uint4*>(dst + 32 * chunk + 16) = hi;
