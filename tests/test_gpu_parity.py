@@ -133,6 +133,9 @@ PARTITION_CASES = [
     ([4096, 2000, 77, 16, 1], 1, 16, 2, 128, 0, "bf16", "bf16", False),
     ([1500, 600, 3000], 1, 64, 8, 128, 0, "bf16", "int8", False),
     ([700, 90, 2048], 5, 32, 8, 128, 40, "bf16", "bf16", False),
+    # int8 with a window and 3 query tokens: blocks every row sees whole skip
+    # the masks; the window's edge blocks and the causal last block keep them.
+    ([900, 37, 1500, 260], 3, 32, 8, 128, 100, "bf16", "int8", False),
 ]
 
 
