@@ -81,9 +81,11 @@ enum {
 enum {
   PA_PART_AUTO = 0,      /* the library's choice */
   PA_PART_ALIGNED = 1,   /* each workgroup owns one aligned split of one (sequence, KV head) */
-  PA_PART_LIST = 2,      /* matrix-core kernel: equal shares of the flattened (sequence, KV head, block) list */
+  PA_PART_LIST = 2,      /* matrix-core kernel: equal shares of the flattened (sequence, KV head, block) list,
+                            each unit charged tuning.segment_blocks blocks beyond its own */
   PA_PART_PIECES = 3,    /* matrix-core kernel: units cut into near-equal pieces, one per workgroup */
-  PA_PART_QUEUE = 4      /* matrix-core kernel: pieces handed out through the workspace queue */
+  PA_PART_QUEUE = 4      /* matrix-core kernel: pieces handed out through the workspace queue, largest
+                            first */
 };
 
 typedef struct {
@@ -176,9 +178,11 @@ typedef struct {
   int32_t grid;               /* workgroups of the attention kernel */
   int32_t balanced;           /* 0: each workgroup owns one split of one (sequence, KV head);
                                  1: every workgroup takes an equal share of the flattened
-                                 (sequence, KV head, block) list, cut where a unit ends;
+                                 (sequence, KV head, block) list, cut where a unit ends,
+                                 each unit counted segment_blocks blocks longer;
                                  2: units are cut into near-equal pieces, one per workgroup
-                                 or (queue != 0) handed out to the workgroups in turn */
+                                 or (queue != 0) handed out largest first to the workgroups
+                                 in turn */
   int32_t pieces;             /* partition 2: most pieces the partition can produce */
   int32_t queue;              /* partition 2: 1 if pieces go out through the workspace queue */
   int32_t segment_blocks;     /* partition 1: blocks each unit is charged beyond its own (0: none) */

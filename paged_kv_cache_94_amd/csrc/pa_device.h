@@ -294,10 +294,10 @@ __device__ __forceinline__ void block_prefix(const P& p, int32_t* pre, int32_t* 
 // Piece partition. Unit (b, g) with n_b blocks is cut into
 // k_b = ceil(n_b / per) pieces of ceil(n_b / k_b) blocks; `per` is the
 // smallest count for which all pieces number at most p.pieces. With
-// p.pieces == nwg each workgroup owns the piece of its own index (few units:
-// long contexts on one or two KV heads); with more, workgroups take pieces
-// from a queue until none are left, which evens out the time workgroups take
-// for the same number of blocks.
+// p.pieces == nwg each workgroup owns the piece of its own index (asked for
+// through the launch-plan tuning); with more, workgroups take pieces from a
+// queue until none are left, which evens out the time workgroups take for the
+// same number of blocks.
 //
 // With by_size, pieces are numbered largest first, so that the last ones a
 // queue hands out are the shortest and workgroups run out of work at nearly
