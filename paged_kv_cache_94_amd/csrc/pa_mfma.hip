@@ -54,15 +54,40 @@ struct MfmaLds {
   static constexpr int RSTRIDE = D * 2 + 32;
   static constexpr int TILE = 16 * RSTRIDE;
   static constexpr int WAVE_STAGE = TILE * (ALIAS ? 1 : 2) + 128;
-  static constexpr int STAGE = NW * WAVE_STAGE;
-  // Merge: output tile j belongs to wave j % NW. Every wave parks the tiles
-  // it does not own, [MT][TJ][NW-1 slots][64 lanes] float4 (1 KiB per tile,
-  // lane-ordered, so writes and reads are conflict-free), and its (m, l)
-  // per lane, [NW][MT][64] float2.
-  static constexpr int O_BYTES = MT * TJ * (NW - 1) * 1024;
-  static constexpr int MERGE = O_BYTES + NW * MT * 64 * 8;
-  static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
+  // Merge: output tile j belongs to wave j % NW. Once its block loop is
+  // done, a wave parks in its own slot the NTO tiles it does not own,
+  // [MT][NTO][64 lanes] float4 in increasing j (1 KiB per tile, lane-ordered,
+  // so writes and reads are conflict-free), then its (m, l) per lane,
+  // [MT][64] float2.
+  static constexpr int NTO = TJ - TJ / NW;
+  static constexpr int ML_OFF = MT * NTO * 1024;
+  static constexpr int PARK = ML_OFF + MT * 64 * 8;
+  // One slot per wave holds its staging area and later its parked tiles, so
+  // a wave parks without waiting for the others to finish with their blocks.
+  static constexpr int SLOT = WAVE_STAGE > PARK ? WAVE_STAGE : PARK;
+  static constexpr int BYTES = NW * SLOT;
+  // Position of tile j among the tiles wave w parks.
+  static constexpr int park_index(int j, int w) {
+    int c = 0;
+    for (int x = 0; x < j; ++x) c += x % NW != w;
+    return c;
+  }
 };
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// f(IntC<w>{}) for the wave-uniform w == wave: one code path per wave, so a
+// wave's own tile indices are compile-time constants in f.
+template <int W, int N, typename F>
+__device__ __forceinline__ void for_this_wave(int wave, F& f) {
+  if constexpr (W < N) {
+    if (wave == W) f(IntC<W>{});
+    else for_this_wave<W + 1, N>(wave, f);
+  }
+}
 
 // Blocks a wavefront keeps in flight: as many as fit a register budget for
 // the fetch buffers (FETCH_WORDS 32-bit registers per block), at most 4.
@@ -207,7 +232,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   // MFMA operands are read back from it: K as the A operand of S^T = K Q^T
   // (lane l: token n, dims 32c + 8*q4 .. +7, one 16-byte read), V transposed
   // with ds_read_b64_tr_b16 (lane l: row 4*q4 + (n>>2), dims 16j + 4*(n&3)).
-  char* kst = smem + wave * Lds::WAVE_STAGE;
+  char* kst = smem + wave * Lds::SLOT;
   char* vst = ALIAS ? kst : kst + Lds::TILE;
   float* sst = reinterpret_cast<float*>(kst + Lds::TILE * (ALIAS ? 1 : 2));
   const char* kread = kst + n * RS + 16 * q4;
@@ -504,101 +529,112 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   stamp(p, stamp_base + 2);
   pf = settle(pf);
   pf_claim = settle(pf_claim);
-  if (claim_lds && threadIdx.x == 0) *claim_lds = pf_claim;   // read by all after the merge's barriers
+  if (claim_lds && threadIdx.x == 0) *claim_lds = pf_claim;   // read by all after the merge's barrier
 
   // Row sums: the four lanes of a row each hold a quarter of the tokens.
 #pragma unroll
   for (int tile = 0; tile < MT; ++tile) l[tile] = quads16_sum(l[tile]);
 
-  // Merge the wavefronts through LDS (reusing the staging area). Output
-  // tile j (dims 16j..16j+15) belongs to wave j % NW: every wave parks the
-  // tiles it does not own and its (m, l), then folds the other waves' copies
-  // of its own tiles into its registers with the online-softmax rule and
-  // writes them, so the fold and the stores are spread over all wavefronts.
-  // Lane l holds the same (row, dims) in every wave: the fold is per lane.
-  float4* lds_o = reinterpret_cast<float4*>(smem);
-  float2* lds_ml = reinterpret_cast<float2*>(smem + Lds::O_BYTES);
-  lds_barrier();   // every wavefront is done with its staging tile
+  // Merge the wavefronts through LDS. Output tile j (dims 16j..16j+15)
+  // belongs to wave j % NW. A wave parks the tiles it does not own and its
+  // (m, l) in its own slot as soon as its block loop is done (the slot held
+  // only its own staging area), so parking overlaps the waves still
+  // streaming. After one barrier every wave folds the other waves' copies of
+  // its own tiles into its registers with the online-softmax rule and writes
+  // them, so the fold and the stores are spread over all wavefronts. Lane l
+  // holds the same (row, dims) in every wave: the fold is per lane. Each wave
+  // runs its own copy of this code, in which its tiles are compile-time
+  // constants: the others die once parked, which leaves the registers to
+  // request all the parked copies a fold needs before the first is used.
+  auto merge_as = [&](auto wc) __attribute__((always_inline)) {
+    constexpr int W = decltype(wc)::value;
+    constexpr int OWN = (TJ + NW - 1) / NW;   // at most this many tiles per wave
+    char* mine = smem + W * Lds::SLOT;
 #pragma unroll
-  for (int tile = 0; tile < MT; ++tile) {
-    lds_ml[(wave * MT + tile) * 64 + lane] = make_float2(m[tile], l[tile]);
+    for (int tile = 0; tile < MT; ++tile) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int owner = j % NW;
-      if (owner == wave) continue;
-      const int s = wave < owner ? wave : wave - 1;
-      const f32x4 v = o[tile][j];
-      lds_o[((tile * TJ + j) * (NW - 1) + s) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+      for (int j = 0; j < TJ; ++j) {
+        if (j % NW == W) continue;
+        const f32x4 v = o[tile][j];
+        *reinterpret_cast<float4*>(mine + (tile * Lds::NTO + Lds::park_index(j, W)) * 1024 + 16 * lane) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      }
+      *reinterpret_cast<float2*>(mine + Lds::ML_OFF + (tile * 64 + lane) * 8) = make_float2(m[tile], l[tile]);
     }
-  }
-  lds_barrier();
+    lds_barrier();
 #pragma unroll
-  for (int tile = 0; tile < MT; ++tile) {
-    float2 ml[NW];
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      ml[w] = lds_ml[(w * MT + tile) * 64 + lane];
-      M = fmaxf(M, ml[w].x);
-    }
-    const float Ms = M == -INFINITY ? 0.f : M;
-    float a[NW];
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      a[w] = fast_exp2(ml[w].x - Ms);   // 0 for a wave that saw no key of this row
-      L += a[w] * ml[w].y;
-    }
-    float aself = a[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) aself = wave == w ? a[w] : aself;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      if (j % NW != wave) continue;
-      f32x4 acc = o[tile][j] * aself;
+    for (int tile = 0; tile < MT; ++tile) {
+      float2 ml[NW];
+      float4 x[OWN][NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        if (w == wave) continue;
-        const int s = w < wave ? w : w - 1;
-        const float4 x = lds_o[((tile * TJ + j) * (NW - 1) + s) * 64 + lane];
-        acc += a[w] * f32x4{x.x, x.y, x.z, x.w};
+        if (w == W) {
+          ml[w] = make_float2(m[tile], l[tile]);
+          continue;
+        }
+        const char* theirs = smem + w * Lds::SLOT;
+        ml[w] = *reinterpret_cast<const float2*>(theirs + Lds::ML_OFF + (tile * 64 + lane) * 8);
+#pragma unroll
+        for (int j = W; j < TJ; j += NW)
+          x[j / NW][w] =
+              *reinterpret_cast<const float4*>(theirs + (tile * Lds::NTO + Lds::park_index(j, w)) * 1024 + 16 * lane);
       }
-      o[tile][j] = acc;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[w].x);
+      const float Ms = M == -INFINITY ? 0.f : M;
+      float a[NW];
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        a[w] = fast_exp2(ml[w].x - Ms);   // 0 for a wave that saw no key of this row
+        L += a[w] * ml[w].y;
+      }
+#pragma unroll
+      for (int j = W; j < TJ; j += NW) {
+        f32x4 acc = o[tile][j] * a[W];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          if (w == W) continue;
+          const float4 v = x[j / NW][w];
+          acc += a[w] * f32x4{v.x, v.y, v.z, v.w};
+        }
+        o[tile][j] = acc;
+      }
+      m[tile] = M;
+      l[tile] = L;
     }
-    m[tile] = M;
-    l[tile] = L;
-  }
 
 #pragma unroll
-  for (int tile = 0; tile < MT; ++tile) {
-    const int r = n + 16 * tile;
-    if (r >= p.rows) continue;
-    const int t = r / p.G;
-    const int h = g * p.G + r % p.G;
-    if (slot >= 0) {
-      const size_t row_slot = (size_t)slot * p.rows + r;
+    for (int tile = 0; tile < MT; ++tile) {
+      const int r = n + 16 * tile;
+      if (r >= p.rows) continue;
+      const int t = r / p.G;
+      const int h = g * p.G + r % p.G;
+      if (slot >= 0) {
+        const size_t row_slot = (size_t)slot * p.rows + r;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        if (j % NW != wave) continue;
-        const f32x4 v = o[tile][j];
-        *reinterpret_cast<float4*>(p.ws_acc + row_slot * D + 16 * j + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      if (wave == 0 && q4 == 0) {
-        p.ws_ml[row_slot * 2] = m[tile];
-        p.ws_ml[row_slot * 2 + 1] = l[tile];
-      }
-    } else {
-      const float inv = 1.f / l[tile];
-      __bf16* out = reinterpret_cast<__bf16*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + 4 * q4;
+        for (int j = W; j < TJ; j += NW) {
+          const f32x4 v = o[tile][j];
+          *reinterpret_cast<float4*>(p.ws_acc + row_slot * D + 16 * j + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (W == 0 && q4 == 0) {
+          p.ws_ml[row_slot * 2] = m[tile];
+          p.ws_ml[row_slot * 2 + 1] = l[tile];
+        }
+      } else {
+        const float inv = 1.f / l[tile];
+        __bf16* out = reinterpret_cast<__bf16*>(p.out) + (((size_t)b * p.q_len + t) * p.Hq + h) * D + 4 * q4;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        if (j % NW != wave) continue;
-        const f32x4 v = o[tile][j];
-        *reinterpret_cast<uint2*>(out + 16 * j) =
-            make_uint2(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv));
+        for (int j = W; j < TJ; j += NW) {
+          const f32x4 v = o[tile][j];
+          *reinterpret_cast<uint2*>(out + 16 * j) =
+              make_uint2(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv));
+        }
       }
     }
-  }
+  };
+  for_this_wave<0, NW>(wave, merge_as);
   if (next_g >= 0) {
     constexpr int LR = (ROW_BYTES + 127) / 128;         // 128-byte lines per cached row
     constexpr int LB = kBlock * LR * (ALIAS ? 1 : 2);   // lines per block (K, and V unless aliased)
