@@ -11,11 +11,19 @@
 
 namespace pa {
 
+// Flattened-list partition: one combine workgroup per unit when there are
+// fewer units than workgroup boundaries (few long contexts), else one per
+// boundary. Either way only the units that a boundary cuts have partials.
+__host__ __device__ inline bool combine_by_unit(const Params& p) {
+  return (int64_t)p.B * p.Hkv < (int64_t)p.nwg - 1;
+}
+
 // Number of combine workgroups per output row: one per unit for aligned
-// splits and the piece partition, one per workgroup boundary for the
-// flattened-list partition (only units cut by a boundary have partials).
+// splits and the piece partition; for the flattened list, one per unit or
+// one per workgroup boundary, whichever is fewer.
 __host__ __device__ inline int64_t combine_groups(const Params& p) {
-  return p.balanced == 1 ? (int64_t)(p.nwg > 1 ? p.nwg - 1 : 0) : (int64_t)p.B * p.Hkv;
+  if (p.balanced != 1) return (int64_t)p.B * p.Hkv;
+  return combine_by_unit(p) ? (int64_t)p.B * p.Hkv : (int64_t)(p.nwg > 1 ? p.nwg - 1 : 0);
 }
 
 constexpr int kCombineWaves = 4;
@@ -212,27 +220,45 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
   int64_t slot_first;
   int32_t ns;
   if (p.balanced == 1) {
-    // Boundary grp lies between workgroups grp and grp+1, at item x of the
-    // flattened list (a unit's p.seg_items leading items, then its blocks).
-    // The unit holding x is merged here if x cuts its blocks and they start
-    // inside workgroup grp (this boundary then cuts them first); workgroups
-    // grp..w1 left its partials in slots w + unit. The item prefix sums are
-    // staged in LDS so the search below costs no memory round trips.
+    // Flattened list: a unit is its p.seg_items leading items, then its
+    // blocks. The item prefix sums are staged in LDS so the search below
+    // costs no memory round trips.
     __shared__ int32_t pre[kMaxBalancedSeqs + 1];
     for (int32_t i = threadIdx.x; i <= p.B; i += 64 * kCombineWaves) pre[i] = p.ws_prefix[i];
     __syncthreads();
     const Balanced bal = balanced_split(pre, p.B, p.Hkv, p.nwg);
-    const int64_t x = (int64_t)(grp + 1) * bal.per;
-    if (x >= bal.total) return;
-    b = balanced_seq(pre, p.B, p.Hkv, x);
-    const int32_t items = pre[b + 1] - pre[b];
-    const int64_t base = (int64_t)p.Hkv * pre[b];
-    g = (int32_t)((x - base) / items);
-    const int64_t blk0 = base + (int64_t)g * items + p.seg_items;   // the unit's first block item
-    if (blk0 >= x || blk0 < (int64_t)grp * bal.per) return;
-    const int64_t w1 = (blk0 + (items - p.seg_items) - 1) / bal.per;   // the last workgroup with its blocks
-    slot_first = grp + (int64_t)b * p.Hkv + g;
-    ns = (int32_t)(w1 - grp + 1);
+    if (combine_by_unit(p)) {
+      // Unit grp: its blocks are items [blk0, blk0 + nb) (after its
+      // p.seg_items leading items); workgroups w0..w1 hold them and left
+      // their partials in slots w + unit, unless one workgroup held them all
+      // and wrote the output itself.
+      b = grp / p.Hkv;
+      g = grp % p.Hkv;
+      const int32_t items = pre[b + 1] - pre[b];
+      if (items <= p.seg_items) return;   // no blocks
+      const int64_t blk0 = (int64_t)p.Hkv * pre[b] + (int64_t)g * items + p.seg_items;
+      const int64_t w0 = blk0 / bal.per;
+      const int64_t w1 = (blk0 + (items - p.seg_items) - 1) / bal.per;
+      if (w1 == w0) return;
+      slot_first = w0 + grp;
+      ns = (int32_t)(w1 - w0 + 1);
+    } else {
+      // Boundary grp lies between workgroups grp and grp+1, at item x. The
+      // unit holding x is merged here if x cuts its blocks and they start
+      // inside workgroup grp (this boundary then cuts them first); workgroups
+      // grp..w1 left its partials in slots w + unit.
+      const int64_t x = (int64_t)(grp + 1) * bal.per;
+      if (x >= bal.total) return;
+      b = balanced_seq(pre, p.B, p.Hkv, x);
+      const int32_t items = pre[b + 1] - pre[b];
+      const int64_t base = (int64_t)p.Hkv * pre[b];
+      g = (int32_t)((x - base) / items);
+      const int64_t blk0 = base + (int64_t)g * items + p.seg_items;   // the unit's first block item
+      if (blk0 >= x || blk0 < (int64_t)grp * bal.per) return;
+      const int64_t w1 = (blk0 + (items - p.seg_items) - 1) / bal.per;   // the last workgroup with its blocks
+      slot_first = grp + (int64_t)b * p.Hkv + g;
+      ns = (int32_t)(w1 - grp + 1);
+    }
   } else {
     b = grp / p.Hkv;
     g = grp % p.Hkv;
