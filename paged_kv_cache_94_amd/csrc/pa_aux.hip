@@ -60,23 +60,25 @@ __device__ __forceinline__ float2 buffer_load_f32x2(__amdgpu_buffer_rsrc_t r, in
 // Merge the rows r0, r0 + step, ... of one unit when a wavefront has several
 // of them (many units, few workgroups per unit). A partial row is D floats,
 // D/4 lanes x 16 bytes, so one load instruction of the wavefront fetches the
-// rows of SPI = 256/D splits at once, and a batch of KF = 8 splits takes
-// 8/SPI instructions. The next row's (m, l) pairs and first batch are
+// rows of SPI = 256/D splits at once, and a batch of KF splits takes
+// KF/SPI instructions. The next row's (m, l) pairs and first batch are
 // requested before the current row is merged, so the rows' memory round
 // trips overlap. Loads go through buffer descriptors that end after the
 // chunk's last split: past it they return zeros without touching memory, so
 // every path issues the same loads and the compiler waits for the current
 // row's alone. Splits past the first batch (units of more than KF pieces)
-// are loaded as the merge reaches them.
+// are loaded as the merge reaches them. Those no-op loads still take the
+// address units' time, so a unit of few pieces gets a batch just large
+// enough for them (combine_rows_sized).
 constexpr int kCombineMaxRowsPerWave = 8;   // rows a wavefront of the pipelined merge can take
 
-template <typename OutT, int D>
+template <typename OutT, int D, int KF>
 __device__ __forceinline__ void combine_rows_pipelined(const Params& p, int32_t b, int32_t g, int64_t slot_first,
                                                        int32_t ns, int r0, int step) {
   constexpr int LPS = D / 4;      // lanes per partial row
   constexpr int SPI = 64 / LPS;   // splits per load instruction
-  constexpr int KF = 8;           // splits per batch
   constexpr int NI = KF / SPI;    // load instructions per batch
+  static_assert(KF % SPI == 0 && KF >= SPI, "a batch is whole load instructions");
   const int lane = __lane_id();
   const int sl = lane / LPS;                  // this lane's split within an instruction
   const int32_t loff = (lane % LPS) * 16;     // this lane's 16 bytes of a partial row
@@ -208,6 +210,19 @@ __device__ __forceinline__ void combine_rows_pipelined(const Params& p, int32_t 
   }
 }
 
+// Batches of one or two load instructions for units of up to 256/D or
+// 512/D pieces, else of 8 splits (C5's combine: 8 splits per batch measured
+// 11.9 us, 4 measured 13.2 us and 16 measured 15.7 us for every unit alike).
+template <typename OutT, int D>
+__device__ __forceinline__ void combine_rows_sized(const Params& p, int32_t b, int32_t g, int64_t slot_first,
+                                                   int32_t ns, int r0, int step) {
+  constexpr int SPI = 256 / D;
+  constexpr int KF2 = 2 * SPI < 8 ? 2 * SPI : 8;
+  if (ns <= SPI) combine_rows_pipelined<OutT, D, SPI>(p, b, g, slot_first, ns, r0, step);
+  else if (ns <= KF2) combine_rows_pipelined<OutT, D, KF2>(p, b, g, slot_first, ns, r0, step);
+  else combine_rows_pipelined<OutT, D, 8>(p, b, g, slot_first, ns, r0, step);
+}
+
 template <typename OutT, int D, bool PIPE>
 __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Params p) {
   constexpr int PER = D / 64;   // dims per lane
@@ -289,7 +304,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
     // Wave-uniform values in scalar registers (the buffer descriptors need them there).
     const int64_t sf = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(slot_first >> 32)) << 32) |
                                  (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)slot_first));
-    combine_rows_pipelined<OutT, D>(p, b, g, sf, __builtin_amdgcn_readfirstlane(ns),
+    combine_rows_sized<OutT, D>(p, b, g, sf, __builtin_amdgcn_readfirstlane(ns),
                                     __builtin_amdgcn_readfirstlane(rg * kCombineWaves + wave), rgs * kCombineWaves);
     return;
   }
