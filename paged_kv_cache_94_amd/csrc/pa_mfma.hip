@@ -237,6 +237,14 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
   float* sst = reinterpret_cast<float*>(kst + Lds::TILE * (ALIAS ? 1 : 2));
   const char* kread = kst + n * RS + 16 * q4;
   const char* vread = vst + (4 * q4 + (n >> 2)) * RS + 8 * (n & 3);
+  // int8 tiles: a lane widens 16 codes to 32 bytes and stores them as two
+  // 16-byte halves. Lanes whose 32-byte chunk has bit 2 set (chunks 4-7,
+  // 12-15) store the halves in swapped order, so each store instruction
+  // covers every 16-byte slot of a 128-byte span instead of every other one.
+  // Readers of those chunks flip bit 4 of the address (kread_x, vread_x).
+  constexpr bool SWZ = INT8;
+  const char* kread_x = SWZ ? kst + n * RS + ((16 * q4) ^ 16) : kread;
+  const char* vread_x = SWZ ? vst + (4 * q4 + (n >> 2)) * RS + ((8 * (n & 3)) ^ 16) : vread;
 
   // One 16-token block as loaded: NLOAD 16-byte pieces of K (and V) rows, and
   // for int8 caches the scale of token l & 15 (K and V).
@@ -299,8 +307,9 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
       if (F16V && as_f16) i8x16_to_f16_exact(w, lo, hi);
       else i8x16_to_bf16(w, lo, hi);
       char* dst = dst_tile + r * RS + 32 * ld_chunk;
-      *reinterpret_cast<uint4*>(dst) = lo;
-      *reinterpret_cast<uint4*>(dst + 16) = hi;
+      const int sw = ((ld_chunk >> 2) & 1) * 16;   // halves swapped in chunks with bit 2 set
+      *reinterpret_cast<uint4*>(dst + sw) = lo;
+      *reinterpret_cast<uint4*>(dst + (16 - sw)) = hi;
     } else {
       *reinterpret_cast<uint4*>(dst_tile + r * RS + 16 * ld_chunk) = w;
     }
@@ -350,7 +359,8 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     // K operand chunks: token n, dims 32c + 8*q4 .. +7.
     bf16x8 kop[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kread + 64 * c));
+    for (int c = 0; c < C; ++c)   // bytes 64c.. lie in 32-byte chunks 2c, 2c+1: swapped when c & 2
+      kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>((SWZ && (c & 2) ? kread_x : kread) + 64 * c));
     float ksc[4], vsc[4];
     if constexpr (INT8) {
       const float4 a = *reinterpret_cast<const float4*>(sst + 4 * q4);
@@ -437,7 +447,7 @@ __device__ __forceinline__ void mfma_segment(const Params& p, char* smem, int32_
     // O^T += V^T [P_hi; P_lo], one 16-dim tile at a time, V^T read transposed from LDS.
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const uint2 a = lds_read_tr16(vread + 32 * j);
+      const uint2 a = lds_read_tr16((SWZ && (j & 4) ? vread_x : vread) + 32 * j);   // chunk j
       if constexpr (F16V) {
         // One 16-deep product: lane l holds V^T for dim n, keys 4*q4 .. +3,
         // against its own four weights.
