@@ -164,6 +164,40 @@ def test_mfma_partitions(case, mode):
     np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
 
 
+# The wavefront count changes how a workgroup shares its blocks and merges its
+# wavefronts' partial outputs (output tile j belongs to wavefront j % waves;
+# at head_dim 64 with 8 waves, wavefronts 4-7 own no tile and park all four).
+# Each count the tuning accepts, over one and two row tiles, shared and
+# separate K/V, int8 and every head_dim, with the partitions that take it.
+WAVE_CASES = [
+    ([300, 1000, 47], 1, 16, 1, 256, 0, "bf16", "bf16", True),      # 16 rows, D 256, shared K/V
+    ([700, 90, 2048], 5, 32, 8, 128, 40, "bf16", "bf16", False),    # 20 rows: two row tiles
+    ([1500, 600, 3000], 1, 64, 8, 128, 0, "bf16", "int8", False),   # int8, 8 rows
+    ([333, 64, 1201], 2, 16, 2, 64, 0, "bf16", "bf16", False),      # D 64, 16 rows
+]
+
+
+@pytest.mark.parametrize("case", WAVE_CASES, ids=_ids)
+@pytest.mark.parametrize("waves,mode", [(2, "list"), (2, "aligned"), (4, "list"), (4, "queue"), (8, "list"),
+                                        (8, "queue"), (8, "aligned")])
+def test_mfma_wave_counts(case, waves, mode):
+    tuning = {"waves": waves, "partition": mode}
+    lens, q_len, Hq, Hkv, D, window, qd, kvd, alias = case
+    x = make_inputs(lens, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, q_dtype=qd, kv_dtype=kvd,
+                    window=window, alias_v=alias, poison=True, seed=zlib.crc32(repr((case, waves, mode)).encode()))
+    _log(f"waves {waves} {mode} {_ids(case)}")
+    dev = Dev(x)
+    plan = dev.plan(tuning=tuning)
+    assert plan["kernel"] == 1 and plan["waves_per_group"] == waves
+    got = dev.run_f64(tuning=tuning)
+    assert not np.isnan(got).any()
+    assert max_err(got, _oracle(x)) <= TOL[kvd]
+    visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
+    dev.run(debug_visits=visits, tuning=tuning)
+    expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
+    np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
+
+
 @pytest.mark.parametrize("per_wg", [1, 3])
 def test_queue_pieces_down_to_one_per_unit(per_wg):
     """An explicit pieces-per-workgroup request may go below the plan's two
