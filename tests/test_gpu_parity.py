@@ -287,6 +287,35 @@ def test_list_partition_segment_charges(seg):
         np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
 
 
+@pytest.mark.parametrize("seg", [0, 40])
+def test_list_partition_more_units_than_boundaries(seg):
+    """96 sequences on 8 KV heads are 768 units, at least as many as the
+    boundaries between the flattened list's workgroups (511 at 512), so the
+    combine takes one workgroup per boundary and finds the unit each one cuts
+    first (with fewer units it takes one workgroup per unit; the other list
+    tests cover that). Lengths of 1-25 blocks, q_len 3, int8 and bf16, the
+    plan's segment charge (0) and a large one. Every output row is compared
+    with the oracle and every block is visited once."""
+    rng = np.random.default_rng(zlib.crc32(b"list-boundaries") + seg)
+    lens = rng.integers(3, 400, 96)
+    for kvd in ("int8", "bf16"):
+        x = make_inputs(lens.tolist(), q_len=3, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                        kv_dtype=kvd, poison=True, seed=seg + 11)
+        dev = Dev(x)
+        tuning = {"partition": "list", "segment_blocks": seg}
+        plan = dev.plan(tuning=tuning)
+        _log(f"list with {x.batch * x.num_kv_heads} units, segment_blocks={seg} {kvd}: plan {plan}")
+        assert plan["kernel"] == 1 and plan["balanced"] == 1
+        assert x.batch * x.num_kv_heads >= plan["grid"] - 1
+        got = dev.run_f64(tuning=tuning)
+        assert not np.isnan(got).any()
+        assert max_err(got, _oracle(x)) <= TOL[kvd]
+        visits = torch.zeros((x.batch, x.num_kv_heads, x.max_blocks), dtype=torch.int32, device="cuda")
+        dev.run(debug_visits=visits, tuning=tuning)
+        expect = oracle.visited_blocks(oracle.Problem.from_inputs(x))
+        np.testing.assert_array_equal(visits.cpu().numpy(), np.broadcast_to(expect[:, None, :], visits.shape))
+
+
 @pytest.mark.parametrize("head_scales", [False, True])
 @pytest.mark.parametrize("q_len", [1, 3])
 def test_int8_large_value_scales(head_scales, q_len):
