@@ -33,7 +33,16 @@ constexpr int kCombineWaves = 4;
 // wavefront chain their memory round trips), unless that would launch
 // thousands of workgroups (2048 units x 5 row groups measured 3 us slower
 // than one workgroup per unit).
+// Few units cut into many slices (the flattened list merged per unit): one
+// workgroup per (unit, row), whose wavefronts each merge a quarter of the
+// row's splits and fold their results through LDS, so up to 64 splits cost
+// one memory round trip.
+__host__ __device__ inline bool combine_wide(const Params& p) {
+  return p.balanced == 1 && combine_by_unit(p);
+}
+
 __host__ __device__ inline int combine_row_groups(const Params& p) {
+  if (combine_wide(p)) return p.rows;
   return combine_groups(p) >= 1024 ? 1 : (p.rows + kCombineWaves - 1) / kCombineWaves;
 }
 
@@ -308,14 +317,16 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
                                     __builtin_amdgcn_readfirstlane(rg * kCombineWaves + wave), rgs * kCombineWaves);
     return;
   }
-  for (int r = rg * kCombineWaves + wave; r < p.rows; r += rgs * kCombineWaves) {
-    const size_t slot0 = (size_t)slot_first * p.rows + r;   // partial s of this row: slot0 + s*rows
+  // Merge partials s0 .. s0+nsw-1 of row r into (M, den, o).
+  auto merge_row = [&](int r, int32_t s0, int32_t nsw, float& M, float& den, float (&o)[PER])
+      __attribute__((always_inline)) {
+    const size_t slot0 = ((size_t)slot_first + s0) * p.rows + r;   // partial s0+s of this row: slot0 + s*rows
     const float* ml = p.ws_ml + slot0 * 2;
     const float* acc = p.ws_acc + slot0 * D + lane * PER;
-    float o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
-    float M = -INFINITY, den = 0.f;
+    M = -INFINITY;
+    den = 0.f;
     // Partial rows j0 .. j0+NB-1 of the chunk starting at c0 (cnt of them), NB loads in flight.
     constexpr int NB = 16;
     float v[NB][PER];
@@ -335,8 +346,8 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
         }
       }
     };
-    for (int32_t c0 = 0; c0 < ns; c0 += 64) {
-      const int32_t cnt = min(64, ns - c0);
+    for (int32_t c0 = 0; c0 < nsw; c0 += 64) {
+      const int32_t cnt = min(64, nsw - c0);
       const float ms = lane < cnt ? ml[(size_t)(c0 + lane) * p.rows * 2] : -INFINITY;
       const float ls = lane < cnt ? ml[(size_t)(c0 + lane) * p.rows * 2 + 1] : 0.f;
       load_rows(c0, 0, cnt);
@@ -367,6 +378,8 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
         }
       }
     }
+  };
+  auto store_row = [&](int r, const float (&o)[PER], float den) __attribute__((always_inline)) {
     const float inv = 1.f / den;
     const int t = r / p.G;
     const int h = g * p.G + r % p.G;
@@ -379,6 +392,45 @@ __global__ void __launch_bounds__(64 * kCombineWaves) pa_combine_kernel(const Pa
         out[e] = (__bf16)(o[e] * inv);
       }
     }
+  };
+  if (combine_wide(p)) {
+    // Row rg; wavefront w merges the w-th quarter of the splits, then
+    // wavefront 0 folds the four (max, sum, row) results with the same rule.
+    __shared__ float wide_o[kCombineWaves][64 * PER];
+    __shared__ float wide_md[kCombineWaves][2];
+    const int32_t q = (ns + kCombineWaves - 1) / kCombineWaves;
+    const int32_t s0 = min(ns, wave * q);
+    float o[PER], M, den;
+    merge_row(rg, s0, min(ns - s0, q), M, den, o);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) wide_o[wave][lane * PER + e] = o[e];
+    if (lane == 0) {
+      wide_md[wave][0] = M;
+      wide_md[wave][1] = den;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; ++w) Mx = fmaxf(Mx, wide_md[w][0]);
+    const float Ms = Mx == -INFINITY ? 0.f : Mx;
+    float dsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; ++w) {
+      const float a = fast_exp2(wide_md[w][0] - Ms);   // 0 for a quarter with no splits
+      dsum += a * wide_md[w][1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] += a * wide_o[w][lane * PER + e];
+    }
+    store_row(rg, o, dsum);
+    return;
+  }
+  for (int r = rg * kCombineWaves + wave; r < p.rows; r += rgs * kCombineWaves) {
+    float o[PER], M, den;
+    merge_row(r, 0, ns, M, den, o);
+    store_row(r, o, den);
   }
 }
 
