@@ -77,16 +77,16 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 89, "fetch_factor": 2.0, "write_kib": 2, "write_factor": 1.0},
     2: {"source": "profiles/pa_valu_kernel-gemma4_12b_local_bf16-hbm_counters.txt", "kernel_sources": "ea299d4735d08495",
         "plan": {"kernel": 0, "rows": 2, "waves_per_group": 8, "splits": 1, "grid": 256, "balanced": 0, "pieces": 0, "queue": 0},
-        "fetch_kib": 132873, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
-    3: {"source": "profiles/pa_mfma_kernel-gemma4_12b_global_bf16-hbm_counters.txt", "kernel_sources": "d58b628e4c09d792",
+        "fetch_kib": 132874, "fetch_factor": 2.0, "write_kib": 256, "write_factor": 1.0},
+    3: {"source": "profiles/pa_mfma_kernel-gemma4_12b_global_bf16-hbm_counters.txt", "kernel_sources": "25f2214b36e1fb52",
         "plan": {"kernel": 1, "rows": 16, "waves_per_group": 8, "splits": 57, "grid": 256, "balanced": 1, "pieces": 0, "queue": 0},
         "fetch_kib": 61373, "fetch_factor": 2.0, "write_kib": 4209, "write_factor": 1.0},
-    4: {"source": "profiles/pa_mfma_kernel-gqa70b_int8kv-hbm_counters.txt", "kernel_sources": "d58b628e4c09d792",
+    4: {"source": "profiles/pa_mfma_kernel-gqa70b_int8kv-hbm_counters.txt", "kernel_sources": "25f2214b36e1fb52",
         "plan": {"kernel": 1, "rows": 8, "waves_per_group": 4, "splits": 4, "grid": 512, "balanced": 1, "pieces": 0, "queue": 0},
-        "fetch_kib": 189701, "fetch_factor": 2.0, "write_kib": 3810, "write_factor": 1.0},
-    5: {"source": "profiles/pa_mfma_kernel-verify5_bf16-hbm_counters.txt", "kernel_sources": "d58b628e4c09d792",
+        "fetch_kib": 189700, "fetch_factor": 2.0, "write_kib": 3810, "write_factor": 1.0},
+    5: {"source": "profiles/pa_mfma_kernel-verify5_bf16-hbm_counters.txt", "kernel_sources": "25f2214b36e1fb52",
         "plan": {"kernel": 1, "rows": 20, "waves_per_group": 4, "splits": 16, "grid": 512, "balanced": 2, "pieces": 4096, "queue": 1},
-        "fetch_kib": 838643, "fetch_factor": 2.0, "write_kib": 35638, "write_factor": 1.0},
+        "fetch_kib": 838642, "fetch_factor": 2.0, "write_kib": 35638, "write_factor": 1.0},
 }
 KERNEL_SOURCES = {0: ("pa_device.h", "pa_common.h", "pa_valu.hip"), 1: ("pa_device.h", "pa_common.h", "pa_mfma.hip")}
 

@@ -33,10 +33,15 @@
 //  * O^T accumulates in fp32: lane l ends with query row n and, per 16-dim
 //    tile j, dims 16j + 4*q4 .. +3.
 //  * int8 caches (tiniestgpt notes, KV cache quantization): codes are
-//    gathered first and widened to bf16 while staging (exact for
-//    |code| <= 127); the key scale multiplies the score of its token and the
-//    value scale is folded into P. Each block's 16 key and 16 value scales
-//    come in with one load each and pass through the staging area.
+//    gathered first and widened while staging, exactly (|code| <= 127): K
+//    codes to bf16, and V codes to f16 when K and V have pools of their own
+//    (a shared pool stages one bf16 tile for both). The key scale multiplies
+//    the score of its token and the value scale is folded into P, which then
+//    goes to the matrix cores as one f16 weight per key against the f16 V.
+//    Each block's 16 key and 16 value scales come in with one load each and
+//    pass through the staging area. A lane's 16 codes widen to 32 bytes,
+//    stored as two 16-byte halves in an order that alternates between
+//    128-byte spans, so the stores meet every LDS bank once.
 //  * When v_pool == k_pool (Gemma4 global layer, shared W_K / W_V) the tile
 //    is read from HBM once and staged once; it serves as both K and V.
 #include "pa_common.h"
