@@ -306,8 +306,12 @@ pa_prefill_kernel(const PrefillParams p) {
         uint4 lo, hi;
         if (isv) i8x16_to_f16_exact(w, lo, hi);
         else i8x16_to_bf16(w, lo, hi);
-        *reinterpret_cast<uint4*>(dst + 32 * chunk) = lo;
-        *reinterpret_cast<uint4*>(dst + 32 * chunk + 16) = hi;
+        // The two 16-byte halves go in swapped order in 32-byte chunks with
+        // bit 2 set, so a store instruction covers every 16-byte slot of a
+        // 128-byte span; the readers flip their half for those chunks.
+        const int sw = ((chunk >> 2) & 1) * 16;
+        *reinterpret_cast<uint4*>(dst + 32 * chunk + sw) = lo;
+        *reinterpret_cast<uint4*>(dst + 32 * chunk + (16 - sw)) = hi;
       } else {
         *reinterpret_cast<uint4*>(dst + 16 * chunk) = w;
       }
@@ -338,8 +342,9 @@ pa_prefill_kernel(const PrefillParams p) {
       bf16x8 kop[C];
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        // dims 32c + 8*q4 .. +7: 16-byte chunk 4c + q4 of the row
-        const int chunk = S::DIRECT ? ((4 * c + q4) ^ lds_swz<D>(krow)) : 4 * c + q4;
+        // dims 32c + 8*q4 .. +7: 16-byte chunk 4c + q4 of the row (int8: its
+        // halves swapped in 32-byte chunks 2c.. with bit 2 set, i.e. when c & 2)
+        const int chunk = S::DIRECT ? ((4 * c + q4) ^ lds_swz<D>(krow)) : (4 * c + q4) ^ ((c >> 1) & 1);
         kop[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kst + krow * RS + 16 * chunk));
       }
 #pragma unroll
@@ -426,7 +431,7 @@ pa_prefill_kernel(const PrefillParams p) {
       const char* vread1 = vread0 + 16 * RS;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const int chunk = 2 * j + ((n & 3) >> 1);
+        const int chunk = (2 * j + ((n & 3) >> 1)) ^ ((j >> 2) & 1);   // halves swapped when j & 4
         const uint2 a0 = lds_read_tr16(vread0 + 16 * chunk);
         const uint2 a1 = lds_read_tr16(vread1 + 16 * chunk);
         const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
